@@ -1,0 +1,389 @@
+"""Pins for the CPU oracle: closed forms, hand-worked examples, brute force and
+library routines (numpy / torch), never the oracle checked against itself.
+
+Each group of tests names the definition it pins.  Hand-worked values live in
+tests/golden/hand_examples.json; the pages' own size figures in
+tests/golden/pages_sizes.json.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+B3, TB = oracle.FMT_B3, oracle.FMT_2B
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _one_group(trits_head, fill=0, fmt=B3):
+    """A 1x128 row whose first trits are given, rest `fill`; scale 1.0."""
+    t = np.full((1, 128), fill, dtype=np.int8)
+    t[0, : len(trits_head)] = trits_head
+    s = np.array([[0x3C00]], dtype=np.uint16)
+    return t, s
+
+
+# ---------------------------------------------------------------- fp16 ----
+
+def test_half_to_float_exhaustive_vs_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.half_to_float(int(b)) for b in bits], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_synth_f16_rounding_matches_numpy():
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+                           [0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e-8, 2.0 ** -25, 3 * 2.0 ** -26]])
+    for v in vals:
+        assert synth.f16_bits(v) == int(np.array([v]).astype(np.float16).view(np.uint16)[0]), v
+
+
+# ---------------------------------------------------------------- B3 ------
+
+def test_b3_hand_bytes():
+    g = _gold("hand_examples.json")
+    for ex in g["b3_bytes"]:
+        t, s = _one_group(ex["trits"])
+        blob = oracle.pack(B3, t, s)
+        assert blob[0] == ex["byte"], ex
+    for ex in g["b3_tail_bytes"]:
+        t = np.zeros((1, 128), dtype=np.int8)
+        t[0, 125:] = ex["trits"]
+        blob = oracle.pack(B3, t, np.array([[0x3C00]], dtype=np.uint16))
+        assert blob[25] == ex["byte"], ex
+
+
+def test_b3_closed_form_groups():
+    for fill, body, tail in ((0, 121, 121), (1, 242, 134), (-1, 0, 108)):
+        t = np.full((1, 128), fill, dtype=np.int8)
+        blob = oracle.pack(B3, t, np.array([[0x3C00]], dtype=np.uint16))
+        assert list(blob[:25]) == [body] * 25 and blob[25] == tail
+        assert list(blob[26:28]) == [0x00, 0x3C]  # scale, little-endian
+
+
+def test_b3_all_243_patterns_vs_python_base3():
+    """Every 5-trit pattern, at the first and at the last full byte of a group,
+    equals Python's int(str, 3) of the digits written most-significant first."""
+    pats = np.array(np.meshgrid(*[[-1, 0, 1]] * 5, indexing="ij")).reshape(5, -1).T
+    seen = set()
+    for p in pats:
+        expect = int("".join(str(d + 1) for d in p[::-1]), 3)
+        for j in (0, 24):
+            t = np.zeros((1, 128), dtype=np.int8)
+            t[0, 5 * j: 5 * j + 5] = p
+            blob = oracle.pack(B3, t, np.array([[0x3C00]], dtype=np.uint16))
+            assert blob[j] == expect
+        seen.add(expect)
+    assert seen == set(range(243))  # a bijection onto 0..242
+
+
+def test_b3_all_27_tail_patterns():
+    pats = np.array(np.meshgrid(*[[-1, 0, 1]] * 3, indexing="ij")).reshape(3, -1).T
+    for p in pats:
+        t = np.zeros((1, 128), dtype=np.int8)
+        t[0, 125:] = p
+        blob = oracle.pack(B3, t, np.array([[0x3C00]], dtype=np.uint16))
+        assert blob[25] == int("11" + "".join(str(d + 1) for d in p[::-1]), 3)
+
+
+def test_b3_every_byte_value_roundtrip_and_rejects():
+    for v in range(256):
+        for j in (0, 13, 24, 25):
+            blob = oracle.pack(B3, np.zeros((1, 128), np.int8), np.array([[0x3C00]], np.uint16))
+            blob[j] = v
+            rc, t, s = oracle.unpack(B3, blob, 1, 128)
+            if j < 25:
+                valid = v < 243
+            else:
+                valid = v < 243 and (v // 27) % 3 == 1 and v // 81 == 1
+            assert (rc == 0) == valid, (v, j, rc)
+            if valid:
+                assert np.array_equal(oracle.pack(B3, t, s), blob)
+
+
+def test_b3_random_roundtrip_and_layout():
+    N, K = 7, 640
+    t = synth.trits(synth.seed(91), N, K)
+    s = synth.scales(synth.seed(92), N, K)
+    blob = oracle.pack(B3, t, s)
+    G = K // 128
+    assert blob.size == N * G * 28 == oracle.packed_bytes(B3, N, K)
+    rc, t2, s2 = oracle.unpack(B3, blob, N, K)
+    assert rc == 0 and np.array_equal(t, t2) and np.array_equal(s, s2)
+    # scale region: [N][G] little-endian after the trit region
+    assert np.array_equal(blob[N * G * 26:].view(np.uint16).reshape(N, G), s)
+    # group (n, g) owns bytes (n*G+g)*26: re-pack one group alone and compare
+    n, g = 5, 3
+    one = oracle.pack(B3, np.ascontiguousarray(t[n: n + 1, 128 * g: 128 * g + 128]),
+                      s[n: n + 1, g: g + 1])
+    assert np.array_equal(blob[(n * G + g) * 26:(n * G + g + 1) * 26], one[:26])
+
+
+def test_pack_rejects_bad_inputs():
+    t = np.zeros((2, 256), np.int8)
+    s = np.full((2, 2), 0x3C00, np.uint16)
+    bad = t.copy()
+    bad[1, 7] = 2
+    for fmt in (B3, TB):
+        with pytest.raises(oracle.OracleError):
+            oracle.pack(fmt, bad, s)
+        for nonfinite in (0x7C00, 0xFC00, 0x7E00):
+            s2 = s.copy()
+            s2[0, 1] = nonfinite
+            with pytest.raises(oracle.OracleError):
+                oracle.pack(fmt, t, s2)
+        with pytest.raises(oracle.OracleError):
+            oracle.pack(fmt, np.zeros((1, 200), np.int8), np.zeros((1, 1), np.uint16))
+    assert oracle.packed_bytes(B3, 1, 100) == 0 and oracle.packed_bytes(TB, 0, 128) == 0
+
+
+# ---------------------------------------------------------------- 2B ------
+
+def test_2b_hand_and_all_81_bytes():
+    for ex in _gold("hand_examples.json")["twobit_bytes"]:
+        t, s = _one_group(ex["trits"])
+        assert oracle.pack(TB, t, s)[0] == ex["byte"]
+    for fill, byte in ((0, 0x55), (1, 0xAA), (-1, 0x00)):
+        blob = oracle.pack(TB, np.full((1, 128), fill, np.int8), np.array([[0x3C00]], np.uint16))
+        assert list(blob[:32]) == [byte] * 32
+    valid = 0
+    for v in range(256):
+        blob = oracle.pack(TB, np.zeros((1, 128), np.int8), np.array([[0x3C00]], np.uint16))
+        blob[9] = v
+        rc, t, _ = oracle.unpack(TB, blob, 1, 128)
+        fields = [(v >> (2 * i)) & 3 for i in range(4)]
+        assert (rc == 0) == (3 not in fields)
+        if rc == 0:
+            valid += 1
+            assert list(t[0, 36:40]) == [f - 1 for f in fields]
+    assert valid == 81
+
+
+def test_2b_random_roundtrip():
+    N, K = 5, 384
+    t = synth.trits(synth.seed(93), N, K)
+    s = synth.scales(synth.seed(94), N, K)
+    blob = oracle.pack(TB, t, s)
+    assert blob.size == N * 3 * 34
+    rc, t2, s2 = oracle.unpack(TB, blob, N, K)
+    assert rc == 0 and np.array_equal(t, t2) and np.array_equal(s, s2)
+
+
+def test_format_sizes_vs_pages():
+    g = _gold("pages_sizes.json")
+    b3_bpw = 28 * 8 / 128
+    tb_bpw = 34 * 8 / 128
+    assert abs(b3_bpw - g["effective_bits_per_weight_with_fp16_group_scales"]["value"]) < 0.02
+    # five trits per byte sits just above the entropy bound log2(3)
+    assert math.log2(3) <= 8 / 5 and abs(math.log2(3) - g["entropy_bits_per_trit"]["value"]) < 0.01
+    assert 8 / 4 == g["two_bit_aligned_storage_bits"]["value"]
+    r = g["pq2_gb_over_ptq1_0_gb"]
+    assert abs(tb_bpw / b3_bpw - r["pq2_gb"] / r["ptq1_0_gb"]) < 0.01 * (r["pq2_gb"] / r["ptq1_0_gb"])
+
+
+# ---------------------------------------------------------------- quant ---
+
+def test_quant_hand_examples():
+    for ex in _gold("hand_examples.json")["quant"]:
+        x = np.array([ex["x"]], dtype=np.float16)
+        q, sc = oracle.quant(x)
+        assert list(q[0]) == ex["q"], ex
+        if ex.get("scale_is_1_over_127"):
+            assert sc[0] == np.float32(1.0) / np.float32(127.0)
+        if "scale" in ex:
+            assert sc[0] == ex["scale"]
+
+
+def _numpy_quant_f32(x32):
+    a = np.abs(x32).max(axis=-1, keepdims=True).astype(np.float32)
+    inv = np.float32(127.0) / a
+    q = np.clip(np.rint((x32 * inv).astype(np.float32)), -127, 127).astype(np.int8)
+    return q, (a / np.float32(127.0)).astype(np.float32)[..., 0]
+
+
+def test_quant_bruteforce_all_fp16_pairs():
+    """K=2, x0 = +-1, x1 = every finite fp16: covers |x1| <= 1 and the regime
+    where x1 becomes the absmax.  Compared with numpy float32 arithmetic."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x1 = bits.view(np.float16)
+    x1 = x1[np.isfinite(x1)]
+    assert x1.size == 63488
+    for x0 in (1.0, -1.0):
+        x = np.stack([np.full(x1.size, x0, np.float16), x1], axis=1)
+        q, sc = oracle.quant(x)
+        qr, scr = _numpy_quant_f32(x.astype(np.float32))
+        assert np.array_equal(q, qr)
+        assert np.array_equal(sc.view(np.uint32), scr.view(np.uint32))
+
+
+def test_quant_invariants():
+    x = synth.normal_f32(synth.seed(95), 64, 1000)
+    q, sc = oracle.quant(x)
+    am = np.abs(x).argmax(axis=1)
+    assert np.all(np.abs(q[np.arange(64), am]) == 127)
+    assert np.all(np.abs(q).max(axis=1) == 127)
+    qn, scn = oracle.quant(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(scn, sc)
+    for k in (-3, 5):
+        qk, sck = oracle.quant((x * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(qk, q)
+        assert np.allclose(sck, sc * 2.0 ** k, rtol=0, atol=0)
+    # fp16 input equals fp32 input of the widened values
+    xh = synth.normal_f16(synth.seed(96), 8, 640)
+    assert np.array_equal(oracle.quant(xh)[0], oracle.quant(xh.astype(np.float32))[0])
+
+
+def test_quant_rejects_nonfinite():
+    for bad in (np.inf, -np.inf, np.nan):
+        x = np.array([[1.0, bad, 0.5]], dtype=np.float32)
+        with pytest.raises(oracle.OracleError):
+            oracle.quant(x)
+    with pytest.raises(oracle.OracleError):  # 127/a overflows
+        oracle.quant(np.array([[1e-39, 0.0]], dtype=np.float32))
+
+
+# ------------------------------------------------------- integer core -----
+
+def test_group_sums_vs_numpy_int64():
+    M, N, K = 3, 9, 512
+    t = synth.trits(synth.seed(97), N, K)
+    q, _ = oracle.quant(synth.normal_f16(synth.seed(98), M, K))
+    S = oracle.group_sums(t, q)
+    G = K // 128
+    ref = np.einsum("ngi,mgi->mng", t.reshape(N, G, 128).astype(np.int64),
+                    q.reshape(M, G, 128).astype(np.int64))
+    assert np.array_equal(S.astype(np.int64), ref)
+    assert np.abs(S).max() <= 127 * 128
+
+
+def test_group_sums_special_cases():
+    K = 256
+    q, _ = oracle.quant(synth.normal_f16(synth.seed(99), 1, K))
+    assert not oracle.group_sums(np.zeros((2, K), np.int8), q).any()
+    for sign in (1, -1):
+        for k in (0, 127, 128, 255):
+            t = np.zeros((1, K), np.int8)
+            t[0, k] = sign
+            S = oracle.group_sums(t, q)[0, 0]
+            expect = np.zeros(2, np.int64)
+            expect[k // 128] = sign * int(q[0, k])
+            assert np.array_equal(S, expect)
+        S = oracle.group_sums(np.full((1, K), sign, np.int8), q)[0, 0]
+        assert np.array_equal(S, sign * q[0].reshape(2, 128).astype(np.int64).sum(1))
+    # additivity over disjoint supports
+    a = synth.trits(synth.seed(100), 1, K)
+    b = np.where(a == 0, synth.trits(synth.seed(101), 1, K), 0).astype(np.int8)
+    assert np.array_equal(oracle.group_sums(a + b, q),
+                          oracle.group_sums(a, q) + oracle.group_sums(b, q))
+
+
+# ------------------------------------------------------------ output ------
+
+def _deq_ref(t, s, q, a):
+    """float64 dequantize-then-matmul: W[n,k] = s[n,k//128] * t[n,k]."""
+    sf = s.view(np.float16).astype(np.float64)
+    W = t.astype(np.float64) * np.repeat(sf, 128, axis=1)
+    return (q.astype(np.float64) @ W.T) * a.astype(np.float64)[:, None]
+
+
+def test_gemv_vs_float64_dequant_matmul():
+    M, N, K = 4, 33, 1024
+    t = synth.trits(synth.seed(102), N, K)
+    s = synth.scales(synth.seed(103), N, K)
+    q, a = oracle.quant(synth.normal_f16(synth.seed(104), M, K))
+    y = oracle.gemv(t, s, q, a)
+    ref = _deq_ref(t, s, q, a)
+    assert np.allclose(y, ref, rtol=1e-6, atol=1e-7 * np.abs(ref).max())
+    # rounding is the only difference: one fp32 rounding of the double value
+    assert np.max(np.abs(y - ref) / np.maximum(np.abs(ref), 1e-30)) <= 2.0 ** -23
+    # With scales in [0.005, 0.05] every term s*t*q is a multiple of 2^-18 below
+    # 2^13, so both double sums are exact whatever their order, and the result
+    # is the exact value times a, rounded once to double and once to fp32.
+    assert np.array_equal(y, ref.astype(np.float32))
+
+
+def test_gemv_long_k_exact_rounding():
+    """K=17408 (136 groups): the scaled group sums need more than 24 bits, so
+    only an accumulation wider than fp32 reproduces the once-rounded value."""
+    M, N, K = 2, 24, 17408
+    t = synth.trits(synth.seed(112), N, K)
+    s = synth.scales(synth.seed(113), N, K)
+    q, a = oracle.quant(synth.normal_f16(synth.seed(114), M, K))
+    y = oracle.gemv(t, s, q, a)
+    assert np.array_equal(y, _deq_ref(t, s, q, a).astype(np.float32))
+
+
+def test_gemv_unit_scales_is_exact_integer_matmul():
+    M, N, K = 2, 17, 384
+    t = synth.trits(synth.seed(105), N, K)
+    s = np.full((N, K // 128), 0x3C00, np.uint16)
+    q, _ = oracle.quant(synth.normal_f16(synth.seed(106), M, K))
+    y = oracle.gemv(t, s, q, np.ones(M, np.float32))
+    ref = q.astype(np.int64) @ t.astype(np.int64).T
+    assert np.array_equal(y.astype(np.int64), ref)
+
+
+def test_gemv_hand_example():
+    ex = _gold("hand_examples.json")["gemv_k128"]
+    t = np.zeros((1, 128), np.int8)
+    t[0, 0], t[0, 1] = 1, -1
+    s = np.array([[0x3800]], np.uint16)  # 0.5
+    x = np.zeros((1, 128), np.float16)
+    x[0, :3] = [1.0, -0.5, 0.25]
+    q, a = oracle.quant(x)
+    assert oracle.group_sums(t, q)[0, 0, 0] == ex["S"]
+    y = oracle.gemv(t, s, q, a)[0, 0]
+    assert abs(y - ex["y"]) <= 1e-7
+
+
+def test_gemv_rows_and_packed_agree_with_gemv():
+    M, N, K = 2, 21, 768
+    t = synth.trits(synth.seed(107), N, K)
+    s = synth.scales(synth.seed(108), N, K)
+    q, a = oracle.quant(synth.normal_f16(synth.seed(109), M, K))
+    y = oracle.gemv(t, s, q, a)
+    rows = np.array([0, 20, 7, 7])
+    assert np.array_equal(oracle.gemv_rows(t, s, q, a, rows), y[:, rows])
+    for fmt in (B3, TB):
+        assert np.array_equal(oracle.project_packed(fmt, oracle.pack(fmt, t, s), N, K, q, a), y)
+    oracle.set_threads(4)
+    try:
+        assert np.array_equal(oracle.gemv(t, s, q, a), y)
+    finally:
+        oracle.set_threads(1)
+
+
+# ----------------------------------------------------------- swiglu -------
+
+def test_swiglu_vs_torch_silu_float64():
+    g = synth.normal_f32(synth.seed(110), 4096) * np.float32(6)
+    u = synth.normal_f32(synth.seed(111), 4096)
+    h = oracle.swiglu(g, u)
+    ref = (torch.nn.functional.silu(torch.from_numpy(g.astype(np.float64)))
+           * torch.from_numpy(u.astype(np.float64))).numpy()
+    assert np.allclose(h, ref, rtol=2.0 ** -23, atol=1e-37)
+    assert np.array_equal(h, ref.astype(np.float32))
+
+
+def test_swiglu_special_values():
+    g = np.array([0.0, 80.0, -80.0, 1.0], np.float32)
+    u = np.array([3.0, 2.0, 1.0, 1.0], np.float32)
+    h = oracle.swiglu(g, u)
+    assert h[0] == 0.0
+    assert h[1] == np.float32(160.0)
+    assert h[2] <= 0.0 and abs(h[2]) < 1e-30
+    assert abs(h[3] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-7
