@@ -1,0 +1,167 @@
+/*
+ * tq.h -- C ABI of libtq: ternary-weight GEMV / GEMM for AMD CDNA4 (gfx950).
+ *
+ * Method (what every entry point computes):
+ *   weights W[N][K] are trits {-1, 0, +1}, so each multiply is negate, zero or
+ *   keep (pwwt.cn/news/4940051, section 1.1 "权重只有{-1,0,1}，其他都扔掉");
+ *   they come in groups of 128 consecutive k of one row, each group sharing
+ *   one FP16 scale s[n][g] that is applied after the signed sum
+ *   ("三值权重 27B 压到 5.9GB｜本地部署成本账单重算", section 三);
+ *   activations are quantised per row to int8 (Q8) by absmax
+ *   ("Ternary Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section
+ *   "后面还有没有优化空间"); the kernels decode the packed trits in registers,
+ *   run an integer dot product per group and scale it (same page, section
+ *   "Decode 为什么只能算一般"):
+ *
+ *     S[m][n][g] = sum_{i<128} t[n][128g+i] * q[m][128g+i]          (int32)
+ *     y[m][n]    = a[m] * sum_g s[n][g] * S[m][n][g]                  (fp32)
+ *
+ * Conventions for every function:
+ *  - Return value: TQ_OK (0) or a negative tq_status.  All argument checks
+ *    happen on the host before any device work is enqueued, so an error
+ *    return means nothing was launched.
+ *  - Device functions are asynchronous on `stream` (a hipStream_t; NULL is
+ *    the default stream) and never synchronise.  A kernel-launch failure
+ *    returns TQ_ERR_HIP; faults surface at the caller's next synchronisation.
+ *  - Device pointers must be 16-byte aligned (TQ_ERR_ALIGN otherwise).
+ *  - The caller owns every buffer; the library never allocates or frees.
+ *  - K must be a positive multiple of 128; N >= 1; M >= 1.
+ *  - Stateless and thread-safe, except that one workspace must not be used
+ *    by two calls that may run concurrently.
+ *
+ * Packed weight blob ("device layout").  Rows are cut into blocks of 64
+ * (the last block holds the remaining w rows, padded up to a multiple of 4
+ * rows for B3 and of 8 rows for 2B; padding rows hold zero trits and a zero
+ * scale).  Let G = K/128 and Wb the (padded) row count of a block.  Block b
+ * starts at byte 64*b*G*P, where P = 28 (B3) or 34 (2B); inside it group g
+ * starts at g*Wb*P, and row r of the block owns:
+ *   B3: bytes 0..15 of the group at +r*16, bytes 16..25 plus the fp16 scale
+ *       (little endian) at +Wb*16 + r*12;
+ *   2B: bytes 0..15 at +r*16, bytes 16..31 at +Wb*16 + r*16, the fp16 scale
+ *       at +Wb*32 + r*2.
+ * So consecutive lanes (rows) read consecutive 16/12/2-byte pieces.  This is
+ * the load-time re-tiling into consumption order that the Bonsai page
+ * suggests ("后面还有没有优化空间": reorder codes and scales into the order
+ * the dot instruction consumes them).
+ *
+ * Group bytes (a permutation of the 128 trits chosen so that activations are
+ * consumed as aligned 4-byte words):
+ *   B3 (five trits per byte, base 3, digit d = t + 1, digit i weighs 3^i):
+ *       byte j < 25: digits 0..3 are k = 4j..4j+3, digit 4 is k = 100 + j;
+ *       byte 25    : digit 0 and digit 4 are padding (d = 1), digits 1..3
+ *                    are k = 125, 126, 127.  Every byte is < 243.
+ *       1.75 bit per weight including the scale.
+ *   2B (four 2-bit codes per byte, code d = t + 1, code 3 invalid):
+ *       byte 4m + c, bits 2s..2s+1 hold k = 16m + 4s + c.
+ *       2.125 bit per weight including the scale.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_NULL = -1,   /* a required pointer is NULL */
+  TQ_ERR_SHAPE = -2,  /* N < 1, M out of range, K not a positive multiple of 128 */
+  TQ_ERR_ALIGN = -3,  /* a device pointer is not 16-byte aligned */
+  TQ_ERR_VALUE = -4,  /* trit outside {-1,0,1} or non-finite scale */
+  TQ_ERR_FORMAT = -5, /* unknown format, or a non-canonical packed byte */
+  TQ_ERR_DTYPE = -6,  /* unknown activation dtype */
+  TQ_ERR_SIZE = -7,   /* a buffer (blob or workspace) is too small */
+  TQ_ERR_HIP = -8     /* the HIP runtime refused a launch */
+} tq_status;
+
+typedef enum { TQ_FMT_B3 = 0, TQ_FMT_2B = 1 } tq_format;
+typedef enum { TQ_F16 = 0, TQ_F32 = 1 } tq_dtype;
+
+#define TQ_GROUP 128
+#define TQ_BLOCK_ROWS 64
+#define TQ_GEMV_MAX_M 16
+
+/* Human-readable name of a status code (static string). */
+const char *tq_status_str(int status);
+
+/* ---- host: packed format --------------------------------------------- */
+
+/* Size in bytes of the packed blob for an N x K matrix; 0 on a bad shape or
+ * format. */
+size_t tq_packed_bytes(int fmt, int64_t N, int64_t K);
+
+/* Pack trits[N][K] (int8 in {-1,0,1}, row-major) and scales[N][K/128]
+ * (IEEE fp16 bit patterns, finite) into dst (host memory, >= dst_bytes).
+ * Host only; the caller uploads the blob.  TQ_ERR_VALUE on a bad trit or a
+ * non-finite scale, TQ_ERR_SIZE if dst_bytes is too small. */
+int tq_pack(int fmt, int64_t N, int64_t K, const int8_t *trits, const uint16_t *scales,
+            void *dst, size_t dst_bytes);
+
+/* Exact inverse of tq_pack (host memory).  Rejects with TQ_ERR_FORMAT any
+ * byte that tq_pack cannot produce (B3 byte >= 243, bad padding digit, 2B
+ * code 3, non-zero padding rows) and with TQ_ERR_VALUE a non-finite scale. */
+int tq_unpack(int fmt, int64_t N, int64_t K, const void *src, size_t src_bytes,
+              int8_t *trits, uint16_t *scales);
+
+/* ---- device: activation quantiser ------------------------------------- */
+
+/* Per row m of x[M][K] (dtype TQ_F16 or TQ_F32, device):
+ *   a = max_k |x|; a == 0 -> a_scale[m] = 0, q = 0;
+ *   else a_scale[m] = a/127, q[m][k] = clamp(rint(x * (127/a)), -127, 127),
+ *   all in IEEE fp32 with round-to-nearest-even (bit-exact with the CPU
+ *   oracle).  Non-finite x, or a row whose 127/a overflows fp32, gives
+ *   unspecified q.  K must be a multiple of 128; any M >= 1. */
+int tq_quant_act(int dtype, int64_t M, int64_t K, const void *x, int8_t *q, float *a_scale,
+                 void *stream);
+
+/* ---- device: decode GEMV (M <= 16 tokens) ----------------------------- */
+
+/* Workspace bytes tq_gemv / tq_gemv_gate_up_swiglu need for this shape
+ * (0 when the launch does not split K across workgroups).  The workspace
+ * is device memory that must be zero-filled once before its first use;
+ * every call leaves it zero-filled again.  Reusing one workspace for calls
+ * that run concurrently on different streams is not allowed. */
+size_t tq_gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
+
+/* y[M][N] (fp32, device) from the packed blob W (device, tq_packed_bytes
+ * bytes), q[M][K] int8 and a_scale[M] fp32 as produced by tq_quant_act.
+ * 1 <= M <= 16. */
+int tq_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
+            const float *a_scale, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* h[M][N] = silu(y_gate) * y_up, silu(z) = z / (1 + exp(-z)), where y_gate
+ * and y_up are tq_gemv of Wg and Wu (same shape and format) on the same
+ * shared q.  The two weight streams are read in one pass. */
+int tq_gemv_gate_up_swiglu(int fmt, int64_t M, int64_t N, int64_t K, const void *Wg,
+                           const void *Wu, const int8_t *q, const float *a_scale, float *h,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* ---- device: prefill GEMM --------------------------------------------- */
+
+/* Workspace bytes tq_gemm needs (same zero-fill rule as above). */
+size_t tq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
+
+/* y[M][N] as tq_gemv, for any M >= 1.  M <= 16 runs the decode GEMV; larger
+ * M unpacks trits to int8 in LDS and runs int8 MFMA with int32
+ * accumulation per group, then scales per group in fp32. */
+int tq_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
+            const float *a_scale, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- device: parity hooks (same decode / integer core as above) ------- */
+
+/* trits[N][K] (int8, device) decoded on the GPU by the GEMV kernels' decoder. */
+int tq_debug_unpack(int fmt, int64_t N, int64_t K, const void *W, int8_t *trits, void *stream);
+
+/* S[M][N][K/128] int32 (device): the per-group integer sums exactly as the
+ * GEMV (use_gemm_path = 0, M <= 16) or the MFMA GEMM (use_gemm_path = 1)
+ * computes them before scaling. */
+int tq_debug_group_sums(int fmt, int64_t M, int64_t N, int64_t K, const void *W,
+                        const int8_t *q, int32_t *S, int use_gemm_path, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,184 @@
+"""Python binding of libtq (ternary-weight GEMV/GEMM for AMD gfx950).
+
+Argument marshalling only: every step of the computation runs in libtq's HIP
+kernels (or, for packing, in its host C++ code).  PyTorch supplies device
+memory and streams.  The functions carry the C ABI's names (see
+include/tq.h); device tensors must be contiguous, on the GPU and 16-byte
+aligned.  If libtq.so is missing the import fails loudly -- there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+TQ_FMT_B3 = 0
+TQ_FMT_2B = 1
+TQ_F16 = 0
+TQ_F32 = 1
+GROUP = 128
+GEMV_MAX_M = 16
+
+_STATUS = {0: "TQ_OK", -1: "TQ_ERR_NULL", -2: "TQ_ERR_SHAPE", -3: "TQ_ERR_ALIGN",
+           -4: "TQ_ERR_VALUE", -5: "TQ_ERR_FORMAT", -6: "TQ_ERR_DTYPE", -7: "TQ_ERR_SIZE",
+           -8: "TQ_ERR_HIP"}
+
+EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant_act",
+           "tq_gemv_workspace_bytes", "tq_gemv", "tq_gemv_gate_up_swiglu",
+           "tq_gemm_workspace_bytes", "tq_gemm", "tq_debug_unpack", "tq_debug_group_sums")
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libtq.so not built ({LIB_PATH}); run ternary_weight_base_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "tq_status_str": ([I], ctypes.c_char_p),
+        "tq_packed_bytes": ([I, I64, I64], SZ),
+        "tq_pack": ([I, I64, I64, P, P, P, SZ], I),
+        "tq_unpack": ([I, I64, I64, P, SZ, P, P], I),
+        "tq_quant_act": ([I, I64, I64, P, P, P, P], I),
+        "tq_gemv_workspace_bytes": ([I, I64, I64, I64], SZ),
+        "tq_gemv": ([I, I64, I64, I64, P, P, P, P, P, SZ, P], I),
+        "tq_gemv_gate_up_swiglu": ([I, I64, I64, I64, P, P, P, P, P, P, SZ, P], I),
+        "tq_gemm_workspace_bytes": ([I, I64, I64, I64], SZ),
+        "tq_gemm": ([I, I64, I64, I64, P, P, P, P, P, SZ, P], I),
+        "tq_debug_unpack": ([I, I64, I64, P, P, P], I),
+        "tq_debug_group_sums": ([I, I64, I64, I64, P, P, P, I, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
+lib = _load()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise TQError(rc, what)
+
+
+def _ptr(t) -> int:
+    """Device address of a torch tensor (or None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def tq_status_str(status: int) -> str:
+    return lib.tq_status_str(status).decode()
+
+
+# ---- host: packed format ------------------------------------------------
+
+def tq_packed_bytes(fmt: int, N: int, K: int) -> int:
+    return int(lib.tq_packed_bytes(fmt, N, K))
+
+
+def tq_pack(fmt: int, trits: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """trits int8 [N][K], scales fp16 bits uint16 [N][K/128] -> packed uint8 blob (host)."""
+    t = np.ascontiguousarray(trits, dtype=np.int8)
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    N, K = t.shape
+    nbytes = tq_packed_bytes(fmt, N, K)
+    out = np.empty(max(nbytes, 1), dtype=np.uint8)
+    _check(lib.tq_pack(fmt, N, K, t.ctypes.data, s.ctypes.data, out.ctypes.data, nbytes),
+           "tq_pack")
+    return out
+
+
+def tq_unpack(fmt: int, blob: np.ndarray, N: int, K: int):
+    """Inverse of tq_pack -> (trits int8 [N][K], scales uint16 [N][K/128])."""
+    b = np.ascontiguousarray(blob, dtype=np.uint8)
+    t = np.empty((N, K), dtype=np.int8)
+    s = np.empty((N, K // GROUP), dtype=np.uint16)
+    _check(lib.tq_unpack(fmt, N, K, b.ctypes.data, b.size, t.ctypes.data, s.ctypes.data),
+           "tq_unpack")
+    return t, s
+
+
+# ---- device ---------------------------------------------------------------
+
+def tq_quant_act(x, q, a_scale, stream=None) -> None:
+    """x [M][K] fp16/fp32 (device) -> q int8 [M][K], a_scale fp32 [M]."""
+    import torch
+    dtype = {torch.float16: TQ_F16, torch.float32: TQ_F32}.get(x.dtype, -1)
+    M, K = x.shape
+    _check(lib.tq_quant_act(dtype, M, K, _ptr(x), _ptr(q), _ptr(a_scale), _stream(stream)),
+           "tq_quant_act")
+
+
+def tq_gemv_workspace_bytes(fmt: int, M: int, N: int, K: int) -> int:
+    return int(lib.tq_gemv_workspace_bytes(fmt, M, N, K))
+
+
+def tq_gemm_workspace_bytes(fmt: int, M: int, N: int, K: int) -> int:
+    return int(lib.tq_gemm_workspace_bytes(fmt, M, N, K))
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
+
+
+def tq_gemv(fmt, M, N, K, W, q, a_scale, y, ws=None, stream=None) -> None:
+    wp, wb = _ws(ws)
+    _check(lib.tq_gemv(fmt, M, N, K, _ptr(W), _ptr(q), _ptr(a_scale), _ptr(y), wp, wb,
+                       _stream(stream)), "tq_gemv")
+
+
+def tq_gemv_gate_up_swiglu(fmt, M, N, K, Wg, Wu, q, a_scale, h, ws=None, stream=None) -> None:
+    wp, wb = _ws(ws)
+    _check(lib.tq_gemv_gate_up_swiglu(fmt, M, N, K, _ptr(Wg), _ptr(Wu), _ptr(q), _ptr(a_scale),
+                                      _ptr(h), wp, wb, _stream(stream)), "tq_gemv_gate_up_swiglu")
+
+
+def tq_gemm(fmt, M, N, K, W, q, a_scale, y, ws=None, stream=None) -> None:
+    wp, wb = _ws(ws)
+    _check(lib.tq_gemm(fmt, M, N, K, _ptr(W), _ptr(q), _ptr(a_scale), _ptr(y), wp, wb,
+                       _stream(stream)), "tq_gemm")
+
+
+def tq_debug_unpack(fmt, N, K, W, trits, stream=None) -> None:
+    _check(lib.tq_debug_unpack(fmt, N, K, _ptr(W), _ptr(trits), _stream(stream)),
+           "tq_debug_unpack")
+
+
+def tq_debug_group_sums(fmt, M, N, K, W, q, S, use_gemm_path=False, stream=None) -> None:
+    _check(lib.tq_debug_group_sums(fmt, M, N, K, _ptr(W), _ptr(q), _ptr(S), int(use_gemm_path),
+                                   _stream(stream)), "tq_debug_group_sums")
+
+
+def workspace(fmt: int, M: int, N: int, K: int, device="cuda"):
+    """A zero-filled workspace tensor sized for tq_gemv / tq_gemm on this shape
+    (None when the shape needs none).  Allocation is the caller's: this helper
+    uses torch, never the library."""
+    import torch
+    nbytes = max(tq_gemv_workspace_bytes(fmt, min(M, GEMV_MAX_M), N, K),
+                 tq_gemm_workspace_bytes(fmt, M, N, K))
+    if nbytes == 0:
+        return None
+    return torch.zeros((nbytes + 15) // 16 * 4, dtype=torch.int32, device=device)

@@ -1,0 +1,914 @@
+// tq_kernels.hip -- device half of libtq for AMD CDNA4 (gfx950).
+//
+// Method: trits {-1,0,+1} (pwwt.cn/news/4940051, section 1.1) in groups of
+// 128 with one fp16 scale applied after the signed sum ("三值权重 27B 压到
+// 5.9GB｜本地部署成本账单重算", section 三); per-row Q8 activations and, per
+// group, decode in registers -> integer dot -> scale ("Ternary Bonsai 2 27B：
+// 8GB 显卡硬塞 27B 三元模型…", sections "Decode 为什么只能算一般" and
+// "后面还有没有优化空间").  Decode (batch 1..16) is a matrix-vector product
+// bound by streaming the packed weights; prefill (many tokens) is a dense
+// contraction and runs on int8 MFMA (same page, "Decode 为什么只能算一般").
+//
+// Kernels:
+//   quant_kernel   per-row absmax -> int8, bit-exact IEEE fp32
+//   gemv_kernel    one lane per weight row, wave-uniform activations in
+//                  SGPRs, packed weights streamed with 16/12-byte loads,
+//                  B3 bytes decoded by an LDS digit table, 2B codes by masks;
+//                  waves and workgroups split K, with a deterministic
+//                  last-workgroup reduction; optional fused SwiGLU epilogue
+//   gemm_kernel    trits decoded to int8 in LDS, v_mfma_i32_16x16x64_i8 per
+//                  group, fp32 rescale per group
+//   unpack_kernel  parity hook: the GEMV decoder's trits
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+#include "tq_layout.h"
+
+using tq::Layout;
+
+namespace {
+
+constexpr int kLutCopies = 32;   // one table copy per lane of a half wave
+constexpr int kLutEntries = 256; // byte values; 243..255 map to zero trits
+constexpr int kWavesMax = 8;     // waves per GEMV workgroup
+constexpr int kGsMax = 8;        // groups per wave slice (all prefetched)
+#ifndef TQ_GEMV_TARGET_WAVES
+#define TQ_GEMV_TARGET_WAVES 4096  // 16 waves per CU on 256 CUs
+#endif
+
+typedef long v2l __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+__device__ __forceinline__ uint32_t perm_b32(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+__device__ __forceinline__ float half_bits(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// ---------------------------------------------------------------------
+// B3 digit table.  For byte value v (0..242): .lo holds the trits of base-3
+// digits 0..3 of v (one signed byte each), .hi the trit of digit 4 in byte 0;
+// values 243..255 (never produced by the packer) decode to zero trits.
+// The table is a compile-time constant; each workgroup copies it into LDS
+// 32 times, entry v of copy c at byte (v * 32 + c) * 8.  Lane l reads copy
+// l % 32, so the 32 lanes served together hit 32 distinct bank pairs
+// whatever byte values they hold.
+// ---------------------------------------------------------------------
+struct B3Table {
+  uint32_t lo[kLutEntries], hi[kLutEntries];
+  constexpr B3Table() : lo(), hi() {
+    for (int v = 0; v < 243; v++) {
+      int x = v;
+      uint32_t l = 0;
+      for (int i = 0; i < 4; i++) {
+        l |= (uint32_t)(uint8_t)(int8_t)(x % 3 - 1) << (8 * i);
+        x /= 3;
+      }
+      lo[v] = l;
+      hi[v] = (uint32_t)(uint8_t)(int8_t)(x - 1);
+    }
+  }
+};
+__device__ constexpr B3Table kB3Table{};
+
+__device__ __forceinline__ void fill_b3_lut(uint2 *lut) {
+  for (int idx = threadIdx.x; idx < kLutEntries * kLutCopies; idx += blockDim.x) {
+    const int v = idx / kLutCopies;
+    lut[idx] = make_uint2(kB3Table.lo[v], kB3Table.hi[v]);
+  }
+}
+
+// Look up byte k of `word`: one v_perm builds the LDS address
+// (byte value in bits 8..15, the lane's copy offset in bits 0..7).
+template <int k>
+__device__ __forceinline__ uint2 lut_lookup(const uint2 *lut, uint32_t word, uint32_t laneoff) {
+  constexpr uint32_t sel = 0x0C0C0000u | ((4u + k) << 8);
+  uint32_t addr = perm_b32(word, laneoff, sel);
+  return *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(lut) + addr);
+}
+
+template <int j>
+__device__ __forceinline__ uint2 b3_byte(const uint2 *lut, const uint32_t (&w)[7],
+                                         uint32_t laneoff) {
+  return lut_lookup<j & 3>(lut, w[j >> 2], laneoff);
+}
+
+// Activations of one group for MT rows, as 32 words per row: either held in
+// (scalar) registers, or read through wave-uniform pointers on use.
+template <int MT>
+struct XRegs {
+  uint32_t v[MT][32];
+  __device__ __forceinline__ uint32_t get(int m, int i) const { return v[m][i]; }
+};
+template <int MT>
+struct XPtrs {
+  const uint32_t *__restrict__ p[MT];
+  __device__ __forceinline__ uint32_t get(int m, int i) const { return p[m][i]; }
+};
+
+// Integer core of one B3 group for MT activation rows.
+//   w[0..3]: device bytes 0..15, w[4..6]: bytes 16..25 and the scale.
+// byte j < 25: digits 0..3 pair with activation word j, digit 4 with byte
+// j % 4 of word 25 + j / 4; byte 25: digits 1..3 pair with bytes 1..3 of
+// word 31 (its digit 0 is a zero-trit padding digit).
+template <int MT, typename XS>
+__device__ __forceinline__ void b3_group(const uint2 *lut, uint32_t laneoff,
+                                         const uint32_t (&w)[7], const XS &x, int (&S)[MT]) {
+#define TQ_B3_BYTE(J)                                                   \
+  {                                                                     \
+    const uint2 e = b3_byte<J>(lut, w, laneoff);                        \
+    _Pragma("unroll") for (int m = 0; m < MT; m++) {                    \
+      S[m] = sdot4(e.x, x.get(m, J), S[m]);                             \
+      S[m] = sdot4(e.y, x.get(m, 25 + (J >> 2)) >> (8 * (J & 3)), S[m]); \
+    }                                                                   \
+  }
+  TQ_B3_BYTE(0) TQ_B3_BYTE(1) TQ_B3_BYTE(2) TQ_B3_BYTE(3) TQ_B3_BYTE(4)
+  TQ_B3_BYTE(5) TQ_B3_BYTE(6) TQ_B3_BYTE(7) TQ_B3_BYTE(8) TQ_B3_BYTE(9)
+  TQ_B3_BYTE(10) TQ_B3_BYTE(11) TQ_B3_BYTE(12) TQ_B3_BYTE(13) TQ_B3_BYTE(14)
+  TQ_B3_BYTE(15) TQ_B3_BYTE(16) TQ_B3_BYTE(17) TQ_B3_BYTE(18) TQ_B3_BYTE(19)
+  TQ_B3_BYTE(20) TQ_B3_BYTE(21) TQ_B3_BYTE(22) TQ_B3_BYTE(23) TQ_B3_BYTE(24)
+#undef TQ_B3_BYTE
+  const uint2 e = b3_byte<25>(lut, w, laneoff);
+#pragma unroll
+  for (int m = 0; m < MT; m++) S[m] = sdot4(e.x, x.get(m, 31), S[m]);
+}
+
+// Integer core of one 2B group.  Device byte 4c' + c, bits 2s hold
+// k = 16c' + 4s + c, so field s of word c' pairs with activation word
+// 4c' + s.  Codes d = t + 1 are dotted directly (fields masked in place, so
+// field s arrives multiplied by 4^s, or by 16 for s = 3 after a 2-bit shift)
+// and the group's activation sum is subtracted: sum t*x = sum d*x - sum x.
+template <int MT, typename XS>
+__device__ __forceinline__ void tb_group(const uint32_t (&w)[9], const XS &x,
+                                         const int (&xsum)[MT], int (&S)[MT]) {
+  int a1[MT], a4[MT], a16[MT];
+#pragma unroll
+  for (int m = 0; m < MT; m++) a1[m] = a4[m] = a16[m] = 0;
+#pragma unroll
+  for (int c = 0; c < 8; c++) {
+    const uint32_t v = w[c];
+    const uint32_t f0 = v & 0x03030303u, f1 = v & 0x0C0C0C0Cu, f2 = v & 0x30303030u,
+                   f3 = (v >> 2) & 0x30303030u;
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+      a1[m] = sdot4(f0, x.get(m, 4 * c + 0), a1[m]);
+      a4[m] = sdot4(f1, x.get(m, 4 * c + 1), a4[m]);
+      a16[m] = sdot4(f2, x.get(m, 4 * c + 2), a16[m]);
+      a16[m] = sdot4(f3, x.get(m, 4 * c + 3), a16[m]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MT; m++) S[m] = a1[m] + (a4[m] >> 2) + (a16[m] >> 4) - xsum[m];
+}
+
+// ---------------------------------------------------------------------
+// Activation quantiser: one workgroup per row.
+// ---------------------------------------------------------------------
+template <typename T>
+struct Vec;
+template <>
+struct Vec<_Float16> {
+  static constexpr int n = 8;
+  __device__ static void load(const _Float16 *p, float (&v)[8]) {
+    uint4 u = *reinterpret_cast<const uint4 *>(p);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = half_bits(w[i] & 0xffffu);
+      v[2 * i + 1] = half_bits(w[i] >> 16);
+    }
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int n = 4;
+  __device__ static void load(const float *p, float (&v)[4]) {
+    float4 u = *reinterpret_cast<const float4 *>(p);
+    v[0] = u.x;
+    v[1] = u.y;
+    v[2] = u.z;
+    v[3] = u.w;
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void quant_kernel(const T *__restrict__ x, int8_t *__restrict__ q,
+                                                    float *__restrict__ scale, int K) {
+  constexpr int V = Vec<T>::n;
+  const int m = blockIdx.x;
+  const T *xr = x + (size_t)m * K;
+  int8_t *qr = q + (size_t)m * K;
+  float a = 0.0f;
+  for (int k = threadIdx.x * V; k < K; k += 256 * V) {
+    float v[V];
+    Vec<T>::load(xr + k, v);
+#pragma unroll
+    for (int i = 0; i < V; i++) a = fmaxf(a, fabsf(v[i]));
+  }
+  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const bool zero = (a == 0.0f);
+  const float inv = zero ? 0.0f : 127.0f / a;  // IEEE division, round to nearest even
+  for (int k = threadIdx.x * V; k < K; k += 256 * V) {
+    float v[V];
+    Vec<T>::load(xr + k, v);
+    uint32_t packed[V / 4];
+#pragma unroll
+    for (int i = 0; i < V / 4; i++) packed[i] = 0;
+#pragma unroll
+    for (int i = 0; i < V; i++) {
+      float r = rintf(v[i] * inv);  // one rounded product, then ties-to-even
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+      int qi = zero ? 0 : (int)r;
+      packed[i / 4] |= (uint32_t)(uint8_t)(int8_t)qi << (8 * (i % 4));
+    }
+    if (V == 8)
+      *reinterpret_cast<uint2 *>(qr + k) = make_uint2(packed[0], packed[V / 4 - 1]);
+    else
+      *reinterpret_cast<uint32_t *>(qr + k) = packed[0];
+  }
+  if (threadIdx.x == 0) scale[m] = zero ? 0.0f : a / 127.0f;
+}
+
+// ---------------------------------------------------------------------
+// Decode GEMV.
+//   grid  = NB * C workgroups; workgroup (b, c) covers weight block b (64
+//           rows) and waves c*nw .. c*nw + nw - 1 of the block's K slices;
+//   wave  = one slice of gs consecutive groups; lane = one weight row.
+// Every group of the slice is loaded before any math (up to kGsMax groups in
+// flight per wave).  Activations are wave-uniform and live in SGPRs; for one
+// row the next group's 32 words are fetched while the current group runs.
+// NMAT = 2 runs gate and up together and applies SwiGLU at the end.
+// SUMS writes the int32 group sums instead of y (parity hook).
+//
+// K split across workgroups (C > 1): each workgroup stores its partial sums
+// with device-scope atomic stores, waits until they have completed, then
+// bumps a per-block counter with a device-scope atomic; the workgroup that
+// sees C - 1 adds the C partials in order (device-scope atomic loads), writes
+// y and re-zeroes the counter.  All cross-workgroup data moves through
+// device-coherent atomic accesses, so no cache-wide release/acquire fence is
+// needed (on this multi-die GPU those write back and invalidate the whole L2).
+// ---------------------------------------------------------------------
+template <int FMT, int MT, int NMAT, bool SUMS>
+__global__ __launch_bounds__(512) void gemv_kernel(
+    const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1,
+    const int8_t *__restrict__ q, const float *__restrict__ a_scale, float *__restrict__ out,
+    int32_t *__restrict__ sums, float *__restrict__ partials, uint32_t *__restrict__ counters,
+    int M, int N, int K, int gs, int nw, int C) {
+  constexpr int kLutSlots = FMT == 0 ? kLutEntries * kLutCopies : 1;
+  constexpr int kXsumStride = kWavesMax * kGsMax;
+  constexpr int kXsumSlots = FMT == 1 ? MT * kXsumStride : 1;
+  constexpr int WPG = FMT == 0 ? 7 : 9;  // words per (row, group) held in registers
+  __shared__ uint2 lut[kLutSlots];
+  __shared__ int xsum_lds[kXsumSlots];
+  __shared__ float red[SUMS ? 1 : NMAT * MT * kWavesMax * 64];
+  __shared__ int last_flag;
+
+  const Layout L(FMT, N, K);
+  const int G = (int)L.G;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform across the wave; say so, so that everything
+  // derived from it (group indices, activation addresses) stays scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x / C, c = blockIdx.x - b * C;
+  const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
+  const int gwg = c * nw * gs;                    // first group of this workgroup
+  const int g0 = gwg + wave * gs;                 // first group of this wave
+  const int ng = max(0, min(G, g0 + gs) - g0);    // groups of this wave
+  const bool lane_ok = lane < Wb;
+  const uint8_t *Wm[2] = {W0, W1};
+
+  // ---- 1. issue the loads of every group of the slice -------------------
+  uint32_t wd[NMAT][kGsMax][WPG];
+#pragma unroll
+  for (int mat = 0; mat < NMAT; mat++) {
+#pragma unroll
+    for (int i = 0; i < kGsMax; i++) {
+#pragma unroll
+      for (int k = 0; k < WPG; k++) wd[mat][i][k] = 0;
+      if (i < ng && lane_ok) {
+        const uint8_t *gb = Wm[mat] + L.group_base(b, g0 + i);
+        const uint4 A = *reinterpret_cast<const uint4 *>(gb + lane * 16);
+        wd[mat][i][0] = A.x;
+        wd[mat][i][1] = A.y;
+        wd[mat][i][2] = A.z;
+        wd[mat][i][3] = A.w;
+        if (FMT == 0) {
+          const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + lane * 12);
+          wd[mat][i][4] = pb[0];
+          wd[mat][i][5] = pb[1];
+          wd[mat][i][6] = pb[2];
+        } else {
+          const uint4 B = *reinterpret_cast<const uint4 *>(gb + Wb * 16 + lane * 16);
+          wd[mat][i][4] = B.x;
+          wd[mat][i][5] = B.y;
+          wd[mat][i][6] = B.z;
+          wd[mat][i][7] = B.w;
+          wd[mat][i][8] = *reinterpret_cast<const uint16_t *>(gb + Wb * 32 + lane * 2);
+        }
+      }
+    }
+  }
+
+  // ---- 2. tables, while the loads are in flight --------------------------
+  if (FMT == 0) {
+    fill_b3_lut(lut);
+  } else {
+    // activation sum of every group this workgroup touches, per token row
+    const int ngw = max(0, min(G - gwg, nw * gs));
+    for (int p = tid; p < MT * ngw; p += blockDim.x) {
+      const int m = p / ngw, gl = p - m * ngw;
+      const uint4 *xp = reinterpret_cast<const uint4 *>(q + (size_t)min(m, M - 1) * K +
+                                                        (size_t)(gwg + gl) * tq::kGroup);
+      uint4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; k++) v[k] = xp[k];
+      int sacc = 0;
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        sacc = sdot4(v[k].x, 0x01010101u, sacc);
+        sacc = sdot4(v[k].y, 0x01010101u, sacc);
+        sacc = sdot4(v[k].z, 0x01010101u, sacc);
+        sacc = sdot4(v[k].w, 0x01010101u, sacc);
+      }
+      xsum_lds[m * kXsumStride + gl] = sacc;
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. decode + integer dot + scale, group by group -------------------
+  const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
+  const uint32_t *__restrict__ xrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; m++)
+    xrow[m] = reinterpret_cast<const uint32_t *>(q + (size_t)min(m, M - 1) * K);
+
+  float acc[NMAT][MT];
+#pragma unroll
+  for (int mat = 0; mat < NMAT; mat++)
+#pragma unroll
+    for (int m = 0; m < MT; m++) acc[mat][m] = 0.0f;
+
+  auto do_group = [&](int i, const auto &xs) {
+    const int g = g0 + i;
+    int xsum[MT];
+    if (FMT == 1) {
+#pragma unroll
+      for (int m = 0; m < MT; m++) xsum[m] = xsum_lds[m * kXsumStride + (g - gwg)];
+    }
+#pragma unroll
+    for (int mat = 0; mat < NMAT; mat++) {
+      int S[MT];
+#pragma unroll
+      for (int m = 0; m < MT; m++) S[m] = 0;
+      float sc;
+      if constexpr (FMT == 0) {
+        const uint32_t w[7] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2], wd[mat][i][3],
+                               wd[mat][i][4], wd[mat][i][5], wd[mat][i][6]};
+        b3_group<MT>(lut, laneoff, w, xs, S);
+        sc = half_bits(wd[mat][i][6] >> 16);
+      } else {
+        const uint32_t w[9] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2],
+                               wd[mat][i][3], wd[mat][i][4], wd[mat][i][5],
+                               wd[mat][i][6], wd[mat][i][7], wd[mat][i][8]};
+        tb_group<MT>(w, xs, xsum, S);
+        sc = half_bits(wd[mat][i][8]);
+      }
+      if (SUMS) {
+        if (lane < rows) {
+          const size_t n = (size_t)b * tq::kBlockRows + lane;
+#pragma unroll
+          for (int m = 0; m < MT; m++)
+            if (m < M) sums[((size_t)m * N + n) * G + g] = S[m];
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < MT; m++) acc[mat][m] = fmaf(sc, (float)S[m], acc[mat][m]);
+      }
+    }
+  };
+
+  if constexpr (MT == 1) {
+    // one token: keep the group's 32 activation words in SGPRs and fetch the
+    // next group's while this one is computed
+    XRegs<1> xa, xb;
+    if (ng > 0) {
+#pragma unroll
+      for (int k = 0; k < 32; k++) xa.v[0][k] = xrow[0][32 * g0 + k];
+    }
+#pragma unroll
+    for (int i = 0; i < kGsMax; i++) {
+      if (i < ng) {
+        if (i + 1 < ng) {
+#pragma unroll
+          for (int k = 0; k < 32; k++) xb.v[0][k] = xrow[0][32 * (g0 + i + 1) + k];
+        }
+        do_group(i, xa);
+        xa = xb;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kGsMax; i++) {
+      if (i < ng) {
+        XPtrs<MT> xp;
+#pragma unroll
+        for (int m = 0; m < MT; m++) xp.p[m] = xrow[m] + 32 * (g0 + i);
+        do_group(i, xp);
+      }
+    }
+  }
+  if (SUMS) return;
+
+  // ---- 4. reduce the slices: waves of this workgroup, in wave order ------
+#pragma unroll
+  for (int mat = 0; mat < NMAT; mat++)
+#pragma unroll
+    for (int m = 0; m < MT; m++) red[((mat * MT + m) * kWavesMax + wave) * 64 + lane] = acc[mat][m];
+  __syncthreads();
+
+  // One (m, row) output per iteration; MT * 64 outputs may exceed the
+  // workgroup's thread count, so every phase below loops.
+  if (C > 1) {
+    for (int o = tid; o < MT * 64; o += blockDim.x) {
+      const int m_out = o >> 6, r_out = o & 63;
+      if (m_out >= M || r_out >= rows) continue;
+      const size_t n_out = (size_t)b * tq::kBlockRows + r_out;
+#pragma unroll
+      for (int mat = 0; mat < NMAT; mat++) {
+        float sum = 0.0f;
+        for (int wv = 0; wv < nw; wv++) sum += red[((mat * MT + m_out) * kWavesMax + wv) * 64 + r_out];
+        __hip_atomic_store(&partials[(((size_t)c * NMAT + mat) * M + m_out) * N + n_out], sum,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
+    __syncthreads();                // ... and so have every other wave's
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(&counters[b], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      last_flag = (prev == (uint32_t)(C - 1));
+    }
+    __syncthreads();
+    if (!last_flag) return;
+  }
+  for (int o = tid; o < MT * 64; o += blockDim.x) {
+    const int m_out = o >> 6, r_out = o & 63;
+    if (m_out >= M || r_out >= rows) continue;
+    const size_t n_out = (size_t)b * tq::kBlockRows + r_out;
+    float tot[NMAT];
+#pragma unroll
+    for (int mat = 0; mat < NMAT; mat++) {
+      float sum = 0.0f;
+      if (C > 1) {
+        for (int cc = 0; cc < C; cc++)
+          sum += __hip_atomic_load(&partials[(((size_t)cc * NMAT + mat) * M + m_out) * N + n_out],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        for (int wv = 0; wv < nw; wv++) sum += red[((mat * MT + m_out) * kWavesMax + wv) * 64 + r_out];
+      }
+      tot[mat] = sum;
+    }
+    const float a = a_scale[m_out];
+    float y;
+    if (NMAT == 1) {
+      y = a * tot[0];
+    } else {
+      const float yg = a * tot[0], yu = a * tot[NMAT - 1];
+      y = yg / (1.0f + expf(-yg)) * yu;
+    }
+    out[(size_t)m_out * N + n_out] = y;
+  }
+  if (C > 1 && tid == 0)
+    __hip_atomic_store(&counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------
+// Parity hook: decode trits exactly as the GEMV does.
+// grid (NB, G), 64 threads: lane = row of the block.
+// ---------------------------------------------------------------------
+template <int FMT>
+__global__ __launch_bounds__(64) void unpack_kernel(const uint8_t *__restrict__ W,
+                                                    int8_t *__restrict__ t, int N, int K) {
+  __shared__ uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
+  const Layout L(FMT, N, K);
+  const int b = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+  if (FMT == 0) fill_b3_lut(lut);
+  __syncthreads();
+  const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
+  if (lane >= rows) return;
+  const uint8_t *gb = W + L.group_base(b, g);
+  int8_t *tr = t + ((size_t)b * tq::kBlockRows + lane) * K + (size_t)g * tq::kGroup;
+  if (FMT == 0) {
+    const uint4 A = *reinterpret_cast<const uint4 *>(gb + lane * 16);
+    const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + lane * 12);
+    const uint32_t w[7] = {A.x, A.y, A.z, A.w, pb[0], pb[1], pb[2]};
+    const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
+    uint2 e[26];
+#define TQ_E(J) e[J] = b3_byte<J>(lut, w, laneoff);
+    TQ_E(0) TQ_E(1) TQ_E(2) TQ_E(3) TQ_E(4) TQ_E(5) TQ_E(6) TQ_E(7) TQ_E(8) TQ_E(9)
+    TQ_E(10) TQ_E(11) TQ_E(12) TQ_E(13) TQ_E(14) TQ_E(15) TQ_E(16) TQ_E(17) TQ_E(18)
+    TQ_E(19) TQ_E(20) TQ_E(21) TQ_E(22) TQ_E(23) TQ_E(24) TQ_E(25)
+#undef TQ_E
+    for (int j = 0; j < 25; j++) {
+      *reinterpret_cast<uint32_t *>(tr + 4 * j) = e[j].x;
+      tr[100 + j] = (int8_t)(e[j].y & 0xff);
+    }
+    tr[125] = (int8_t)((e[25].x >> 8) & 0xff);
+    tr[126] = (int8_t)((e[25].x >> 16) & 0xff);
+    tr[127] = (int8_t)(e[25].x >> 24);
+  } else {
+    const uint4 A = *reinterpret_cast<const uint4 *>(gb + lane * 16);
+    const uint4 B = *reinterpret_cast<const uint4 *>(gb + Wb * 16 + lane * 16);
+    const uint32_t w[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+    for (int c = 0; c < 8; c++) {
+      for (int s = 0; s < 4; s++) {
+        // field s of every byte -> code d, trit d - 1 (v_perm as a 4-entry table)
+        const uint32_t code = (w[c] >> (2 * s)) & 0x03030303u;
+        *reinterpret_cast<uint32_t *>(tr + 16 * c + 4 * s) = perm_b32(0u, 0x000100FFu, code);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------
+// Prefill GEMM.  grid (NB, ceil(M/128)), 256 threads (4 waves).
+// Per group: the block's 64 weight rows x 128 trits are decoded to int8 in
+// LDS (canonical k order), each wave multiplies its 32 activation rows by
+// them with 2 x 4 x 2 v_mfma_i32_16x16x64_i8, and rescales the int32 group
+// sums by s[n][g] into fp32 accumulators.
+// ---------------------------------------------------------------------
+constexpr int kGemmBM = 128;
+constexpr int kBtStride = 144;  // 128 trits + 16 bytes of padding per row
+
+template <int FMT, bool SUMS>
+__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W,
+                                                   const int8_t *__restrict__ q,
+                                                   const float *__restrict__ a_scale,
+                                                   float *__restrict__ out,
+                                                   int32_t *__restrict__ sums, int M, int N, int K) {
+  __shared__ uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
+  __shared__ __attribute__((aligned(16))) int8_t Bt[64 * kBtStride];
+  __shared__ float bscale[64];
+
+  const Layout L(FMT, N, K);
+  const int G = (int)L.G;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = blockIdx.x, m0 = blockIdx.y * kGemmBM;
+  const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
+  if (FMT == 0) fill_b3_lut(lut);
+
+  // decode role: row r of the block, part p
+  const int dr = tid >> 2, dp = tid & 3;
+  const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
+
+  // MFMA role
+  const int li = lane & 15, slot = lane >> 4;
+  v4i acc32[2][4];
+  float accf[2][4][4];
+#pragma unroll
+  for (int ms = 0; ms < 2; ms++)
+#pragma unroll
+    for (int ns = 0; ns < 4; ns++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) accf[ms][ns][v] = 0.0f;
+
+  for (int g = 0; g < G; g++) {
+    __syncthreads();  // previous group's Bt fully consumed (and the table built)
+    // ---- decode this group's 64 x 128 trits into Bt ---------------------
+    int8_t *brow = Bt + dr * kBtStride;
+    if (dr < Wb) {
+      const uint8_t *gb = W + L.group_base(b, g);
+      if (FMT == 0) {
+        // dwords p and p + 4 of the row's 7: bytes 4p..4p+3 and 16+4p..
+        uint32_t w[7];
+        const uint4 A = *reinterpret_cast<const uint4 *>(gb + dr * 16);
+        const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + dr * 12);
+        w[0] = A.x; w[1] = A.y; w[2] = A.z; w[3] = A.w;
+        w[4] = pb[0]; w[5] = pb[1]; w[6] = pb[2];
+#define TQ_DEC(J)                                                       \
+  {                                                                     \
+    uint2 e = b3_byte<J>(lut, w, laneoff);                              \
+    *reinterpret_cast<uint32_t *>(brow + 4 * (J)) = e.x;                \
+    brow[100 + (J)] = (int8_t)(e.y & 0xff);                             \
+  }
+        if (dp == 0) { TQ_DEC(0) TQ_DEC(1) TQ_DEC(2) TQ_DEC(3) TQ_DEC(16) TQ_DEC(17) TQ_DEC(18) }
+        if (dp == 1) { TQ_DEC(4) TQ_DEC(5) TQ_DEC(6) TQ_DEC(7) TQ_DEC(19) TQ_DEC(20) TQ_DEC(21) }
+        if (dp == 2) { TQ_DEC(8) TQ_DEC(9) TQ_DEC(10) TQ_DEC(11) TQ_DEC(22) TQ_DEC(23) }
+        if (dp == 3) {
+          TQ_DEC(12) TQ_DEC(13) TQ_DEC(14) TQ_DEC(15) TQ_DEC(24)
+          uint2 e = b3_byte<25>(lut, w, laneoff);
+          brow[125] = (int8_t)((e.x >> 8) & 0xff);
+          brow[126] = (int8_t)((e.x >> 16) & 0xff);
+          brow[127] = (int8_t)(e.x >> 24);
+          bscale[dr] = half_bits(w[6] >> 16);
+        }
+#undef TQ_DEC
+      } else {
+        const uint4 A = *reinterpret_cast<const uint4 *>(gb + dr * 16);
+        const uint4 B = *reinterpret_cast<const uint4 *>(gb + Wb * 16 + dr * 16);
+        const uint32_t w[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+#pragma unroll
+        for (int cc = 0; cc < 2; cc++) {
+          const int c = dp + 4 * cc;
+#pragma unroll
+          for (int s = 0; s < 4; s++) {
+            const uint32_t code = (w[c] >> (2 * s)) & 0x03030303u;
+            *reinterpret_cast<uint32_t *>(brow + 16 * c + 4 * s) = perm_b32(0u, 0x000100FFu, code);
+          }
+        }
+        if (dp == 0) bscale[dr] = half_bits(*reinterpret_cast<const uint16_t *>(gb + Wb * 32 + dr * 2));
+      }
+    } else {
+      for (int k = dp * 32; k < dp * 32 + 32; k += 4) *reinterpret_cast<uint32_t *>(brow + k) = 0;
+      if (dp == 0) bscale[dr] = 0.0f;
+    }
+    __syncthreads();
+
+    // ---- MFMA: wave rows m0 + 32*wave + 16*ms + i, all 64 columns --------
+    v2l af[2][2];
+#pragma unroll
+    for (int ms = 0; ms < 2; ms++) {
+      const int row = m0 + 32 * wave + 16 * ms + li;
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        if (row < M) {
+          const int8_t *p = q + (size_t)row * K + (size_t)g * 128 + 64 * ks + 16 * slot;
+          af[ms][ks] = *reinterpret_cast<const v2l *>(p);
+        } else {
+          af[ms][ks] = v2l{0, 0};
+        }
+      }
+    }
+#pragma unroll
+    for (int ms = 0; ms < 2; ms++)
+#pragma unroll
+      for (int ns = 0; ns < 4; ns++) acc32[ms][ns] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      v2l bf[4];
+#pragma unroll
+      for (int ns = 0; ns < 4; ns++)
+        bf[ns] = *reinterpret_cast<const v2l *>(Bt + (16 * ns + li) * kBtStride + 64 * ks + 16 * slot);
+#pragma unroll
+      for (int ms = 0; ms < 2; ms++)
+#pragma unroll
+        for (int ns = 0; ns < 4; ns++)
+          acc32[ms][ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[ms][ks], bf[ns], acc32[ms][ns], 0, 0, 0);
+    }
+    // ---- output element (row 4*slot + v, column li) of each 16x16 tile ---
+#pragma unroll
+    for (int ns = 0; ns < 4; ns++) {
+      const int col = 16 * ns + li;
+      const float sc = bscale[col];
+#pragma unroll
+      for (int ms = 0; ms < 2; ms++) {
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          if (SUMS) {
+            const int row = m0 + 32 * wave + 16 * ms + 4 * slot + v;
+            if (row < M && col < rows)
+              sums[((size_t)row * N + (size_t)b * tq::kBlockRows + col) * G + g] = acc32[ms][ns][v];
+          } else {
+            accf[ms][ns][v] = fmaf(sc, (float)acc32[ms][ns][v], accf[ms][ns][v]);
+          }
+        }
+      }
+    }
+  }
+  if (SUMS) return;
+#pragma unroll
+  for (int ms = 0; ms < 2; ms++)
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int row = m0 + 32 * wave + 16 * ms + 4 * slot + v;
+      if (row >= M) continue;
+      const float a = a_scale[row];
+#pragma unroll
+      for (int ns = 0; ns < 4; ns++) {
+        const int col = 16 * ns + li;
+        if (col < rows) out[(size_t)row * N + (size_t)b * tq::kBlockRows + col] = a * accf[ms][ns][v];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------
+// Host side: argument checks and launch plans.
+// ---------------------------------------------------------------------
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool shape_ok(int64_t N, int64_t K) {
+  return N >= 1 && K >= tq::kGroup && K % tq::kGroup == 0 && N <= ((int64_t)1 << 24) &&
+         K <= ((int64_t)1 << 20);
+}
+
+struct GemvPlan {
+  int gs, nw, C, grid;
+  size_t ws_bytes;
+};
+
+GemvPlan gemv_plan(int fmt, int64_t M, int64_t N, int64_t K, int nmat) {
+  const Layout L(fmt, N, K);
+  const int64_t G = L.G, NB = L.NB;
+  const int64_t target_waves = TQ_GEMV_TARGET_WAVES;
+  const int64_t s_target = (target_waves + NB - 1) / NB;
+  int64_t gs = (G + s_target - 1) / s_target;
+  if (gs < 1) gs = 1;
+  if (gs > kGsMax) gs = kGsMax;
+  const int64_t S = (G + gs - 1) / gs;
+  const int64_t C = (S + kWavesMax - 1) / kWavesMax;
+  const int64_t nw = (S + C - 1) / C;
+  GemvPlan p;
+  p.gs = (int)gs;
+  p.nw = (int)nw;
+  p.C = (int)C;
+  p.grid = (int)(NB * C);
+  p.ws_bytes = 0;
+  if (C > 1) {
+    const size_t counters = ((size_t)NB * 4 + 255) / 256 * 256;
+    p.ws_bytes = counters + (size_t)C * nmat * M * N * sizeof(float);
+  }
+  return p;
+}
+
+int check_stream_launch() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+template <int FMT, int MT, int NMAT, bool SUMS>
+int launch_gemv_t(const GemvPlan &p, const void *W0, const void *W1, const int8_t *q,
+                  const float *a, float *out, int32_t *sums, void *ws, int M, int N, int K,
+                  hipStream_t st) {
+  const Layout L(FMT, N, K);
+  float *partials = nullptr;
+  uint32_t *counters = nullptr;
+  if (p.C > 1) {
+    counters = reinterpret_cast<uint32_t *>(ws);
+    const size_t cbytes = ((size_t)L.NB * 4 + 255) / 256 * 256;
+    partials = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + cbytes);
+  }
+  hipLaunchKernelGGL((gemv_kernel<FMT, MT, NMAT, SUMS>), dim3(p.grid), dim3(64 * p.nw), 0, st,
+                     (const uint8_t *)W0, (const uint8_t *)W1, q, a, out, sums, partials, counters,
+                     M, N, K, p.gs, p.nw, p.C);
+  return check_stream_launch();
+}
+
+template <int FMT, int NMAT, bool SUMS>
+int launch_gemv_m(const GemvPlan &p, const void *W0, const void *W1, const int8_t *q,
+                  const float *a, float *out, int32_t *sums, void *ws, int M, int N, int K,
+                  hipStream_t st) {
+  if (M <= 1) return launch_gemv_t<FMT, 1, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+  if (M <= 2) return launch_gemv_t<FMT, 2, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+  if (M <= 4) return launch_gemv_t<FMT, 4, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+  if (M <= 8) return launch_gemv_t<FMT, 8, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+  return launch_gemv_t<FMT, 16, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+}
+
+template <int NMAT, bool SUMS>
+int launch_gemv(int fmt, const GemvPlan &p, const void *W0, const void *W1, const int8_t *q,
+                const float *a, float *out, int32_t *sums, void *ws, int M, int N, int K,
+                hipStream_t st) {
+  if (fmt == TQ_FMT_B3)
+    return launch_gemv_m<0, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+  return launch_gemv_m<1, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+}
+
+int gemv_common(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const void *W1,
+                const int8_t *q, const float *a, float *out, int32_t *sums, void *ws,
+                size_t ws_bytes, void *stream, int nmat) {
+  if (!W0 || !q || (!sums && (!a || !out)) || (nmat == 2 && !W1)) return TQ_ERR_NULL;
+  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
+  if (!shape_ok(N, K) || M < 1 || M > TQ_GEMV_MAX_M) return TQ_ERR_SHAPE;
+  if (!aligned16(W0) || (W1 && !aligned16(W1)) || !aligned16(q) || (a && !aligned16(a)) ||
+      (out && !aligned16(out)) || (sums && !aligned16(sums)))
+    return TQ_ERR_ALIGN;
+  const GemvPlan p = gemv_plan(fmt, M, N, K, nmat);
+  if (!sums && p.ws_bytes > 0) {
+    if (!ws) return TQ_ERR_NULL;
+    if (!aligned16(ws)) return TQ_ERR_ALIGN;
+    if (ws_bytes < p.ws_bytes) return TQ_ERR_SIZE;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (sums) return launch_gemv<1, true>(fmt, p, W0, W0, q, a, out, sums, ws, (int)M, (int)N, (int)K, st);
+  if (nmat == 2)
+    return launch_gemv<2, false>(fmt, p, W0, W1, q, a, out, sums, ws, (int)M, (int)N, (int)K, st);
+  return launch_gemv<1, false>(fmt, p, W0, W0, q, a, out, sums, ws, (int)M, (int)N, (int)K, st);
+}
+
+int gemm_launch(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
+                const float *a, float *y, int32_t *sums, hipStream_t st) {
+  const Layout L(fmt, N, K);
+  dim3 grid((unsigned)L.NB, (unsigned)((M + kGemmBM - 1) / kGemmBM));
+  const uint8_t *Wb = (const uint8_t *)W;
+  if (fmt == TQ_FMT_B3) {
+    if (sums)
+      hipLaunchKernelGGL((gemm_kernel<0, true>), grid, dim3(256), 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
+    else
+      hipLaunchKernelGGL((gemm_kernel<0, false>), grid, dim3(256), 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
+  } else {
+    if (sums)
+      hipLaunchKernelGGL((gemm_kernel<1, true>), grid, dim3(256), 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
+    else
+      hipLaunchKernelGGL((gemm_kernel<1, false>), grid, dim3(256), 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
+  }
+  return check_stream_launch();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------
+extern "C" int tq_quant_act(int dtype, int64_t M, int64_t K, const void *x, int8_t *q,
+                            float *a_scale, void *stream) {
+  if (!x || !q || !a_scale) return TQ_ERR_NULL;
+  if (dtype != TQ_F16 && dtype != TQ_F32) return TQ_ERR_DTYPE;
+  if (M < 1 || M > ((int64_t)1 << 30) || K < tq::kGroup || K % tq::kGroup != 0 ||
+      K > ((int64_t)1 << 24))
+    return TQ_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(a_scale)) return TQ_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == TQ_F16)
+    hipLaunchKernelGGL((quant_kernel<_Float16>), dim3((unsigned)M), dim3(256), 0, st,
+                       (const _Float16 *)x, q, a_scale, (int)K);
+  else
+    hipLaunchKernelGGL((quant_kernel<float>), dim3((unsigned)M), dim3(256), 0, st,
+                       (const float *)x, q, a_scale, (int)K);
+  return check_stream_launch();
+}
+
+extern "C" size_t tq_gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
+  if ((fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) || !shape_ok(N, K) || M < 1 || M > TQ_GEMV_MAX_M)
+    return 0;
+  // the fused gate/up launch uses the same plan with two partial planes
+  return gemv_plan(fmt, M, N, K, 2).ws_bytes;
+}
+
+extern "C" int tq_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
+                       const float *a_scale, float *y, void *ws, size_t ws_bytes, void *stream) {
+  if (!y || !a_scale) return TQ_ERR_NULL;
+  return gemv_common(fmt, M, N, K, W, nullptr, q, a_scale, y, nullptr, ws, ws_bytes, stream, 1);
+}
+
+extern "C" int tq_gemv_gate_up_swiglu(int fmt, int64_t M, int64_t N, int64_t K, const void *Wg,
+                                      const void *Wu, const int8_t *q, const float *a_scale,
+                                      float *h, void *ws, size_t ws_bytes, void *stream) {
+  if (!h || !a_scale || !Wu) return TQ_ERR_NULL;
+  return gemv_common(fmt, M, N, K, Wg, Wu, q, a_scale, h, nullptr, ws, ws_bytes, stream, 2);
+}
+
+extern "C" size_t tq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (M >= 1 && M <= TQ_GEMV_MAX_M) return tq_gemv_workspace_bytes(fmt, M, N, K);
+  return 0;
+}
+
+extern "C" int tq_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
+                       const float *a_scale, float *y, void *ws, size_t ws_bytes, void *stream) {
+  if (M >= 1 && M <= TQ_GEMV_MAX_M) return tq_gemv(fmt, M, N, K, W, q, a_scale, y, ws, ws_bytes, stream);
+  if (!W || !q || !a_scale || !y) return TQ_ERR_NULL;
+  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
+  if (!shape_ok(N, K) || M < 1 || M > ((int64_t)1 << 24)) return TQ_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(q) || !aligned16(a_scale) || !aligned16(y)) return TQ_ERR_ALIGN;
+  return gemm_launch(fmt, M, N, K, W, q, a_scale, y, nullptr, (hipStream_t)stream);
+}
+
+extern "C" int tq_debug_unpack(int fmt, int64_t N, int64_t K, const void *W, int8_t *trits,
+                               void *stream) {
+  if (!W || !trits) return TQ_ERR_NULL;
+  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
+  if (!shape_ok(N, K)) return TQ_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(trits)) return TQ_ERR_ALIGN;
+  const Layout L(fmt, N, K);
+  dim3 grid((unsigned)L.NB, (unsigned)L.G);
+  hipStream_t st = (hipStream_t)stream;
+  if (fmt == TQ_FMT_B3)
+    hipLaunchKernelGGL((unpack_kernel<0>), grid, dim3(64), 0, st, (const uint8_t *)W, trits, (int)N, (int)K);
+  else
+    hipLaunchKernelGGL((unpack_kernel<1>), grid, dim3(64), 0, st, (const uint8_t *)W, trits, (int)N, (int)K);
+  return check_stream_launch();
+}
+
+extern "C" int tq_debug_group_sums(int fmt, int64_t M, int64_t N, int64_t K, const void *W,
+                                   const int8_t *q, int32_t *S, int use_gemm_path, void *stream) {
+  if (!W || !q || !S) return TQ_ERR_NULL;
+  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
+  if (!shape_ok(N, K) || M < 1) return TQ_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(q) || !aligned16(S)) return TQ_ERR_ALIGN;
+  if (use_gemm_path) {
+    if (M > ((int64_t)1 << 24)) return TQ_ERR_SHAPE;
+    return gemm_launch(fmt, M, N, K, W, q, nullptr, nullptr, S, (hipStream_t)stream);
+  }
+  if (M > TQ_GEMV_MAX_M) return TQ_ERR_SHAPE;
+  return gemv_common(fmt, M, N, K, W, nullptr, q, nullptr, nullptr, S, nullptr, 0, stream, 1);
+}

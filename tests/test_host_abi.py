@@ -1,0 +1,245 @@
+"""Host-side tests of libtq (no GPU): the library loads and exports every
+symbol include/tq.h declares; the packer follows the documented layout and
+round-trips; every argument error is reported before any device work."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import ternary_weight_base_amd as tq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+B3, TB = tq.TQ_FMT_B3, tq.TQ_FMT_2B
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _header_functions()
+    assert len(names) >= 12
+    raw = ctypes.CDLL(tq.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(tq.EXPORTS)
+
+
+def test_status_strings():
+    for code in range(0, -9, -1):
+        assert tq.tq_status_str(code) not in ("", "unknown status")
+    assert tq.tq_status_str(-100) == "unknown status"
+
+
+def _rand(N, K, seed):
+    return synth.trits(synth.seed(seed, 1), N, K), synth.scales(synth.seed(seed, 2), N, K)
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
+@pytest.mark.parametrize("N,K", [(1, 128), (3, 256), (64, 1024), (65, 384), (130, 640), (200, 128)])
+def test_pack_roundtrip_and_size(fmt, N, K):
+    t, s = _rand(N, K, N * 7 + K)
+    blob = tq.tq_pack(fmt, t, s)
+    P = 28 if fmt == B3 else 34
+    align = 4 if fmt == B3 else 8
+    nb = (N + 63) // 64
+    w = N - 64 * (nb - 1)
+    rows = 64 * (nb - 1) + (w + align - 1) // align * align
+    assert blob.size == tq.tq_packed_bytes(fmt, N, K) == rows * (K // 128) * P
+    t2, s2 = tq.tq_unpack(fmt, blob, N, K)
+    assert np.array_equal(t, t2) and np.array_equal(s, s2)
+
+
+def _device_group_bytes(fmt, blob, N, K, n, g):
+    """The (row n, group g) bytes and scale, located as include/tq.h describes."""
+    G = K // 128
+    P = 28 if fmt == B3 else 34
+    align = 4 if fmt == B3 else 8
+    nb = (N + 63) // 64
+    b, r = divmod(n, 64)
+    w = N - 64 * (nb - 1)
+    Wb = 64 if b < nb - 1 else (w + align - 1) // align * align
+    gb = 64 * b * G * P + g * Wb * P
+    if fmt == B3:
+        body = np.concatenate([blob[gb + r * 16: gb + r * 16 + 16],
+                               blob[gb + Wb * 16 + r * 12: gb + Wb * 16 + r * 12 + 10]])
+        sc = blob[gb + Wb * 16 + r * 12 + 10: gb + Wb * 16 + r * 12 + 12]
+    else:
+        body = np.concatenate([blob[gb + r * 16: gb + r * 16 + 16],
+                               blob[gb + Wb * 16 + r * 16: gb + Wb * 16 + r * 16 + 16]])
+        sc = blob[gb + Wb * 32 + r * 2: gb + Wb * 32 + r * 2 + 2]
+    return body, int(sc[0]) | (int(sc[1]) << 8)
+
+
+def _decode_b3_doc(body):
+    """Decode 26 device bytes by the rule written in include/tq.h, using
+    Python's base-3 string conversion."""
+    t = np.full(128, 99, dtype=np.int64)
+    for j, v in enumerate(body):
+        assert v < 243
+        digits = [int(c) for c in np.base_repr(int(v), 3).rjust(5, "0")][::-1]
+        if j < 25:
+            for i in range(4):
+                t[4 * j + i] = digits[i] - 1
+            t[100 + j] = digits[4] - 1
+        else:
+            assert digits[0] == 1 and digits[4] == 1
+            t[125:128] = np.array(digits[1:4]) - 1
+    return t
+
+
+def _decode_2b_doc(body):
+    t = np.full(128, 99, dtype=np.int64)
+    for byte_idx, v in enumerate(body):
+        m, c = divmod(byte_idx, 4)
+        for s in range(4):
+            code = (int(v) >> (2 * s)) & 3
+            assert code != 3
+            t[16 * m + 4 * s + c] = code - 1
+    return t
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
+def test_pack_matches_documented_layout(fmt):
+    N, K = 70, 384
+    t, s = _rand(N, K, 5 + fmt)
+    blob = tq.tq_pack(fmt, t, s)
+    for n in (0, 1, 63, 64, 69):
+        for g in range(K // 128):
+            body, sc = _device_group_bytes(fmt, blob, N, K, n, g)
+            dec = _decode_b3_doc(body) if fmt == B3 else _decode_2b_doc(body)
+            assert np.array_equal(dec, t[n, 128 * g: 128 * g + 128]), (n, g)
+            assert sc == s[n, g]
+
+
+def test_pack_same_information_as_oracle_canonical():
+    N, K = 33, 512
+    t, s = _rand(N, K, 77)
+    for fmt in (B3, TB):
+        rc, t1, s1 = oracle.unpack(fmt, oracle.pack(fmt, t, s), N, K)
+        t2, s2 = tq.tq_unpack(fmt, tq.tq_pack(fmt, t, s), N, K)
+        assert rc == 0 and np.array_equal(t1, t2) and np.array_equal(s1, s2)
+
+
+def test_b3_closed_form_device_bytes():
+    # all-zero trits -> every full byte 121 (digits all 1); the tail byte too
+    N, K = 4, 128
+    blob = tq.tq_pack(B3, np.zeros((N, K), np.int8), np.full((N, 1), 0x3C00, np.uint16))
+    body, sc = _device_group_bytes(B3, blob, N, K, 2, 0)
+    assert list(body) == [121] * 26 and sc == 0x3C00
+    blob = tq.tq_pack(B3, np.ones((N, K), np.int8), np.zeros((N, 1), np.uint16))
+    body, _ = _device_group_bytes(B3, blob, N, K, 1, 0)
+    assert list(body[:25]) == [242] * 25 and body[25] == 1 + 2 * 3 + 2 * 9 + 2 * 27 + 81
+
+
+def test_unpack_rejects_noncanonical():
+    N, K = 5, 256
+    t, s = _rand(N, K, 9)
+    blob = tq.tq_pack(B3, t, s)
+    for pos, val in ((0, 243), (17, 255)):
+        bad = blob.copy()
+        bad[pos] = val
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_unpack(B3, bad, N, K)
+        assert e.value.status == -5
+    # tail byte with a non-unit padding digit (digit 0 = 0)
+    bad = blob.copy()
+    off = 8 * 16 + 0 * 12 + 9  # block 0 (padded to 8 rows), group 0, row 0, device byte 25
+    assert bad[off] % 3 == 1
+    bad[off] -= 1
+    with pytest.raises(tq.TQError):
+        tq.tq_unpack(B3, bad, N, K)
+    # padding rows must stay zero trits / zero scale
+    bad = blob.copy()
+    bad[8 * 16 + 5 * 12 + 10] = 1  # scale of padding row 5 (rows 5..7 pad)
+    with pytest.raises(tq.TQError):
+        tq.tq_unpack(B3, bad, N, K)
+    blob2 = tq.tq_pack(TB, t, s)
+    bad = blob2.copy()
+    bad[3] = 0xFF
+    with pytest.raises(tq.TQError):
+        tq.tq_unpack(TB, bad, N, K)
+    # non-finite scale
+    bad = blob.copy()
+    bad[8 * 16 + 1 * 12 + 11] = 0x7C
+    bad[8 * 16 + 1 * 12 + 10] = 0x00
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_unpack(B3, bad, N, K)
+    assert e.value.status == -4
+
+
+def test_pack_rejects_bad_arguments():
+    L = tq.lib
+    t = np.zeros((2, 256), np.int8)
+    s = np.full((2, 2), 0x3C00, np.uint16)
+    out = np.empty(tq.tq_packed_bytes(B3, 2, 256), np.uint8)
+    P = lambda a: a.ctypes.data
+    assert L.tq_pack(B3, 2, 256, None, P(s), P(out), out.size) == -1
+    assert L.tq_pack(B3, 2, 200, P(t), P(s), P(out), out.size) == -2
+    assert L.tq_pack(B3, 0, 256, P(t), P(s), P(out), out.size) == -2
+    assert L.tq_pack(7, 2, 256, P(t), P(s), P(out), out.size) == -5
+    assert L.tq_pack(B3, 2, 256, P(t), P(s), P(out), out.size - 1) == -7
+    t2 = t.copy()
+    t2[1, 3] = 2
+    assert L.tq_pack(B3, 2, 256, P(t2), P(s), P(out), out.size) == -4
+    s2 = s.copy()
+    s2[0, 0] = 0x7E00
+    out2 = np.empty(tq.tq_packed_bytes(TB, 2, 256), np.uint8)
+    assert L.tq_pack(TB, 2, 256, P(t), P(s2), P(out2), out2.size) == -4
+    assert tq.tq_packed_bytes(B3, 2, 100) == 0 and tq.tq_packed_bytes(9, 2, 128) == 0
+
+
+# Device entry points: every check below fails on the host, before any launch,
+# so these run without a GPU.  Fake device addresses are never dereferenced.
+FAKE = 0x10000  # 16-byte aligned
+MIS = 0x10004   # misaligned
+
+
+def test_device_entry_points_validate_on_host():
+    L = tq.lib
+    # quant
+    assert L.tq_quant_act(5, 1, 128, FAKE, FAKE, FAKE, None) == -6
+    assert L.tq_quant_act(0, 0, 128, FAKE, FAKE, FAKE, None) == -2
+    assert L.tq_quant_act(0, 1, 100, FAKE, FAKE, FAKE, None) == -2
+    assert L.tq_quant_act(0, 1, 128, None, FAKE, FAKE, None) == -1
+    assert L.tq_quant_act(0, 1, 128, MIS, FAKE, FAKE, None) == -3
+    # gemv
+    assert L.tq_gemv(B3, 0, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
+    assert L.tq_gemv(B3, 17, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
+    assert L.tq_gemv(B3, 1, 64, 130, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
+    assert L.tq_gemv(3, 1, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
+    assert L.tq_gemv(B3, 1, 64, 128, None, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert L.tq_gemv(B3, 1, 64, 128, FAKE, MIS, FAKE, FAKE, None, 0, None) == -3
+    # a shape that splits K across workgroups needs a workspace of the stated size
+    need = tq.tq_gemv_workspace_bytes(B3, 1, 5120, 17408)
+    assert need > 0
+    assert L.tq_gemv(B3, 1, 5120, 17408, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert L.tq_gemv(B3, 1, 5120, 17408, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == -7
+    assert L.tq_gemv_gate_up_swiglu(B3, 1, 5120, 17408, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    need - 1, None) == -7
+    assert L.tq_gemv(B3, 1, 5120, 17408, FAKE, FAKE, FAKE, FAKE, MIS, need, None) == -3
+    assert L.tq_gemv_gate_up_swiglu(B3, 1, 64, 128, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == -1
+    # gemm
+    assert L.tq_gemm(B3, 0, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
+    assert L.tq_gemm(B3, 512, 64, 96, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
+    assert L.tq_gemm(B3, 512, 64, 128, FAKE, FAKE, MIS, FAKE, None, 0, None) == -3
+    assert L.tq_gemm(4, 512, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
+    # debug hooks
+    assert L.tq_debug_unpack(B3, 64, 128, FAKE, None, None) == -1
+    assert L.tq_debug_unpack(B3, 0, 128, FAKE, FAKE, None) == -2
+    assert L.tq_debug_group_sums(B3, 17, 64, 128, FAKE, FAKE, FAKE, 0, None) == -2
+    assert L.tq_debug_group_sums(B3, 1, 64, 128, FAKE, FAKE, MIS, 1, None) == -3
+
+
+def test_workspace_sizes():
+    assert tq.tq_gemv_workspace_bytes(B3, 1, 1024, 1024) == 0
+    for N, K in ((5120, 8192), (5120, 17408), (10240, 5120)):
+        assert tq.tq_gemv_workspace_bytes(B3, 1, N, K) > 0
+    assert tq.tq_gemm_workspace_bytes(B3, 512, 17408, 5120) == 0
+    assert tq.tq_gemv_workspace_bytes(B3, 17, 1024, 1024) == 0  # out of range
