@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Decode throughput of the 64-layer 27B-shaped ternary projection stack on one GPU.
+
+One step = one token through all 64 layers.  Per layer: quantise a fresh fp16
+input and run the QKV projection (5120 -> 10240); quantise a fresh fp16 input
+and run O (8192 -> 5120); quantise O's output and run the fused gate/up/SwiGLU
+(5120 -> 17408, two matrices); quantise h and run down (17408 -> 5120).  All
+weights are distinct per layer (about 5.06 GB of B3-packed trits and fp16
+scales), resident in HBM before timing starts.  Inputs are seeded synthetic
+data with the shapes and distributions of the workload (trits P(0) = 1/2,
+P(+-1) = 1/4; scales uniform in [0.005, 0.05]; activations N(0,1) in fp16).
+
+Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ternary GEMV weight-stream GB/s (% HBM peak); 27B-stack decode tok/s"
+HIDDEN, INTER, QKV_OUT, O_IN, LAYERS = 5120, 17408, 10240, 8192, 64
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_swiglu_stack_b3.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--fmt", choices=["b3", "2b"], default="b3")
+    p.add_argument("--layers", type=int, default=LAYERS,
+                   help="layers in the stack (the workload is 64; fewer is for quick checks)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    return p.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in ("ternary_weight_base_amd/csrc/tq_kernels.hip", "ternary_weight_base_amd/csrc/tq_layout.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Stack:
+    """Packed weights of all layers, resident on the GPU."""
+
+    SHAPES = {"qkv": (QKV_OUT, HIDDEN), "o": (HIDDEN, O_IN), "gate": (INTER, HIDDEN),
+              "up": (INTER, HIDDEN), "down": (HIDDEN, INTER)}
+    MATRIX_ID = {"qkv": 0, "o": 1, "gate": 2, "up": 3, "down": 4}
+
+    def __init__(self, tq, synth, torch, fmt: int, layers: int):
+        self.fmt, self.layers = fmt, layers
+        self.bytes = {k: tq.tq_packed_bytes(fmt, n, k2) for k, (n, k2) in self.SHAPES.items()}
+        self.W = {k: [] for k in self.SHAPES}
+        for l in range(layers):
+            for name, (N, K) in self.SHAPES.items():
+                seed = synth.seed(3, 1000 + l, self.MATRIX_ID[name])
+                t = synth.trits(synth.seed(seed, 1), N, K)
+                s = synth.scales(synth.seed(seed, 2), N, K)
+                blob = tq.tq_pack(fmt, t, s)
+                self.W[name].append(torch.from_numpy(blob).cuda())
+                del t, s, blob
+        self.step_weight_bytes = layers * sum(self.bytes.values())
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; --gpus N with N > 1 is not "
+              "supported (no collectives are built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import ternary_weight_base_amd as tq
+
+    torch.cuda.set_device(0)
+    fmt = tq.TQ_FMT_B3 if args.fmt == "b3" else tq.TQ_FMT_2B
+    L = args.layers
+    t0 = time.time()
+    stack = Stack(tq, synth, torch, fmt, L)
+    print(f"# stack packed and uploaded: {L} layers, {stack.step_weight_bytes / 1e9:.3f} GB "
+          f"in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    dev = "cuda"
+    x_in = torch.from_numpy(synth.normal_f16(synth.seed(3, 7, 1), L, HIDDEN)).to(dev)
+    a_in = torch.from_numpy(synth.normal_f16(synth.seed(3, 7, 2), L, O_IN)).to(dev)
+    q5, q8, q17 = (torch.empty((1, k), dtype=torch.int8, device=dev) for k in (HIDDEN, O_IN, INTER))
+    sc = torch.empty(4, dtype=torch.float32, device=dev)
+    y_qkv = torch.empty((1, QKV_OUT), dtype=torch.float32, device=dev)
+    y_o = torch.empty((1, HIDDEN), dtype=torch.float32, device=dev)
+    h = torch.empty((1, INTER), dtype=torch.float32, device=dev)
+    y_dn = torch.empty((L, HIDDEN), dtype=torch.float32, device=dev)
+    ws_bytes = max(tq.tq_gemv_workspace_bytes(fmt, 1, n, k) for n, k in Stack.SHAPES.values())
+    ws = torch.zeros(max(1, (ws_bytes + 15) // 16 * 4), dtype=torch.int32, device=dev)
+
+    def token():
+        for l in range(L):
+            tq.tq_quant_act(x_in[l:l + 1], q5, sc[0:1])
+            tq.tq_gemv(fmt, 1, QKV_OUT, HIDDEN, stack.W["qkv"][l], q5, sc[0:1], y_qkv, ws)
+            tq.tq_quant_act(a_in[l:l + 1], q8, sc[1:2])
+            tq.tq_gemv(fmt, 1, HIDDEN, O_IN, stack.W["o"][l], q8, sc[1:2], y_o, ws)
+            tq.tq_quant_act(y_o, q5, sc[2:3])
+            tq.tq_gemv_gate_up_swiglu(fmt, 1, INTER, HIDDEN, stack.W["gate"][l], stack.W["up"][l],
+                                      q5, sc[2:3], h, ws)
+            tq.tq_quant_act(h, q17, sc[3:4])
+            tq.tq_gemv(fmt, 1, HIDDEN, INTER, stack.W["down"][l], q17, sc[3:4], y_dn[l:l + 1], ws)
+
+    # A plain device copy of known size (64 MiB read + 64 MiB written), untimed:
+    # profiles of this command use it to calibrate the FETCH_SIZE / WRITE_SIZE
+    # counters against bytes that are known exactly.
+    calib_src = torch.ones(64 << 20, dtype=torch.uint8, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
+
+    # capture one token as a graph (512 launches) and replay it
+    cap = torch.cuda.Stream()
+    token()  # eager run: loads kernels, checks arguments
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cap):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            token()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(y_dn).all().item(), "non-finite output"
+    tok_s = 1000.0 / ms_per_step
+    stream_gbps = stack.step_weight_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # ---- dominant kernel: the fused gate/up/SwiGLU GEMV, timed on its own over
+    # the same 64 layers' weights (graph of L launches, HIP events around it)
+    gu_bytes = 2 * stack.bytes["gate"] + HIDDEN + 4 + INTER * 4
+    with torch.cuda.stream(cap):
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2, stream=cap):
+            for l in range(L):
+                tq.tq_gemv_gate_up_swiglu(fmt, 1, INTER, HIDDEN, stack.W["gate"][l],
+                                          stack.W["up"][l], q5, sc[2:3], h, ws)
+    torch.cuda.synchronize()
+    g2.replay()
+    torch.cuda.synchronize()
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        g2.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    gu_us = e0.elapsed_time(e1) * 1000.0 / (reps * L)
+    gu_gbps = gu_bytes / (gu_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha") == kernel_source_sha() and tr.get("fmt") == args.fmt:
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(gu_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gu_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                "kernel": "gemv_kernel<fmt,1,2,false> (tq_gemv_gate_up_swiglu, 17408x5120 x2)",
+                "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3)}
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(synth, args.cpu_seconds, args.fmt)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8xtrit->int32, fp32 scale",
+        "data": "synthetic (seeded trits/scales/N(0,1) fp16 inputs; no checkpoint)",
+        "config": {"workload": f"27B-shaped {L}-layer ternary projection stack, decode batch 1",
+                   "layers": L, "fmt": args.fmt, "hidden": HIDDEN, "intermediate": INTER,
+                   "qkv_out": QKV_OUT, "o_in": O_IN, "group": 128,
+                   "weight_bytes_per_token": stack.step_weight_bytes},
+        "weight_stream_GBps": round(stream_gbps, 1),
+        "weight_stream_frac_of_8TBps": round(stream_gbps / PEAK_HBM_GBPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(synth, budget_s: float, fmt_name: str):
+    """The oracle (plain C, OpenMP over rows) on whole layers of the stack, from
+    canonical packed blobs: unpack, quantise, project, SwiGLU, as the GPU does.
+    Layers are run until the time budget is spent; tok/s = layers/s / 64."""
+    import oracle
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    oracle.set_threads(cores)
+    fmt = oracle.FMT_B3 if fmt_name == "b3" else oracle.FMT_2B
+    done, elapsed, l = 0, 0.0, 0
+    while elapsed < budget_s and l < LAYERS:
+        blobs = {}
+        for name, (N, K) in Stack.SHAPES.items():
+            seed = synth.seed(3, 1000 + l, Stack.MATRIX_ID[name])
+            blobs[name] = oracle.pack(fmt, synth.trits(synth.seed(seed, 1), N, K),
+                                      synth.scales(synth.seed(seed, 2), N, K))
+        x = synth.normal_f16(synth.seed(3, 7, 1), LAYERS, HIDDEN)[l:l + 1]
+        a = synth.normal_f16(synth.seed(3, 7, 2), LAYERS, O_IN)[l:l + 1]
+        t0 = time.time()
+        q, s = oracle.quant(x)
+        oracle.project_packed(fmt, blobs["qkv"], QKV_OUT, HIDDEN, q, s)
+        q, s = oracle.quant(a)
+        yo = oracle.project_packed(fmt, blobs["o"], HIDDEN, O_IN, q, s)
+        q, s = oracle.quant(yo)
+        hh = oracle.swiglu(oracle.project_packed(fmt, blobs["gate"], INTER, HIDDEN, q, s),
+                           oracle.project_packed(fmt, blobs["up"], INTER, HIDDEN, q, s))
+        q, s = oracle.quant(hh)
+        oracle.project_packed(fmt, blobs["down"], HIDDEN, INTER, q, s)
+        elapsed += time.time() - t0
+        done += 1
+        l += 1
+    layers_per_s = done / elapsed
+    return {"value": round(layers_per_s / LAYERS, 4), "unit": "tok/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{done} of {LAYERS} layers of the same stack (unpack+quant+project+SwiGLU "
+                      f"from canonical packed blobs, {fmt_name}), {elapsed:.1f} s; tok/s = "
+                      f"layers/s / {LAYERS}"}
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,9 @@
  *  - Device functions are asynchronous on `stream` (a hipStream_t; NULL is
  *    the default stream) and never synchronise.  A kernel-launch failure
  *    returns TQ_ERR_HIP; faults surface at the caller's next synchronisation.
- *  - Device pointers must be 16-byte aligned (TQ_ERR_ALIGN otherwise).
+ *  - Packed weights, int8 activations and fp16/fp32 inputs x must be 16-byte
+ *    aligned; scale, output and debug arrays 4-byte aligned (TQ_ERR_ALIGN
+ *    otherwise).  Rows of q and x are K elements apart with K % 128 == 0.
  *  - The caller owns every buffer; the library never allocates or frees.
  *  - K must be a positive multiple of 128; N >= 1; M >= 1.
  *  - Stateless and thread-safe, except that one workspace must not be used
@@ -69,7 +71,7 @@ typedef enum {
   TQ_OK = 0,
   TQ_ERR_NULL = -1,   /* a required pointer is NULL */
   TQ_ERR_SHAPE = -2,  /* N < 1, M out of range, K not a positive multiple of 128 */
-  TQ_ERR_ALIGN = -3,  /* a device pointer is not 16-byte aligned */
+  TQ_ERR_ALIGN = -3,  /* a device pointer misses its required alignment */
   TQ_ERR_VALUE = -4,  /* trit outside {-1,0,1} or non-finite scale */
   TQ_ERR_FORMAT = -5, /* unknown format, or a non-canonical packed byte */
   TQ_ERR_DTYPE = -6,  /* unknown activation dtype */

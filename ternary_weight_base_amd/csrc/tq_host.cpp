@@ -22,7 +22,7 @@ extern "C" const char *tq_status_str(int status) {
     case TQ_OK: return "ok";
     case TQ_ERR_NULL: return "null pointer";
     case TQ_ERR_SHAPE: return "bad shape";
-    case TQ_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case TQ_ERR_ALIGN: return "device pointer misaligned";
     case TQ_ERR_VALUE: return "bad value (trit or scale)";
     case TQ_ERR_FORMAT: return "bad format or non-canonical packed data";
     case TQ_ERR_DTYPE: return "bad dtype";

@@ -33,8 +33,8 @@ constexpr int kLutCopies = 32;   // one table copy per lane of a half wave
 constexpr int kLutEntries = 256; // byte values; 243..255 map to zero trits
 constexpr int kWavesMax = 8;     // waves per GEMV workgroup
 constexpr int kGsMax = 8;        // groups per wave slice (all prefetched)
-#ifndef TQ_GEMV_TARGET_WAVES
-#define TQ_GEMV_TARGET_WAVES 4096  // 16 waves per CU on 256 CUs
+#ifndef TQ_ACT_LDS
+#define TQ_ACT_LDS 0
 #endif
 
 typedef long v2l __attribute__((ext_vector_type(2)));
@@ -56,32 +56,39 @@ __device__ __forceinline__ float half_bits(uint32_t bits) {
 // B3 digit table.  For byte value v (0..242): .lo holds the trits of base-3
 // digits 0..3 of v (one signed byte each), .hi the trit of digit 4 in byte 0;
 // values 243..255 (never produced by the packer) decode to zero trits.
-// The table is a compile-time constant; each workgroup copies it into LDS
-// 32 times, entry v of copy c at byte (v * 32 + c) * 8.  Lane l reads copy
+// Each workgroup builds it in LDS 32 times, entry v of copy c at byte
+// (v * 32 + c) * 8.  Lane l reads copy
 // l % 32, so the 32 lanes served together hit 32 distinct bank pairs
 // whatever byte values they hold.
 // ---------------------------------------------------------------------
-struct B3Table {
-  uint32_t lo[kLutEntries], hi[kLutEntries];
-  constexpr B3Table() : lo(), hi() {
-    for (int v = 0; v < 243; v++) {
-      int x = v;
-      uint32_t l = 0;
-      for (int i = 0; i < 4; i++) {
-        l |= (uint32_t)(uint8_t)(int8_t)(x % 3 - 1) << (8 * i);
-        x /= 3;
-      }
-      lo[v] = l;
-      hi[v] = (uint32_t)(uint8_t)(int8_t)(x - 1);
+__device__ __forceinline__ uint2 b3_entry(int v) {
+  uint32_t lo = 0, hi = 0;
+  if (v < 243) {
+    int x = v;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      lo |= (uint32_t)(uint8_t)(int8_t)(x % 3 - 1) << (8 * i);
+      x /= 3;
     }
+    hi = (uint32_t)(uint8_t)(int8_t)(x - 1);
   }
-};
-__device__ constexpr B3Table kB3Table{};
+  return make_uint2(lo, hi);
+}
 
+// Fill the 32 copies.  With a block size that is a multiple of 256 every
+// thread computes one entry v and stores it into 32 / (blockDim / 256) of the
+// copies; lane l starts at copy l % 32, so the 32 lanes of a store hit 32
+// distinct bank pairs.
 __device__ __forceinline__ void fill_b3_lut(uint2 *lut) {
-  for (int idx = threadIdx.x; idx < kLutEntries * kLutCopies; idx += blockDim.x) {
-    const int v = idx / kLutCopies;
-    lut[idx] = make_uint2(kB3Table.lo[v], kB3Table.hi[v]);
+  if ((blockDim.x & 255u) == 0) {
+    const int v = threadIdx.x & 255;
+    const uint2 e = b3_entry(v);
+    const int per = kLutCopies / (int)(blockDim.x >> 8);
+    const int k0 = (int)(threadIdx.x >> 8) * per;
+    for (int k = k0; k < k0 + per; k++) lut[v * kLutCopies + ((threadIdx.x + k) & (kLutCopies - 1))] = e;
+  } else {
+    for (int idx = threadIdx.x; idx < kLutEntries * kLutCopies; idx += blockDim.x)
+      lut[idx] = b3_entry(idx / kLutCopies);
   }
 }
 
@@ -113,6 +120,12 @@ struct XPtrs {
   __device__ __forceinline__ uint32_t get(int m, int i) const { return p[m][i]; }
 };
 
+template <int MT>
+struct XLds {
+  const uint32_t *p[MT];  // LDS addresses of the group's 32 words, per token row
+  __device__ __forceinline__ uint32_t get(int m, int i) const { return p[m][i]; }
+};
+
 // Integer core of one B3 group for MT activation rows.
 //   w[0..3]: device bytes 0..15, w[4..6]: bytes 16..25 and the scale.
 // byte j < 25: digits 0..3 pair with activation word j, digit 4 with byte
@@ -121,23 +134,28 @@ struct XPtrs {
 template <int MT, typename XS>
 __device__ __forceinline__ void b3_group(const uint2 *lut, uint32_t laneoff,
                                          const uint32_t (&w)[7], const XS &x, int (&S)[MT]) {
-#define TQ_B3_BYTE(J)                                                   \
-  {                                                                     \
-    const uint2 e = b3_byte<J>(lut, w, laneoff);                        \
-    _Pragma("unroll") for (int m = 0; m < MT; m++) {                    \
-      S[m] = sdot4(e.x, x.get(m, J), S[m]);                             \
-      S[m] = sdot4(e.y, x.get(m, 25 + (J >> 2)) >> (8 * (J & 3)), S[m]); \
-    }                                                                   \
-  }
-  TQ_B3_BYTE(0) TQ_B3_BYTE(1) TQ_B3_BYTE(2) TQ_B3_BYTE(3) TQ_B3_BYTE(4)
-  TQ_B3_BYTE(5) TQ_B3_BYTE(6) TQ_B3_BYTE(7) TQ_B3_BYTE(8) TQ_B3_BYTE(9)
-  TQ_B3_BYTE(10) TQ_B3_BYTE(11) TQ_B3_BYTE(12) TQ_B3_BYTE(13) TQ_B3_BYTE(14)
-  TQ_B3_BYTE(15) TQ_B3_BYTE(16) TQ_B3_BYTE(17) TQ_B3_BYTE(18) TQ_B3_BYTE(19)
-  TQ_B3_BYTE(20) TQ_B3_BYTE(21) TQ_B3_BYTE(22) TQ_B3_BYTE(23) TQ_B3_BYTE(24)
-#undef TQ_B3_BYTE
-  const uint2 e = b3_byte<25>(lut, w, laneoff);
+  // All 26 table lookups are issued before the first dot so that the LDS
+  // latency overlaps; two accumulator chains per row halve the dependency.
+  uint2 e[26];
+#define TQ_LK(J) e[J] = b3_byte<J>(lut, w, laneoff);
+  TQ_LK(0) TQ_LK(1) TQ_LK(2) TQ_LK(3) TQ_LK(4) TQ_LK(5) TQ_LK(6) TQ_LK(7) TQ_LK(8)
+  TQ_LK(9) TQ_LK(10) TQ_LK(11) TQ_LK(12) TQ_LK(13) TQ_LK(14) TQ_LK(15) TQ_LK(16)
+  TQ_LK(17) TQ_LK(18) TQ_LK(19) TQ_LK(20) TQ_LK(21) TQ_LK(22) TQ_LK(23) TQ_LK(24)
+  TQ_LK(25)
+#undef TQ_LK
+  int S2[MT];
 #pragma unroll
-  for (int m = 0; m < MT; m++) S[m] = sdot4(e.x, x.get(m, 31), S[m]);
+  for (int m = 0; m < MT; m++) S2[m] = 0;
+#pragma unroll
+  for (int j = 0; j < 25; j++) {
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+      S[m] = sdot4(e[j].x, x.get(m, j), S[m]);
+      S2[m] = sdot4(e[j].y, x.get(m, 25 + (j >> 2)) >> (8 * (j & 3)), S2[m]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MT; m++) S[m] = sdot4(e[25].x, x.get(m, 31), S[m]) + S2[m];
 }
 
 // Integer core of one 2B group.  Device byte 4c' + c, bits 2s hold
@@ -198,9 +216,71 @@ struct Vec<float> {
   }
 };
 
+// One workgroup (512 threads) per row; the row is read once into registers
+// (NV vectors per thread, all loads issued before the first use), reduced to
+// its absmax, then quantised from the registers.
+constexpr int kQuantThreads = 512;
+
+template <typename T, int NV>
+__global__ __launch_bounds__(kQuantThreads) void quant_kernel(const T *__restrict__ x,
+                                                              int8_t *__restrict__ q,
+                                                              float *__restrict__ scale, int K) {
+  constexpr int V = Vec<T>::n;
+  const int m = blockIdx.x;
+  const T *xr = x + (size_t)m * K;
+  int8_t *qr = q + (size_t)m * K;
+  float v[NV][V];
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int k = (i * kQuantThreads + (int)threadIdx.x) * V;
+    if (k < K) {
+      Vec<T>::load(xr + k, v[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; j++) v[i][j] = 0.0f;
+    }
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; i++)
+#pragma unroll
+    for (int j = 0; j < V; j++) a = fmaxf(a, fabsf(v[i][j]));
+  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+  __shared__ float wmax[kQuantThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kQuantThreads / 64; w++) a = fmaxf(a, wmax[w]);
+  const bool zero = (a == 0.0f);
+  const float inv = zero ? 0.0f : 127.0f / a;  // IEEE division, round to nearest even
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int k = (i * kQuantThreads + (int)threadIdx.x) * V;
+    if (k >= K) continue;
+    uint32_t packed[V / 4];
+#pragma unroll
+    for (int w = 0; w < V / 4; w++) packed[w] = 0;
+#pragma unroll
+    for (int j = 0; j < V; j++) {
+      float r = rintf(v[i][j] * inv);  // one rounded product, then ties-to-even
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+      const int qi = zero ? 0 : (int)r;
+      packed[j / 4] |= (uint32_t)(uint8_t)(int8_t)qi << (8 * (j % 4));
+    }
+    if (V == 8)
+      *reinterpret_cast<uint2 *>(qr + k) = make_uint2(packed[0], packed[V / 4 - 1]);
+    else
+      *reinterpret_cast<uint32_t *>(qr + k) = packed[0];
+  }
+  if (threadIdx.x == 0) scale[m] = zero ? 0.0f : a / 127.0f;
+}
+
+// Rows longer than the register-resident kernel holds: two passes over x.
 template <typename T>
-__global__ __launch_bounds__(256) void quant_kernel(const T *__restrict__ x, int8_t *__restrict__ q,
-                                                    float *__restrict__ scale, int K) {
+__global__ __launch_bounds__(256) void quant_kernel_long(const T *__restrict__ x,
+                                                         int8_t *__restrict__ q,
+                                                         float *__restrict__ scale, int K) {
   constexpr int V = Vec<T>::n;
   const int m = blockIdx.x;
   const T *xr = x + (size_t)m * K;
@@ -218,7 +298,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const T *__restrict__ x, int
   __syncthreads();
   a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const bool zero = (a == 0.0f);
-  const float inv = zero ? 0.0f : 127.0f / a;  // IEEE division, round to nearest even
+  const float inv = zero ? 0.0f : 127.0f / a;
   for (int k = threadIdx.x * V; k < K; k += 256 * V) {
     float v[V];
     Vec<T>::load(xr + k, v);
@@ -227,9 +307,9 @@ __global__ __launch_bounds__(256) void quant_kernel(const T *__restrict__ x, int
     for (int i = 0; i < V / 4; i++) packed[i] = 0;
 #pragma unroll
     for (int i = 0; i < V; i++) {
-      float r = rintf(v[i] * inv);  // one rounded product, then ties-to-even
+      float r = rintf(v[i] * inv);
       r = fminf(fmaxf(r, -127.0f), 127.0f);
-      int qi = zero ? 0 : (int)r;
+      const int qi = zero ? 0 : (int)r;
       packed[i / 4] |= (uint32_t)(uint8_t)(int8_t)qi << (8 * (i % 4));
     }
     if (V == 8)
@@ -259,7 +339,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const T *__restrict__ x, int
 // device-coherent atomic accesses, so no cache-wide release/acquire fence is
 // needed (on this multi-die GPU those write back and invalidate the whole L2).
 // ---------------------------------------------------------------------
-template <int FMT, int MT, int NMAT, bool SUMS>
+template <int FMT, int MT, int NMAT, bool SUMS, int GS>
 __global__ __launch_bounds__(512) void gemv_kernel(
     const uint8_t *__restrict__ W0, const uint8_t *__restrict__ W1,
     const int8_t *__restrict__ q, const float *__restrict__ a_scale, float *__restrict__ out,
@@ -273,6 +353,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(
   __shared__ int xsum_lds[kXsumSlots];
   __shared__ float red[SUMS ? 1 : NMAT * MT * kWavesMax * 64];
   __shared__ int last_flag;
+  constexpr bool kActLds = TQ_ACT_LDS && MT <= 2;
+  __shared__ __attribute__((aligned(16))) uint32_t xlds[kActLds ? MT * kWavesMax * kGsMax * 32 : 1];
 
   const Layout L(FMT, N, K);
   const int G = (int)L.G;
@@ -288,39 +370,62 @@ __global__ __launch_bounds__(512) void gemv_kernel(
   const bool lane_ok = lane < Wb;
   const uint8_t *Wm[2] = {W0, W1};
 
+  const uint32_t *__restrict__ xrow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; m++)
+    xrow[m] = reinterpret_cast<const uint32_t *>(q + (size_t)min(m, M - 1) * K);
+  // one token: the first group's activation words go out before the weights
+  XRegs<1> xa, xb;
+  if constexpr (MT == 1) {
+    const int gf = min(g0, G - 1);
+#pragma unroll
+    for (int k = 0; k < 32; k++) xa.v[0][k] = xrow[0][32 * gf + k];
+  }
+
   // ---- 1. issue the loads of every group of the slice -------------------
-  uint32_t wd[NMAT][kGsMax][WPG];
+  // Unconditional and branch-free (rows and groups past the end are clamped
+  // to valid ones and their results dropped), so the number of loads in
+  // flight is static and group 0 is waited for alone.
+  const int lr = min(lane, Wb - 1);
+  uint32_t wd[NMAT][GS][WPG];
 #pragma unroll
   for (int mat = 0; mat < NMAT; mat++) {
 #pragma unroll
-    for (int i = 0; i < kGsMax; i++) {
-#pragma unroll
-      for (int k = 0; k < WPG; k++) wd[mat][i][k] = 0;
-      if (i < ng && lane_ok) {
-        const uint8_t *gb = Wm[mat] + L.group_base(b, g0 + i);
-        const uint4 A = *reinterpret_cast<const uint4 *>(gb + lane * 16);
-        wd[mat][i][0] = A.x;
-        wd[mat][i][1] = A.y;
-        wd[mat][i][2] = A.z;
-        wd[mat][i][3] = A.w;
-        if (FMT == 0) {
-          const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + lane * 12);
-          wd[mat][i][4] = pb[0];
-          wd[mat][i][5] = pb[1];
-          wd[mat][i][6] = pb[2];
-        } else {
-          const uint4 B = *reinterpret_cast<const uint4 *>(gb + Wb * 16 + lane * 16);
-          wd[mat][i][4] = B.x;
-          wd[mat][i][5] = B.y;
-          wd[mat][i][6] = B.z;
-          wd[mat][i][7] = B.w;
-          wd[mat][i][8] = *reinterpret_cast<const uint16_t *>(gb + Wb * 32 + lane * 2);
-        }
+    for (int i = 0; i < GS; i++) {
+      const int gi = min(g0 + i, G - 1);
+      const uint8_t *gb = Wm[mat] + L.group_base(b, gi);
+      const uint4 A = *reinterpret_cast<const uint4 *>(gb + lr * 16);
+      wd[mat][i][0] = A.x;
+      wd[mat][i][1] = A.y;
+      wd[mat][i][2] = A.z;
+      wd[mat][i][3] = A.w;
+      if (FMT == 0) {
+        const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + lr * 12);
+        wd[mat][i][4] = pb[0];
+        wd[mat][i][5] = pb[1];
+        wd[mat][i][6] = pb[2];
+      } else {
+        const uint4 B = *reinterpret_cast<const uint4 *>(gb + Wb * 16 + lr * 16);
+        wd[mat][i][4] = B.x;
+        wd[mat][i][5] = B.y;
+        wd[mat][i][6] = B.z;
+        wd[mat][i][7] = B.w;
+        wd[mat][i][8] = *reinterpret_cast<const uint16_t *>(gb + Wb * 32 + lr * 2);
       }
     }
   }
+  (void)lane_ok;
 
   // ---- 2. tables, while the loads are in flight --------------------------
+  if constexpr (kActLds) {
+    const int ngw = max(0, min(G - gwg, nw * gs));
+    for (int p = tid; p < MT * ngw * 8; p += blockDim.x) {
+      const int m = p / (ngw * 8), r = p - m * ngw * 8;
+      const uint4 v = *reinterpret_cast<const uint4 *>(q + (size_t)min(m, M - 1) * K +
+                                                       (size_t)gwg * tq::kGroup + 16 * r);
+      *reinterpret_cast<uint4 *>(&xlds[(m * kWavesMax * kGsMax) * 32 + 4 * r]) = v;
+    }
+  }
   if (FMT == 0) {
     fill_b3_lut(lut);
   } else {
@@ -348,10 +453,6 @@ __global__ __launch_bounds__(512) void gemv_kernel(
 
   // ---- 3. decode + integer dot + scale, group by group -------------------
   const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
-  const uint32_t *__restrict__ xrow[MT];
-#pragma unroll
-  for (int m = 0; m < MT; m++)
-    xrow[m] = reinterpret_cast<const uint32_t *>(q + (size_t)min(m, M - 1) * K);
 
   float acc[NMAT][MT];
 #pragma unroll
@@ -359,12 +460,17 @@ __global__ __launch_bounds__(512) void gemv_kernel(
 #pragma unroll
     for (int m = 0; m < MT; m++) acc[mat][m] = 0.0f;
 
+  // Slot i of the slice.  Slots past the slice's end (i >= ng) run on a
+  // clamped, valid group and are dropped (zero scale, no store), which keeps
+  // the loop free of branches and the load counters static.
   auto do_group = [&](int i, const auto &xs) {
-    const int g = g0 + i;
+    const bool live = i < ng;
+    const int g = min(g0 + i, G - 1);
     int xsum[MT];
     if (FMT == 1) {
+      const int gl = min(max(g - gwg, 0), kXsumStride - 1);
 #pragma unroll
-      for (int m = 0; m < MT; m++) xsum[m] = xsum_lds[m * kXsumStride + (g - gwg)];
+      for (int m = 0; m < MT; m++) xsum[m] = xsum_lds[m * kXsumStride + gl];
     }
 #pragma unroll
     for (int mat = 0; mat < NMAT; mat++) {
@@ -385,47 +491,51 @@ __global__ __launch_bounds__(512) void gemv_kernel(
         sc = half_bits(wd[mat][i][8]);
       }
       if (SUMS) {
-        if (lane < rows) {
+        if (live && lane < rows) {
           const size_t n = (size_t)b * tq::kBlockRows + lane;
 #pragma unroll
           for (int m = 0; m < MT; m++)
             if (m < M) sums[((size_t)m * N + n) * G + g] = S[m];
         }
       } else {
+        sc = live ? sc : 0.0f;
 #pragma unroll
         for (int m = 0; m < MT; m++) acc[mat][m] = fmaf(sc, (float)S[m], acc[mat][m]);
       }
     }
   };
 
-  if constexpr (MT == 1) {
+  if constexpr (kActLds) {
+#pragma unroll
+    for (int i = 0; i < GS; i++) {
+      XLds<MT> xl;
+      const int gl = min(max(min(g0 + i, G - 1) - gwg, 0), kWavesMax * kGsMax - 1);
+#pragma unroll
+      for (int m = 0; m < MT; m++) xl.p[m] = &xlds[(m * kWavesMax * kGsMax + gl) * 32];
+      do_group(i, xl);
+    }
+    (void)xb;
+  } else if constexpr (MT == 1) {
     // one token: keep the group's 32 activation words in SGPRs and fetch the
     // next group's while this one is computed
-    XRegs<1> xa, xb;
-    if (ng > 0) {
 #pragma unroll
-      for (int k = 0; k < 32; k++) xa.v[0][k] = xrow[0][32 * g0 + k];
-    }
+    for (int i = 0; i < GS; i++) {
+      if (i + 1 < GS) {
+        const int gn = min(g0 + i + 1, G - 1);
 #pragma unroll
-    for (int i = 0; i < kGsMax; i++) {
-      if (i < ng) {
-        if (i + 1 < ng) {
-#pragma unroll
-          for (int k = 0; k < 32; k++) xb.v[0][k] = xrow[0][32 * (g0 + i + 1) + k];
-        }
-        do_group(i, xa);
-        xa = xb;
+        for (int k = 0; k < 32; k++) xb.v[0][k] = xrow[0][32 * gn + k];
       }
+      do_group(i, xa);
+      xa = xb;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kGsMax; i++) {
-      if (i < ng) {
-        XPtrs<MT> xp;
+    for (int i = 0; i < GS; i++) {
+      XPtrs<MT> xp;
+      const int gi = min(g0 + i, G - 1);
 #pragma unroll
-        for (int m = 0; m < MT; m++) xp.p[m] = xrow[m] + 32 * (g0 + i);
-        do_group(i, xp);
-      }
+      for (int m = 0; m < MT; m++) xp.p[m] = xrow[m] + 32 * gi;
+      do_group(i, xp);
     }
   }
   if (SUMS) return;
@@ -706,6 +816,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
 // Host side: argument checks and launch plans.
 // ---------------------------------------------------------------------
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 bool shape_ok(int64_t N, int64_t K) {
   return N >= 1 && K >= tq::kGroup && K % tq::kGroup == 0 && N <= ((int64_t)1 << 24) &&
@@ -717,26 +828,43 @@ struct GemvPlan {
   size_t ws_bytes;
 };
 
+// Launch plan.  Two workgroups fit a CU (the B3 digit table takes 64 KB of
+// LDS), so up to 512 are resident at once on 256 CUs: split K over C
+// workgroups per block so that NB * C stays within one resident round, then
+// give each workgroup 4 or 8 waves (a multiple of 256 threads builds the
+// table fastest) and each wave gs <= kGsMax groups, preferring the split
+// that leaves the fewest idle group slots.
 GemvPlan gemv_plan(int fmt, int64_t M, int64_t N, int64_t K, int nmat) {
   const Layout L(fmt, N, K);
   const int64_t G = L.G, NB = L.NB;
-  const int64_t target_waves = TQ_GEMV_TARGET_WAVES;
-  const int64_t s_target = (target_waves + NB - 1) / NB;
-  int64_t gs = (G + s_target - 1) / s_target;
-  if (gs < 1) gs = 1;
-  if (gs > kGsMax) gs = kGsMax;
-  const int64_t S = (G + gs - 1) / gs;
-  const int64_t C = (S + kWavesMax - 1) / kWavesMax;
-  const int64_t nw = (S + C - 1) / C;
+  const int64_t resident = 512;
+  int64_t C = resident / NB;
+  if (C < 1) C = 1;
+  if (C > G) C = G;
+  int64_t best_gs = 1, best_nw = 8, best_C = C, best_idle = -1;
+  for (int64_t nw : {8, 4}) {
+    int64_t gs = (G + C * nw - 1) / (C * nw);
+    if (gs < 1) gs = 1;
+    if (gs > kGsMax) gs = kGsMax;
+    const int64_t S = (G + gs - 1) / gs;
+    const int64_t c2 = (S + nw - 1) / nw;
+    const int64_t idle = c2 * nw * gs - G + (c2 > C ? (c2 - C) * nw * gs * 4 : 0);
+    if (best_idle < 0 || idle < best_idle) {
+      best_idle = idle;
+      best_gs = gs;
+      best_nw = nw;
+      best_C = c2;
+    }
+  }
   GemvPlan p;
-  p.gs = (int)gs;
-  p.nw = (int)nw;
-  p.C = (int)C;
-  p.grid = (int)(NB * C);
+  p.gs = (int)best_gs;
+  p.nw = (int)best_nw;
+  p.C = (int)best_C;
+  p.grid = (int)(NB * best_C);
   p.ws_bytes = 0;
-  if (C > 1) {
+  if (best_C > 1) {
     const size_t counters = ((size_t)NB * 4 + 255) / 256 * 256;
-    p.ws_bytes = counters + (size_t)C * nmat * M * N * sizeof(float);
+    p.ws_bytes = counters + (size_t)best_C * nmat * M * N * sizeof(float);
   }
   return p;
 }
@@ -746,8 +874,21 @@ int check_stream_launch() {
   return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
-template <int FMT, int MT, int NMAT, bool SUMS>
-int launch_gemv_t(const GemvPlan &p, const void *W0, const void *W1, const int8_t *q,
+template <typename T>
+void launch_quant(const T *x, int8_t *q, float *a, int64_t M, int64_t K, hipStream_t st) {
+  const int64_t per_pass = (int64_t)kQuantThreads * Vec<T>::n;
+  const int64_t nv = (K + per_pass - 1) / per_pass;
+  const dim3 grid((unsigned)M), blk(kQuantThreads);
+  if (nv <= 1) hipLaunchKernelGGL((quant_kernel<T, 1>), grid, blk, 0, st, x, q, a, (int)K);
+  else if (nv <= 2) hipLaunchKernelGGL((quant_kernel<T, 2>), grid, blk, 0, st, x, q, a, (int)K);
+  else if (nv <= 4) hipLaunchKernelGGL((quant_kernel<T, 4>), grid, blk, 0, st, x, q, a, (int)K);
+  else if (nv <= 8) hipLaunchKernelGGL((quant_kernel<T, 8>), grid, blk, 0, st, x, q, a, (int)K);
+  else if (nv <= 16) hipLaunchKernelGGL((quant_kernel<T, 16>), grid, blk, 0, st, x, q, a, (int)K);
+  else hipLaunchKernelGGL((quant_kernel_long<T>), grid, dim3(256), 0, st, x, q, a, (int)K);
+}
+
+template <int FMT, int MT, int NMAT, bool SUMS, int GS>
+int launch_gemv_g(const GemvPlan &p, const void *W0, const void *W1, const int8_t *q,
                   const float *a, float *out, int32_t *sums, void *ws, int M, int N, int K,
                   hipStream_t st) {
   const Layout L(FMT, N, K);
@@ -758,10 +899,28 @@ int launch_gemv_t(const GemvPlan &p, const void *W0, const void *W1, const int8_
     const size_t cbytes = ((size_t)L.NB * 4 + 255) / 256 * 256;
     partials = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + cbytes);
   }
-  hipLaunchKernelGGL((gemv_kernel<FMT, MT, NMAT, SUMS>), dim3(p.grid), dim3(64 * p.nw), 0, st,
+  hipLaunchKernelGGL((gemv_kernel<FMT, MT, NMAT, SUMS, GS>), dim3(p.grid), dim3(64 * p.nw), 0, st,
                      (const uint8_t *)W0, (const uint8_t *)W1, q, a, out, sums, partials, counters,
                      M, N, K, p.gs, p.nw, p.C);
   return check_stream_launch();
+}
+
+// One token: the slice length is a template constant (exactly gs loads per
+// wave); several tokens are bound by the dot products, kGsMax suffices.
+template <int FMT, int MT, int NMAT, bool SUMS>
+int launch_gemv_t(const GemvPlan &p, const void *W0, const void *W1, const int8_t *q,
+                  const float *a, float *out, int32_t *sums, void *ws, int M, int N, int K,
+                  hipStream_t st) {
+#define TQ_GS(n) \
+  case n: return launch_gemv_g<FMT, MT, NMAT, SUMS, n>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+  if (MT == 1) {
+    switch (p.gs) {
+      TQ_GS(1) TQ_GS(2) TQ_GS(3) TQ_GS(4) TQ_GS(5) TQ_GS(6) TQ_GS(7)
+      default: break;
+    }
+  }
+#undef TQ_GS
+  return launch_gemv_g<FMT, MT, NMAT, SUMS, kGsMax>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
 }
 
 template <int FMT, int NMAT, bool SUMS>
@@ -790,8 +949,8 @@ int gemv_common(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const 
   if (!W0 || !q || (!sums && (!a || !out)) || (nmat == 2 && !W1)) return TQ_ERR_NULL;
   if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
   if (!shape_ok(N, K) || M < 1 || M > TQ_GEMV_MAX_M) return TQ_ERR_SHAPE;
-  if (!aligned16(W0) || (W1 && !aligned16(W1)) || !aligned16(q) || (a && !aligned16(a)) ||
-      (out && !aligned16(out)) || (sums && !aligned16(sums)))
+  if (!aligned16(W0) || (W1 && !aligned16(W1)) || !aligned16(q) || (a && !aligned4(a)) ||
+      (out && !aligned4(out)) || (sums && !aligned4(sums)))
     return TQ_ERR_ALIGN;
   const GemvPlan p = gemv_plan(fmt, M, N, K, nmat);
   if (!sums && p.ws_bytes > 0) {
@@ -837,14 +996,10 @@ extern "C" int tq_quant_act(int dtype, int64_t M, int64_t K, const void *x, int8
   if (M < 1 || M > ((int64_t)1 << 30) || K < tq::kGroup || K % tq::kGroup != 0 ||
       K > ((int64_t)1 << 24))
     return TQ_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(q) || !aligned16(a_scale)) return TQ_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(q) || !aligned4(a_scale)) return TQ_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
-  if (dtype == TQ_F16)
-    hipLaunchKernelGGL((quant_kernel<_Float16>), dim3((unsigned)M), dim3(256), 0, st,
-                       (const _Float16 *)x, q, a_scale, (int)K);
-  else
-    hipLaunchKernelGGL((quant_kernel<float>), dim3((unsigned)M), dim3(256), 0, st,
-                       (const float *)x, q, a_scale, (int)K);
+  if (dtype == TQ_F16) launch_quant<_Float16>((const _Float16 *)x, q, a_scale, M, K, st);
+  else launch_quant<float>((const float *)x, q, a_scale, M, K, st);
   return check_stream_launch();
 }
 
@@ -879,7 +1034,7 @@ extern "C" int tq_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, 
   if (!W || !q || !a_scale || !y) return TQ_ERR_NULL;
   if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
   if (!shape_ok(N, K) || M < 1 || M > ((int64_t)1 << 24)) return TQ_ERR_SHAPE;
-  if (!aligned16(W) || !aligned16(q) || !aligned16(a_scale) || !aligned16(y)) return TQ_ERR_ALIGN;
+  if (!aligned16(W) || !aligned16(q) || !aligned4(a_scale) || !aligned4(y)) return TQ_ERR_ALIGN;
   return gemm_launch(fmt, M, N, K, W, q, a_scale, y, nullptr, (hipStream_t)stream);
 }
 
@@ -888,7 +1043,7 @@ extern "C" int tq_debug_unpack(int fmt, int64_t N, int64_t K, const void *W, int
   if (!W || !trits) return TQ_ERR_NULL;
   if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
   if (!shape_ok(N, K)) return TQ_ERR_SHAPE;
-  if (!aligned16(W) || !aligned16(trits)) return TQ_ERR_ALIGN;
+  if (!aligned16(W) || !aligned4(trits)) return TQ_ERR_ALIGN;
   const Layout L(fmt, N, K);
   dim3 grid((unsigned)L.NB, (unsigned)L.G);
   hipStream_t st = (hipStream_t)stream;
@@ -904,7 +1059,7 @@ extern "C" int tq_debug_group_sums(int fmt, int64_t M, int64_t N, int64_t K, con
   if (!W || !q || !S) return TQ_ERR_NULL;
   if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
   if (!shape_ok(N, K) || M < 1) return TQ_ERR_SHAPE;
-  if (!aligned16(W) || !aligned16(q) || !aligned16(S)) return TQ_ERR_ALIGN;
+  if (!aligned16(W) || !aligned16(q) || !aligned4(S)) return TQ_ERR_ALIGN;
   if (use_gemm_path) {
     if (M > ((int64_t)1 << 24)) return TQ_ERR_SHAPE;
     return gemm_launch(fmt, M, N, K, W, q, nullptr, nullptr, S, (hipStream_t)stream);

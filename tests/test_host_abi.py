@@ -198,7 +198,8 @@ def test_pack_rejects_bad_arguments():
 # Device entry points: every check below fails on the host, before any launch,
 # so these run without a GPU.  Fake device addresses are never dereferenced.
 FAKE = 0x10000  # 16-byte aligned
-MIS = 0x10004   # misaligned
+MIS = 0x10004   # 4-byte but not 16-byte aligned
+ODD = 0x10002   # not even 4-byte aligned
 
 
 def test_device_entry_points_validate_on_host():
@@ -209,6 +210,7 @@ def test_device_entry_points_validate_on_host():
     assert L.tq_quant_act(0, 1, 100, FAKE, FAKE, FAKE, None) == -2
     assert L.tq_quant_act(0, 1, 128, None, FAKE, FAKE, None) == -1
     assert L.tq_quant_act(0, 1, 128, MIS, FAKE, FAKE, None) == -3
+    assert L.tq_quant_act(0, 1, 128, FAKE, FAKE, ODD, None) == -3
     # gemv
     assert L.tq_gemv(B3, 0, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
     assert L.tq_gemv(B3, 17, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
@@ -228,13 +230,15 @@ def test_device_entry_points_validate_on_host():
     # gemm
     assert L.tq_gemm(B3, 0, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
     assert L.tq_gemm(B3, 512, 64, 96, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
-    assert L.tq_gemm(B3, 512, 64, 128, FAKE, FAKE, MIS, FAKE, None, 0, None) == -3
+    assert L.tq_gemm(B3, 512, 64, 128, FAKE, MIS, FAKE, FAKE, None, 0, None) == -3
+    assert L.tq_gemm(B3, 512, 64, 128, FAKE, FAKE, ODD, FAKE, None, 0, None) == -3
     assert L.tq_gemm(4, 512, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
     # debug hooks
     assert L.tq_debug_unpack(B3, 64, 128, FAKE, None, None) == -1
     assert L.tq_debug_unpack(B3, 0, 128, FAKE, FAKE, None) == -2
     assert L.tq_debug_group_sums(B3, 17, 64, 128, FAKE, FAKE, FAKE, 0, None) == -2
-    assert L.tq_debug_group_sums(B3, 1, 64, 128, FAKE, FAKE, MIS, 1, None) == -3
+    assert L.tq_debug_group_sums(B3, 1, 64, 128, FAKE, FAKE, ODD, 1, None) == -3
+    assert L.tq_debug_group_sums(B3, 1, 64, 128, FAKE, MIS, FAKE, 1, None) == -3
 
 
 def test_workspace_sizes():
