@@ -89,6 +89,7 @@ def main():
     import ternary_weight_base_amd as tq
 
     torch.cuda.set_device(0)
+    dev = "cuda"
     fmt = tq.TQ_FMT_B3 if args.fmt == "b3" else tq.TQ_FMT_2B
     L = args.layers
     t0 = time.time()
@@ -96,29 +97,46 @@ def main():
     print(f"# stack packed and uploaded: {L} layers, {stack.step_weight_bytes / 1e9:.3f} GB "
           f"in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
-    dev = "cuda"
     x_in = torch.from_numpy(synth.normal_f16(synth.seed(3, 7, 1), L, HIDDEN)).to(dev)
     a_in = torch.from_numpy(synth.normal_f16(synth.seed(3, 7, 2), L, O_IN)).to(dev)
+    y_qkv = torch.empty((L, QKV_OUT), dtype=torch.float32, device=dev)
+    y_o = torch.empty((L, HIDDEN), dtype=torch.float32, device=dev)
+    h = torch.empty((L, INTER), dtype=torch.float32, device=dev)
+    y_dn = torch.empty((L, HIDDEN), dtype=torch.float32, device=dev)
+    layers = tq.stack_layers([(stack.W["qkv"][l], stack.W["o"][l], stack.W["gate"][l],
+                               stack.W["up"][l], stack.W["down"][l]) for l in range(L)])
+    st_bytes = tq.tq_decode_stack_workspace_bytes(fmt, L, HIDDEN, INTER, QKV_OUT, O_IN)
+    st_ws = torch.zeros((st_bytes + 15) // 16 * 4, dtype=torch.int32, device=dev)
+
+    # the decode step: tq_decode_stack, 2 launches per layer
+    def token():
+        tq.tq_decode_stack(fmt, L, HIDDEN, INTER, QKV_OUT, O_IN, layers, x_in, a_in,
+                           y_qkv, y_o, h, y_dn, st_ws)
+
+    # the same token as 8 separate launches per layer (quantiser, then GEMV)
     q5, q8, q17 = (torch.empty((1, k), dtype=torch.int8, device=dev) for k in (HIDDEN, O_IN, INTER))
     sc = torch.empty(4, dtype=torch.float32, device=dev)
-    y_qkv = torch.empty((1, QKV_OUT), dtype=torch.float32, device=dev)
-    y_o = torch.empty((1, HIDDEN), dtype=torch.float32, device=dev)
-    h = torch.empty((1, INTER), dtype=torch.float32, device=dev)
-    y_dn = torch.empty((L, HIDDEN), dtype=torch.float32, device=dev)
+    y1, h1 = torch.empty((1, QKV_OUT), device=dev), torch.empty((1, INTER), device=dev)
+    yo1, yd1 = torch.empty((1, HIDDEN), device=dev), torch.empty((1, HIDDEN), device=dev)
     ws_bytes = max(tq.tq_gemv_workspace_bytes(fmt, 1, n, k) for n, k in Stack.SHAPES.values())
     ws = torch.zeros(max(1, (ws_bytes + 15) // 16 * 4), dtype=torch.int32, device=dev)
 
-    def token():
+    def token_separate():
         for l in range(L):
             tq.tq_quant_act(x_in[l:l + 1], q5, sc[0:1])
-            tq.tq_gemv(fmt, 1, QKV_OUT, HIDDEN, stack.W["qkv"][l], q5, sc[0:1], y_qkv, ws)
+            tq.tq_gemv(fmt, 1, QKV_OUT, HIDDEN, stack.W["qkv"][l], q5, sc[0:1], y1, ws)
             tq.tq_quant_act(a_in[l:l + 1], q8, sc[1:2])
-            tq.tq_gemv(fmt, 1, HIDDEN, O_IN, stack.W["o"][l], q8, sc[1:2], y_o, ws)
-            tq.tq_quant_act(y_o, q5, sc[2:3])
-            tq.tq_gemv_gate_up_swiglu(fmt, 1, INTER, HIDDEN, stack.W["gate"][l], stack.W["up"][l],
-                                      q5, sc[2:3], h, ws)
-            tq.tq_quant_act(h, q17, sc[3:4])
-            tq.tq_gemv(fmt, 1, HIDDEN, INTER, stack.W["down"][l], q17, sc[3:4], y_dn[l:l + 1], ws)
+            tq.tq_gemv(fmt, 1, HIDDEN, O_IN, stack.W["o"][l], q8, sc[1:2], yo1, ws)
+            tq.tq_quant_act(yo1, q5, sc[2:3])
+            tq.tq_gemv_gate_up_swiglu(fmt, 1, INTER, HIDDEN, stack.W["gate"][l],
+                                      stack.W["up"][l], q5, sc[2:3], h1, ws)
+            tq.tq_quant_act(h1, q17, sc[3:4])
+            tq.tq_gemv(fmt, 1, HIDDEN, INTER, stack.W["down"][l], q17, sc[3:4], yd1, ws)
+
+    def gate_up_all():
+        for l in range(L):
+            tq.tq_gemv_gate_up_swiglu(fmt, 1, INTER, HIDDEN, stack.W["gate"][l],
+                                      stack.W["up"][l], q5, sc[2:3], h1, ws)
 
     # A plain device copy of known size (64 MiB read + 64 MiB written), untimed:
     # profiles of this command use it to calibrate the FETCH_SIZE / WRITE_SIZE
@@ -129,48 +147,42 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
-    # capture one token as a graph (512 launches) and replay it
     cap = torch.cuda.Stream()
-    token()  # eager run: loads kernels, checks arguments
-    torch.cuda.synchronize()
-    with torch.cuda.stream(cap):
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=cap):
-            token()
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    assert torch.isfinite(y_dn).all().item(), "non-finite output"
+
+    def capture(fn):
+        fn()  # eager run: loads kernels, checks arguments
+        torch.cuda.synchronize()
+        with torch.cuda.stream(cap):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, steps, warmup):
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    # ---- timed region: K tokens through the stack ---------------------------
+    graph = capture(token)
+    ms_per_step = time_graph(graph, args.steps, args.warmup)
+    assert torch.isfinite(y_dn).all().item() and torch.isfinite(h).all().item(), "non-finite"
     tok_s = 1000.0 / ms_per_step
     stream_gbps = stack.step_weight_bytes / (ms_per_step * 1e-3) / 1e9
+    sep_ms = time_graph(capture(token_separate), max(3, args.steps // 4), 1)
 
-    # ---- dominant kernel: the fused gate/up/SwiGLU GEMV, timed on its own over
-    # the same 64 layers' weights (graph of L launches, HIP events around it)
+    # ---- dominant kernel: the fused gate/up/SwiGLU projection, timed on its
+    # own over the same 64 layers' weights (graph of L launches, HIP events)
     gu_bytes = 2 * stack.bytes["gate"] + HIDDEN + 4 + INTER * 4
-    with torch.cuda.stream(cap):
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g2, stream=cap):
-            for l in range(L):
-                tq.tq_gemv_gate_up_swiglu(fmt, 1, INTER, HIDDEN, stack.W["gate"][l],
-                                          stack.W["up"][l], q5, sc[2:3], h, ws)
-    torch.cuda.synchronize()
-    g2.replay()
-    torch.cuda.synchronize()
-    reps = 5
-    e0.record()
-    for _ in range(reps):
-        g2.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    gu_us = e0.elapsed_time(e1) * 1000.0 / (reps * L)
+    gu_us = time_graph(capture(gate_up_all), 5, 1) * 1000.0 / L
     gu_gbps = gu_bytes / (gu_us * 1e-6) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -180,13 +192,11 @@ def main():
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(gu_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(gu_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                "kernel": "gemv_kernel<fmt,1,2,false> (tq_gemv_gate_up_swiglu, 17408x5120 x2)",
+                "kernel": "proj_kernel<fmt,2> (fused gate/up/SwiGLU, 2 x 17408x5120)",
                 "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3)}
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
-    cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(synth, args.cpu_seconds, args.fmt)
+    cpu = cpu_baseline(synth, args.cpu_seconds, args.fmt) if args.cpu_seconds > 0 else None
 
     out = {
         "metric": METRIC,
@@ -207,6 +217,7 @@ def main():
                    "weight_bytes_per_token": stack.step_weight_bytes},
         "weight_stream_GBps": round(stream_gbps, 1),
         "weight_stream_frac_of_8TBps": round(stream_gbps / PEAK_HBM_GBPS, 4),
+        "separate_launch_tok_s": round(1000.0 / sep_ms, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

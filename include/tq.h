@@ -141,6 +141,39 @@ int tq_gemv_gate_up_swiglu(int fmt, int64_t M, int64_t N, int64_t K, const void 
                            const void *Wu, const int8_t *q, const float *a_scale, float *h,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* ---- device: decode stack --------------------------------------------- */
+
+/* Packed weights of one layer (device pointers, tq_pack layout). */
+typedef struct {
+  const void *qkv;  /* qkv_out x hidden */
+  const void *o;    /* hidden x o_in */
+  const void *gate; /* inter x hidden */
+  const void *up;   /* inter x hidden */
+  const void *down; /* hidden x inter */
+} tq_layer;
+
+/* Workspace bytes of tq_decode_stack (zero-filled once before first use,
+ * left zero-filled by every call). */
+size_t tq_decode_stack_workspace_bytes(int fmt, int64_t layers, int64_t hidden, int64_t inter,
+                                       int64_t qkv_out, int64_t o_in);
+
+/* One decode token (batch 1) through `layers` projection layers.  Layer l:
+ *   y_qkv[l] = QKV  . quant(x_in[l])          (x_in fp16 [layers][hidden])
+ *   y_o[l]   = O    . quant(a_in[l])          (a_in fp16 [layers][o_in])
+ *   h[l]     = silu(gate . quant(y_o[l])) * (up . quant(y_o[l]))
+ *   y_out[l] = down . quant(h[l])
+ * Every quant is tq_quant_act's per-row absmax int8 quantisation (done
+ * inside the projections that consume it); every product is tq_gemv's.
+ * x_in and a_in are the layer inputs that the attention and normalisation
+ * steps (not part of this library) would produce.  Outputs are fp32,
+ * [layers][N].  The call enqueues 2*layers+1 kernel launches on `stream`
+ * (graph-capturable): {down of layer l-1, QKV and O of layer l} share one
+ * launch, gate/up of layer l has its own. */
+int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t inter, int64_t qkv_out,
+                    int64_t o_in, const tq_layer *weights /* host array [layers] */,
+                    const void *x_in, const void *a_in, float *y_qkv, float *y_o, float *h,
+                    float *y_out, void *ws, size_t ws_bytes, void *stream);
+
 /* ---- device: prefill GEMM --------------------------------------------- */
 
 /* Workspace bytes tq_gemm needs (same zero-fill rule as above). */

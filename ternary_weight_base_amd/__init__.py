@@ -30,7 +30,14 @@ _STATUS = {0: "TQ_OK", -1: "TQ_ERR_NULL", -2: "TQ_ERR_SHAPE", -3: "TQ_ERR_ALIGN"
 
 EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant_act",
            "tq_gemv_workspace_bytes", "tq_gemv", "tq_gemv_gate_up_swiglu",
-           "tq_gemm_workspace_bytes", "tq_gemm", "tq_debug_unpack", "tq_debug_group_sums")
+           "tq_gemm_workspace_bytes", "tq_gemm", "tq_debug_unpack", "tq_debug_group_sums",
+           "tq_decode_stack_workspace_bytes", "tq_decode_stack")
+
+
+class TqLayer(ctypes.Structure):
+    """Packed weights of one layer (device addresses), as tq_layer in tq.h."""
+    _fields_ = [("qkv", ctypes.c_void_p), ("o", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("up", ctypes.c_void_p), ("down", ctypes.c_void_p)]
 
 
 class TQError(RuntimeError):
@@ -57,6 +64,8 @@ def _load():
         "tq_gemm": ([I, I64, I64, I64, P, P, P, P, P, SZ, P], I),
         "tq_debug_unpack": ([I, I64, I64, P, P, P], I),
         "tq_debug_group_sums": ([I, I64, I64, I64, P, P, P, I, P], I),
+        "tq_decode_stack_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
+        "tq_decode_stack": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -170,6 +179,30 @@ def tq_debug_unpack(fmt, N, K, W, trits, stream=None) -> None:
 def tq_debug_group_sums(fmt, M, N, K, W, q, S, use_gemm_path=False, stream=None) -> None:
     _check(lib.tq_debug_group_sums(fmt, M, N, K, _ptr(W), _ptr(q), _ptr(S), int(use_gemm_path),
                                    _stream(stream)), "tq_debug_group_sums")
+
+
+def tq_decode_stack_workspace_bytes(fmt, layers, hidden, inter, qkv_out, o_in) -> int:
+    return int(lib.tq_decode_stack_workspace_bytes(fmt, layers, hidden, inter, qkv_out, o_in))
+
+
+def tq_decode_stack(fmt, layers, hidden, inter, qkv_out, o_in, weights, x_in, a_in,
+                    y_qkv, y_o, h, y_out, ws, stream=None) -> None:
+    """weights: list of (qkv, o, gate, up, down) device tensors per layer (or a
+    ctypes array of TqLayer built once with stack_layers())."""
+    arr = weights if isinstance(weights, ctypes.Array) else stack_layers(weights)
+    wp, wb = _ws(ws)
+    _check(lib.tq_decode_stack(fmt, layers, hidden, inter, qkv_out, o_in,
+                               ctypes.cast(arr, ctypes.c_void_p), _ptr(x_in), _ptr(a_in),
+                               _ptr(y_qkv), _ptr(y_o), _ptr(h), _ptr(y_out), wp, wb,
+                               _stream(stream)), "tq_decode_stack")
+
+
+def stack_layers(weights):
+    """Host array of TqLayer from [(qkv, o, gate, up, down), ...] device tensors."""
+    arr = (TqLayer * len(weights))()
+    for i, w in enumerate(weights):
+        arr[i] = TqLayer(*[_ptr(t) for t in w])
+    return arr
 
 
 def workspace(fmt: int, M: int, N: int, K: int, device="cuda"):

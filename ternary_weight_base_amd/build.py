@@ -33,12 +33,15 @@ def build() -> str:
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
     host_o = os.path.join(bdir, "tq_host.o")
-    dev_o = os.path.join(bdir, "tq_kernels.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-fopenmp", "-Wall", "-Wextra", "-I", INC,
           "-c", os.path.join(CSRC, "tq_host.cpp"), "-o", host_o])
-    _run(["hipcc", *HIP_FLAGS, "-I", INC, "-c", os.path.join(CSRC, "tq_kernels.hip"), "-o", dev_o])
+    objs = []
+    for src in ("tq_kernels.hip", "tq_proj.hip"):
+        o = os.path.join(bdir, src.replace(".hip", ".o"))
+        _run(["hipcc", *HIP_FLAGS, "-I", INC, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", o])
+        objs.append(o)
     tmp = LIB + ".tmp"
-    _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, dev_o, host_o,
+    _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, host_o,
           "-fopenmp=libgomp", "-lgomp"])
     os.replace(tmp, LIB)
     return LIB

@@ -1,0 +1,160 @@
+// tq_device.h -- device helpers shared by the HIP kernels of libtq: the B3
+// digit table in LDS, the per-group integer cores of both packed formats,
+// and small bit utilities.  Internal to the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_layout.h"
+
+namespace tqdev {
+
+constexpr int kLutCopies = 32;   // one table copy per lane of a half wave
+constexpr int kLutEntries = 256; // byte values; 243..255 map to zero trits
+constexpr int kWavesMax = 8;     // waves per GEMV workgroup
+constexpr int kGsMax = 8;        // groups per wave slice (all prefetched)
+
+typedef long v2l __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+__device__ __forceinline__ uint32_t perm_b32(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+__device__ __forceinline__ float half_bits(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// ---------------------------------------------------------------------
+// B3 digit table.  For byte value v (0..242): .lo holds the trits of base-3
+// digits 0..3 of v (one signed byte each), .hi the trit of digit 4 in byte 0;
+// values 243..255 (never produced by the packer) decode to zero trits.
+// Each workgroup builds it in LDS 32 times, entry v of copy c at byte
+// (v * 32 + c) * 8.  Lane l reads copy
+// l % 32, so the 32 lanes served together hit 32 distinct bank pairs
+// whatever byte values they hold.
+// ---------------------------------------------------------------------
+__device__ __forceinline__ uint2 b3_entry(int v) {
+  uint32_t lo = 0, hi = 0;
+  if (v < 243) {
+    int x = v;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      lo |= (uint32_t)(uint8_t)(int8_t)(x % 3 - 1) << (8 * i);
+      x /= 3;
+    }
+    hi = (uint32_t)(uint8_t)(int8_t)(x - 1);
+  }
+  return make_uint2(lo, hi);
+}
+
+// Fill the 32 copies.  With a block size that is a multiple of 256 every
+// thread computes one entry v and stores it into 32 / (blockDim / 256) of the
+// copies; lane l starts at copy l % 32, so the 32 lanes of a store hit 32
+// distinct bank pairs.
+__device__ __forceinline__ void fill_b3_lut(uint2 *lut) {
+  if ((blockDim.x & 255u) == 0) {
+    const int v = threadIdx.x & 255;
+    const uint2 e = b3_entry(v);
+    const int per = kLutCopies / (int)(blockDim.x >> 8);
+    const int k0 = (int)(threadIdx.x >> 8) * per;
+    for (int k = k0; k < k0 + per; k++) lut[v * kLutCopies + ((threadIdx.x + k) & (kLutCopies - 1))] = e;
+  } else {
+    for (int idx = threadIdx.x; idx < kLutEntries * kLutCopies; idx += blockDim.x)
+      lut[idx] = b3_entry(idx / kLutCopies);
+  }
+}
+
+// Look up byte k of `word`: one v_perm builds the LDS address
+// (byte value in bits 8..15, the lane's copy offset in bits 0..7).
+template <int k>
+__device__ __forceinline__ uint2 lut_lookup(const uint2 *lut, uint32_t word, uint32_t laneoff) {
+  constexpr uint32_t sel = 0x0C0C0000u | ((4u + k) << 8);
+  uint32_t addr = perm_b32(word, laneoff, sel);
+  return *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(lut) + addr);
+}
+
+template <int j>
+__device__ __forceinline__ uint2 b3_byte(const uint2 *lut, const uint32_t (&w)[7],
+                                         uint32_t laneoff) {
+  return lut_lookup<j & 3>(lut, w[j >> 2], laneoff);
+}
+
+// Activations of one group for MT rows, as 32 words per row: either held in
+// (scalar) registers, or read through wave-uniform pointers on use.
+template <int MT>
+struct XRegs {
+  uint32_t v[MT][32];
+  __device__ __forceinline__ uint32_t get(int m, int i) const { return v[m][i]; }
+};
+template <int MT>
+struct XPtrs {
+  const uint32_t *__restrict__ p[MT];
+  __device__ __forceinline__ uint32_t get(int m, int i) const { return p[m][i]; }
+};
+
+// Integer core of one B3 group for MT activation rows.
+//   w[0..3]: device bytes 0..15, w[4..6]: bytes 16..25 and the scale.
+// byte j < 25: digits 0..3 pair with activation word j, digit 4 with byte
+// j % 4 of word 25 + j / 4; byte 25: digits 1..3 pair with bytes 1..3 of
+// word 31 (its digit 0 is a zero-trit padding digit).
+template <int MT, typename XS>
+__device__ __forceinline__ void b3_group(const uint2 *lut, uint32_t laneoff,
+                                         const uint32_t (&w)[7], const XS &x, int (&S)[MT]) {
+  // All 26 table lookups are issued before the first dot so that the LDS
+  // latency overlaps; two accumulator chains per row halve the dependency.
+  uint2 e[26];
+#define TQ_LK(J) e[J] = b3_byte<J>(lut, w, laneoff);
+  TQ_LK(0) TQ_LK(1) TQ_LK(2) TQ_LK(3) TQ_LK(4) TQ_LK(5) TQ_LK(6) TQ_LK(7) TQ_LK(8)
+  TQ_LK(9) TQ_LK(10) TQ_LK(11) TQ_LK(12) TQ_LK(13) TQ_LK(14) TQ_LK(15) TQ_LK(16)
+  TQ_LK(17) TQ_LK(18) TQ_LK(19) TQ_LK(20) TQ_LK(21) TQ_LK(22) TQ_LK(23) TQ_LK(24)
+  TQ_LK(25)
+#undef TQ_LK
+  int S2[MT];
+#pragma unroll
+  for (int m = 0; m < MT; m++) S2[m] = 0;
+#pragma unroll
+  for (int j = 0; j < 25; j++) {
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+      S[m] = sdot4(e[j].x, x.get(m, j), S[m]);
+      S2[m] = sdot4(e[j].y, x.get(m, 25 + (j >> 2)) >> (8 * (j & 3)), S2[m]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MT; m++) S[m] = sdot4(e[25].x, x.get(m, 31), S[m]) + S2[m];
+}
+
+// Integer core of one 2B group.  Device byte 4c' + c, bits 2s hold
+// k = 16c' + 4s + c, so field s of word c' pairs with activation word
+// 4c' + s.  Codes d = t + 1 are dotted directly (fields masked in place, so
+// field s arrives multiplied by 4^s, or by 16 for s = 3 after a 2-bit shift)
+// and the group's activation sum is subtracted: sum t*x = sum d*x - sum x.
+template <int MT, typename XS>
+__device__ __forceinline__ void tb_group(const uint32_t (&w)[9], const XS &x,
+                                         const int (&xsum)[MT], int (&S)[MT]) {
+  int a1[MT], a4[MT], a16[MT];
+#pragma unroll
+  for (int m = 0; m < MT; m++) a1[m] = a4[m] = a16[m] = 0;
+#pragma unroll
+  for (int c = 0; c < 8; c++) {
+    const uint32_t v = w[c];
+    const uint32_t f0 = v & 0x03030303u, f1 = v & 0x0C0C0C0Cu, f2 = v & 0x30303030u,
+                   f3 = (v >> 2) & 0x30303030u;
+#pragma unroll
+    for (int m = 0; m < MT; m++) {
+      a1[m] = sdot4(f0, x.get(m, 4 * c + 0), a1[m]);
+      a4[m] = sdot4(f1, x.get(m, 4 * c + 1), a4[m]);
+      a16[m] = sdot4(f2, x.get(m, 4 * c + 2), a16[m]);
+      a16[m] = sdot4(f3, x.get(m, 4 * c + 3), a16[m]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MT; m++) S[m] = a1[m] + (a4[m] >> 2) + (a16[m] >> 4) - xsum[m];
+}
+
+}  // namespace tqdev

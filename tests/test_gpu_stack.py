@@ -1,0 +1,106 @@
+"""GPU parity of tq_decode_stack (the fused-launch decode stack) against the
+oracle, layer by layer.  Each stage is checked on the GPU's own input of that
+stage (stage-isolated), because chained fp32 stages cannot be bit-exact
+end-to-end (an ulp of difference can move an int8 across a rounding tie);
+the chain as a whole is checked within the same tolerance."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import B3, TB, FMTS, assert_close, dev, say
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.set_threads(8)
+
+
+def _run_stack(fmt, L, hidden, inter, qkv_out, o_in, seed):
+    import ternary_weight_base_amd as tq
+    shapes = {"qkv": (qkv_out, hidden), "o": (hidden, o_in), "gate": (inter, hidden),
+              "up": (inter, hidden), "down": (hidden, inter)}
+    host, devw = [], []
+    for l in range(L):
+        hw, dw = {}, []
+        for i, (name, (N, K)) in enumerate(shapes.items()):
+            t = synth.trits(synth.seed(seed, l, i, 1), N, K)
+            s = synth.scales(synth.seed(seed, l, i, 2), N, K)
+            hw[name] = (t, s)
+            dw.append(dev(tq.tq_pack(fmt, t, s)))
+        host.append(hw)
+        devw.append(dw)
+    x = synth.normal_f16(synth.seed(seed, 99, 1), L, hidden)
+    a = synth.normal_f16(synth.seed(seed, 99, 2), L, o_in)
+    y_qkv = torch.full((L, qkv_out), float("nan"), device="cuda")
+    y_o = torch.full((L, hidden), float("nan"), device="cuda")
+    h = torch.full((L, inter), float("nan"), device="cuda")
+    y_out = torch.full((L, hidden), float("nan"), device="cuda")
+    nbytes = tq.tq_decode_stack_workspace_bytes(fmt, L, hidden, inter, qkv_out, o_in)
+    ws = torch.zeros((nbytes + 15) // 16 * 4, dtype=torch.int32, device="cuda")
+    outs = []
+    for rep in range(2):  # twice: the workspace must come back ready for reuse
+        tq.tq_decode_stack(fmt, L, hidden, inter, qkv_out, o_in, devw, dev(x), dev(a),
+                           y_qkv, y_o, h, y_out, ws)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy().copy() for t in (y_qkv, y_o, h, y_out)])
+    for r0, r1 in zip(*outs):
+        assert np.array_equal(r0.view(np.uint32), r1.view(np.uint32)), "not deterministic"
+    return host, x, a, outs[0]
+
+
+def _check_layers(host, x, a, outs, what):
+    y_qkv, y_o, h, y_out = outs
+    for l, hw in enumerate(host):
+        q, s = oracle.quant(x[l:l + 1])
+        assert_close(y_qkv[l:l + 1], oracle.gemv(*hw["qkv"], q, s), f"{what} qkv[{l}]")
+        q, s = oracle.quant(a[l:l + 1])
+        assert_close(y_o[l:l + 1], oracle.gemv(*hw["o"], q, s), f"{what} o[{l}]")
+        q, s = oracle.quant(y_o[l:l + 1])  # stage-isolated: the GPU's y_o
+        h_ref = oracle.swiglu(oracle.gemv(*hw["gate"], q, s), oracle.gemv(*hw["up"], q, s))
+        assert_close(h[l:l + 1], h_ref, f"{what} h[{l}]")
+        q, s = oracle.quant(h[l:l + 1])  # stage-isolated: the GPU's h
+        assert_close(y_out[l:l + 1], oracle.gemv(*hw["down"], q, s), f"{what} down[{l}]")
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
+@pytest.mark.parametrize("L,hidden,inter,qkv_out,o_in", [(3, 640, 1152, 1280, 1024),
+                                                          (2, 384, 2176, 1600, 768)])
+def test_decode_stack_small(fmt, L, hidden, inter, qkv_out, o_in):
+    say(f"stack {FMTS[fmt]} L={L} {hidden}/{inter}/{qkv_out}/{o_in}")
+    host, x, a, outs = _run_stack(fmt, L, hidden, inter, qkv_out, o_in, 11 + L)
+    _check_layers(host, x, a, outs, FMTS[fmt])
+
+
+def test_decode_stack_full_shapes_two_layers():
+    """The 27B-shaped layer (hidden 5120, intermediate 17408, QKV 10240, O 8192),
+    two layers, B3."""
+    say("stack b3 full shapes L=2")
+    host, x, a, outs = _run_stack(B3, 2, 5120, 17408, 10240, 8192, 5)
+    _check_layers(host, x, a, outs, "full")
+
+
+def test_decode_stack_matches_separate_calls():
+    """The fused launches compute what tq_quant_act followed by tq_gemv and
+    tq_gemv_gate_up_swiglu compute (within tolerance; bit patterns may differ
+    only through fp32 summation order)."""
+    import ternary_weight_base_amd as tq
+    say("stack vs separate calls")
+    L, hidden, inter, qkv_out, o_in = 2, 640, 1152, 1280, 1024
+    host, x, a, outs = _run_stack(B3, L, hidden, inter, qkv_out, o_in, 21)
+    y_o = outs[1]
+    for l, hw in enumerate(host):
+        Wg = dev(tq.tq_pack(B3, *hw["gate"]))
+        Wu = dev(tq.tq_pack(B3, *hw["up"]))
+        q = torch.empty((1, hidden), dtype=torch.int8, device="cuda")
+        sc = torch.empty(1, dtype=torch.float32, device="cuda")
+        tq.tq_quant_act(dev(y_o[l:l + 1]), q, sc)
+        hh = torch.empty((1, inter), dtype=torch.float32, device="cuda")
+        tq.tq_gemv_gate_up_swiglu(B3, 1, inter, hidden, Wg, Wu, q, sc, hh, tq.workspace(B3, 1, inter, hidden))
+        torch.cuda.synchronize()
+        assert_close(outs[2][l:l + 1], hh.cpu().numpy(), f"h[{l}] vs separate")

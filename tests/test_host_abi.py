@@ -241,6 +241,27 @@ def test_device_entry_points_validate_on_host():
     assert L.tq_debug_group_sums(B3, 1, 64, 128, FAKE, MIS, FAKE, 1, None) == -3
 
 
+def test_decode_stack_validates_on_host():
+    L = tq.lib
+    args = (B3, 2, 640, 1152, 1280, 1024)
+    need = tq.tq_decode_stack_workspace_bytes(*args)
+    assert need > 0
+    assert tq.tq_decode_stack_workspace_bytes(B3, 0, 640, 1152, 1280, 1024) == 0
+    assert tq.tq_decode_stack_workspace_bytes(B3, 2, 600, 1152, 1280, 1024) == 0
+    good = (tq.TqLayer * 2)(*[tq.TqLayer(FAKE, FAKE, FAKE, FAKE, FAKE)] * 2)
+    bad = (tq.TqLayer * 2)(tq.TqLayer(FAKE, FAKE, FAKE, FAKE, FAKE), tq.TqLayer(FAKE, None, FAKE, FAKE, FAKE))
+    mis = (tq.TqLayer * 2)(tq.TqLayer(FAKE, FAKE, FAKE, FAKE, FAKE), tq.TqLayer(FAKE, FAKE, MIS, FAKE, FAKE))
+    c = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    outs = (FAKE,) * 4
+    assert L.tq_decode_stack(*args, c(good), FAKE, FAKE, *outs, FAKE, need - 1, None) == -7
+    assert L.tq_decode_stack(*args, c(bad), FAKE, FAKE, *outs, FAKE, need, None) == -1
+    assert L.tq_decode_stack(*args, c(mis), FAKE, FAKE, *outs, FAKE, need, None) == -3
+    assert L.tq_decode_stack(*args, c(good), MIS, FAKE, *outs, FAKE, need, None) == -3
+    assert L.tq_decode_stack(*args, c(good), FAKE, FAKE, FAKE, ODD, FAKE, FAKE, FAKE, need, None) == -3
+    assert L.tq_decode_stack(*args, None, FAKE, FAKE, *outs, FAKE, need, None) == -1
+    assert L.tq_decode_stack(5, 2, 640, 1152, 1280, 1024, c(good), FAKE, FAKE, *outs, FAKE, need, None) == -5
+
+
 def test_workspace_sizes():
     assert tq.tq_gemv_workspace_bytes(B3, 1, 1024, 1024) == 0
     for N, K in ((5120, 8192), (5120, 17408), (10240, 5120)):
