@@ -163,12 +163,15 @@ size_t tq_decode_stack_workspace_bytes(int fmt, int64_t layers, int64_t hidden, 
  *   h[l]     = silu(gate . quant(y_o[l])) * (up . quant(y_o[l]))
  *   y_out[l] = down . quant(h[l])
  * Every quant is tq_quant_act's per-row absmax int8 quantisation (done
- * inside the projections that consume it); every product is tq_gemv's.
- * x_in and a_in are the layer inputs that the attention and normalisation
- * steps (not part of this library) would produce.  Outputs are fp32,
- * [layers][N].  The call enqueues 2*layers+1 kernel launches on `stream`
- * (graph-capturable): {down of layer l-1, QKV and O of layer l} share one
- * launch, gate/up of layer l has its own. */
+ * inside the projection that consumes it, bit-exact with tq_quant_act);
+ * every product is tq_gemv's.  x_in and a_in are the layer inputs that the
+ * attention and normalisation steps (not part of this library) would
+ * produce.  Outputs are fp32, [layers][N]; y_o, h and the workspace must be
+ * 16-byte aligned, hidden and inter multiples of 128.  The call enqueues
+ * 4*layers kernel launches on `stream` (graph-capturable), one per
+ * projection, in the order QKV, O, gate/up, down of layer 0, then layer 1,
+ * ...: each starts after the previous one ends, as the projections of a
+ * decoder must. */
 int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t inter, int64_t qkv_out,
                     int64_t o_in, const tq_layer *weights /* host array [layers] */,
                     const void *x_in, const void *a_in, float *y_qkv, float *y_o, float *h,

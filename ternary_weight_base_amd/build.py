@@ -17,16 +17,30 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _run(cmd):
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
+NOISE = "is not a recognized feature for this target"
+
+
+def _report(cmd, rc, out):
+    if rc != 0:
+        sys.stderr.write(out)
         raise RuntimeError("build step failed: " + " ".join(cmd))
     # keep real diagnostics, drop hipcc's host-pass notice about the device-only feature
-    noise = "is not a recognized feature for this target"
-    for line in (r.stdout + r.stderr).splitlines():
-        if noise not in line and line.strip():
+    for line in out.splitlines():
+        if NOISE not in line and line.strip():
             sys.stderr.write(line + "\n")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    _report(cmd, r.returncode, r.stdout + r.stderr)
+
+
+def _run_parallel(cmds):
+    procs = [(c, subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+             for c in cmds]
+    for c, p in procs:
+        out, _ = p.communicate()
+        _report(c, p.returncode, out)
 
 
 def build() -> str:
@@ -35,11 +49,13 @@ def build() -> str:
     host_o = os.path.join(bdir, "tq_host.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-fopenmp", "-Wall", "-Wextra", "-I", INC,
           "-c", os.path.join(CSRC, "tq_host.cpp"), "-o", host_o])
-    objs = []
-    for src in ("tq_kernels.hip", "tq_proj.hip"):
+    objs, cmds = [], []
+    for src in ("tq_kernels.hip", "tq_proj.hip", "tq_proj_b3.hip", "tq_proj_2b.hip"):
         o = os.path.join(bdir, src.replace(".hip", ".o"))
-        _run(["hipcc", *HIP_FLAGS, "-I", INC, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", o])
+        cmds.append(["hipcc", *HIP_FLAGS, "-I", INC, "-I", CSRC, "-c", os.path.join(CSRC, src),
+                     "-o", o])
         objs.append(o)
+    _run_parallel(cmds)
     tmp = LIB + ".tmp"
     _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, host_o,
           "-fopenmp=libgomp", "-lgomp"])

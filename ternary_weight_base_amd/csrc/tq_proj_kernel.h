@@ -1,0 +1,345 @@
+// tq_proj_kernel.h -- the one-token projection kernel: activation quantiser
+// fused in, weight stream software-pipelined.  Included by the per-format
+// instantiation units tq_proj_b3.hip and tq_proj_2b.hip.
+//
+// What is computed is the decode GEMV of include/tq.h: per group of 128
+// weights an integer dot of decoded trits with int8 activations, scaled by
+// the group's fp16 scale ("三值权重 27B 压到 5.9GB｜本地部署成本账单重算",
+// section 三; "Ternary Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section
+// "Decode 为什么只能算一般"), the activations quantised per token to int8 by
+// absmax (same page, section "后面还有没有优化空间").  The Bonsai page runs
+// the activation quantiser as its own launch and measures it at about 1.1 us;
+// here it is folded into the projection that consumes it.
+//
+// Workgroup (block b, chunk c) owns one 64-row weight block and a balanced
+// chunk of its K groups; each of its 8 waves takes GS consecutive groups of
+// the chunk, one lane per weight row.  Per wave, in program order:
+//   1. issue the loads of its activation slice (and of what the absmax
+//      needs), then the weight loads of its first D groups;
+//   2. fill the B3 digit table, barrier;
+//   3. absmax -> quantise its slice in registers (bit-exact with
+//      tq_quant_act; int8 input arrives quantised), move each group's 32
+//      int8 words into SGPRs with v_readlane;
+//   4. for each group i: issue group i + D, then decode + dot group i.
+// Issuing everything at once stalls each wave on a full memory queue until
+// most of its data has arrived, so decode would only start after the whole
+// transfer; the D-deep pipeline lets decode run while later groups stream.
+// The waves' partial sums meet in LDS; with several K chunks per block, the
+// last chunk to finish (agent-scope counter) adds the partials in chunk
+// order, so results do not depend on timing.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+#include "tq_device.h"
+#include "tq_layout.h"
+#include "tq_proj.h"
+
+namespace tqproj {
+
+using namespace tqdev;
+using tq::Layout;
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// The quantiser's fp32 steps for four values: rint(v * inv), clamp to
+// [-127, 127]; packed as four int8 in one word.
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float inv, bool zero) {
+  const float v[4] = {a, b, c, d};
+  uint32_t p = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    float r = rintf(v[i] * inv);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    const int qi = zero ? 0 : (int)r;
+    p |= (uint32_t)(uint8_t)(int8_t)qi << (8 * i);
+  }
+  return p;
+}
+
+__device__ __forceinline__ float habs_max8(uint4 u, float m) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int t = 0; t < 4; t++)
+    m = fmaxf(m, fmaxf(fabsf(half_bits(w[t] & 0xffffu)), fabsf(half_bits(w[t] >> 16))));
+  return m;
+}
+
+template <int FMT, int NMAT, int IN, int GS, int D>
+__global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs A) {
+  constexpr int WPG = FMT == 0 ? 7 : 9;   // words per (row, group) in registers
+  constexpr int NP = (GS + 1) / 2;        // group pairs: one activation word per lane each
+  constexpr int D0 = D < GS ? D : GS;
+  __shared__ uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
+  __shared__ float red[NMAT * kNW * 64];
+  __shared__ float wmax[kNW];
+
+  const Layout L(FMT, A.N, A.K);
+  const int G = (int)L.G, N = A.N, K = A.K;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x / A.C, c = blockIdx.x - b * A.C;
+  const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
+  const int gbeg = (int)((int64_t)c * G / A.C), gend = (int)((int64_t)(c + 1) * G / A.C);
+  const int g0 = gbeg + wave * GS;               // first group of this wave
+  const int ng = max(0, min(gend - g0, GS));     // live groups of this wave
+  const int glast = gend - 1;                    // dead slots reload this group
+  const int lr = min(lane, Wb - 1);
+  const uint8_t *Wm[2] = {A.W0, A.W1};
+
+  // ---- 1a. activation slice: lane l holds word l % 32 of group 2p + l / 32
+  // (int8 input: the words themselves; fp16 / fp32: four values to quantise)
+  const int hsel = lane >> 5, word = lane & 31;
+  float4 xf[IN == kInF32 ? NP : 1];
+  uint2 xh[IN == kInF16 ? NP : 1];
+  uint32_t qv[NP];
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    const int gp = min(g0 + 2 * p + hsel, glast);
+    const size_t off = (size_t)gp * tq::kGroup + 4 * (size_t)word;
+    if constexpr (IN == kInF32) xf[p] = *reinterpret_cast<const float4 *>((const float *)A.in + off);
+    else if constexpr (IN == kInF16) xh[p] = *reinterpret_cast<const uint2 *>((const uint16_t *)A.in + off);
+    else qv[p] = *reinterpret_cast<const uint32_t *>((const int8_t *)A.in + off);
+  }
+  // ---- 1b. what the absmax needs
+  float bm[IN == kInF32 ? kBmaxPerLane : 1];
+  uint4 xm[IN == kInF16 ? kXmaxLoads : 1];
+  if constexpr (IN == kInF32) {
+#pragma unroll
+    for (int i = 0; i < kBmaxPerLane; i++) bm[i] = A.in_aux[min(lane + 64 * i, A.in_nb - 1)];
+  }
+  if constexpr (IN == kInF16) {
+#pragma unroll
+    for (int i = 0; i < kXmaxLoads; i++)
+      xm[i] = reinterpret_cast<const uint4 *>(A.in)[min(tid + kThreads * i, K / 8 - 1)];
+  }
+
+  // ---- 1c. weight loads of the first D groups (dead slots: a live group)
+  uint32_t wd[NMAT][GS][WPG];
+  auto issue = [&](int i) {
+    int gi = min(g0 + i, glast);
+    asm volatile("" : "+v"(gi));  // keeps the loads at this point of the program
+#pragma unroll
+    for (int mat = 0; mat < NMAT; mat++) {
+      const uint8_t *gb = Wm[mat] + L.group_base(b, gi);
+      const uint4 P = *reinterpret_cast<const uint4 *>(gb + lr * 16);
+      wd[mat][i][0] = P.x;
+      wd[mat][i][1] = P.y;
+      wd[mat][i][2] = P.z;
+      wd[mat][i][3] = P.w;
+      if constexpr (FMT == 0) {
+        const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + lr * 12);
+        wd[mat][i][4] = pb[0];
+        wd[mat][i][5] = pb[1];
+        wd[mat][i][6] = pb[2];
+      } else {
+        const uint4 Q = *reinterpret_cast<const uint4 *>(gb + Wb * 16 + lr * 16);
+        wd[mat][i][4] = Q.x;
+        wd[mat][i][5] = Q.y;
+        wd[mat][i][6] = Q.z;
+        wd[mat][i][7] = Q.w;
+        wd[mat][i][8] = *reinterpret_cast<const uint16_t *>(gb + Wb * 32 + lr * 2);
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < D0; i++) issue(i);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. digit table; fp16 input: per-wave maxima of the whole x ----------
+  if constexpr (FMT == 0) fill_b3_lut(lut);
+  if constexpr (IN == kInF16) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kXmaxLoads; i++) m = habs_max8(xm[i], m);
+    for (int j = tid + kThreads * kXmaxLoads; j < K / 8; j += kThreads)
+      m = habs_max8(reinterpret_cast<const uint4 *>(A.in)[j], m);
+    m = wave_max(m);
+    if (lane == 0) wmax[wave] = m;
+  }
+  __syncthreads();
+
+  // ---- 3. absmax, quantise the slice ----------------------------------------
+  float a_scale;
+  if constexpr (IN == kInInt8) {
+    a_scale = A.in_aux[0];
+  } else {
+    float amax = 0.0f;
+    if constexpr (IN == kInF16) {
+#pragma unroll
+      for (int w = 0; w < kNW; w++) amax = fmaxf(amax, wmax[w]);
+    } else {
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kBmaxPerLane; i++) m = fmaxf(m, bm[i]);
+      for (int j = lane + 64 * kBmaxPerLane; j < A.in_nb; j += 64) m = fmaxf(m, A.in_aux[j]);
+      amax = wave_max(m);
+    }
+    const bool zero = amax == 0.0f;
+    const float inv = zero ? 0.0f : 127.0f / amax;  // IEEE division, as the quantiser
+    a_scale = zero ? 0.0f : amax / 127.0f;
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+      if constexpr (IN == kInF32) {
+        qv[p] = quant4(xf[p].x, xf[p].y, xf[p].z, xf[p].w, inv, zero);
+      } else {
+        qv[p] = quant4(half_bits(xh[p].x & 0xffffu), half_bits(xh[p].x >> 16),
+                       half_bits(xh[p].y & 0xffffu), half_bits(xh[p].y >> 16), inv, zero);
+      }
+    }
+  }
+  // 2B: activation sum of every group of the slice (a 32-lane reduction)
+  int xsum[GS];
+  if constexpr (FMT == 1) {
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+      int s = sdot4(qv[p], 0x01010101u, 0);
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off, 32);
+      xsum[2 * p] = __builtin_amdgcn_readlane(s, 0);
+      if (2 * p + 1 < GS) xsum[2 * p + 1] = __builtin_amdgcn_readlane(s, 32);
+    }
+  }
+
+  // ---- 4. pipelined decode + integer dot + scale ---------------------------
+  const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
+  float acc[NMAT];
+#pragma unroll
+  for (int mat = 0; mat < NMAT; mat++) acc[mat] = 0.0f;
+  // Empty asm statements (kept in program order) pin the schedule through
+  // data dependences: a group's weights and activation words enter its
+  // iteration through one, so the wait for its loads lands there; each
+  // matrix's table offset enters through one and its accumulator leaves
+  // through another, so one matrix's lookups are in flight at a time; the
+  // loads of issue() take their group index from one.  Without them the
+  // compiler interleaves iterations and holds several groups' lookups at
+  // once.  No memory clobber: the int8 activation words stay scalar loads.
+#pragma unroll
+  for (int i = 0; i < GS; i++) {
+    if (i + D0 < GS) issue(i + D0);
+#pragma unroll
+    for (int mat = 0; mat < NMAT; mat++)
+#pragma unroll
+      for (int k = 0; k < WPG; k++) asm volatile("" : "+v"(wd[mat][i][k]));
+    asm volatile("" : "+v"(qv[i >> 1]));
+    XRegs<1> xa;
+#pragma unroll
+    for (int k = 0; k < 32; k++) xa.v[0][k] = __builtin_amdgcn_readlane(qv[i >> 1], 32 * (i & 1) + k);
+    const bool live = i < ng;
+#pragma unroll
+    for (int mat = 0; mat < NMAT; mat++) {
+      int S[1] = {0};
+      float sc;
+      if constexpr (FMT == 0) {
+        const uint32_t w[7] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2], wd[mat][i][3],
+                               wd[mat][i][4], wd[mat][i][5], wd[mat][i][6]};
+        uint32_t lo = laneoff;
+        asm volatile("" : "+v"(lo));  // this matrix's lookups start here
+        b3_group<1>(lut, lo, w, xa, S);
+        sc = half_bits(wd[mat][i][6] >> 16);
+      } else {
+        const uint32_t w[9] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2],
+                               wd[mat][i][3], wd[mat][i][4], wd[mat][i][5],
+                               wd[mat][i][6], wd[mat][i][7], wd[mat][i][8]};
+        const int xs[1] = {xsum[i]};
+        tb_group<1>(w, xa, xs, S);
+        sc = half_bits(wd[mat][i][8]);
+      }
+      acc[mat] = fmaf(live ? sc : 0.0f, (float)S[0], acc[mat]);
+      asm volatile("" : "+v"(acc[mat]));  // ... and end here: one matrix at a time
+    }
+  }
+
+  // ---- 5. reduce: waves in LDS, chunks through the workspace ---------------
+#pragma unroll
+  for (int mat = 0; mat < NMAT; mat++) red[(mat * kNW + wave) * 64 + lane] = acc[mat];
+  __syncthreads();
+  if (wave != 0) return;
+  float tot[NMAT];
+#pragma unroll
+  for (int mat = 0; mat < NMAT; mat++) {
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNW; w++) s += red[(mat * kNW + w) * 64 + lane];
+    tot[mat] = s;
+  }
+  const size_t n = (size_t)b * tq::kBlockRows + lane;
+  const bool row_ok = lane < rows;
+  if (A.C > 1) {
+    if (row_ok) {
+#pragma unroll
+      for (int mat = 0; mat < NMAT; mat++)
+        __hip_atomic_store(&A.partials[((size_t)c * NMAT + mat) * N + n], tot[mat],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the partial sums have reached device scope
+    uint32_t prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(&A.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0, 64);
+    if (prev != (uint32_t)(A.C - 1)) return;  // another chunk finishes this block
+#pragma unroll
+    for (int mat = 0; mat < NMAT; mat++) {
+      float s = 0.0f;
+      if (row_ok)
+        for (int cc = 0; cc < A.C; cc++)
+          s += __hip_atomic_load(&A.partials[((size_t)cc * NMAT + mat) * N + n], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      tot[mat] = s;
+    }
+    if (lane == 0) __hip_atomic_store(&A.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  float y;
+  if (NMAT == 1) {
+    y = a_scale * tot[0];
+  } else {
+    const float yg = a_scale * tot[0], yu = a_scale * tot[NMAT - 1];
+    y = yg / (1.0f + expf(-yg)) * yu;
+  }
+  if (row_ok) A.out[n] = y;
+  if (A.out_bmax) {
+    const float m = wave_max(row_ok ? fabsf(y) : 0.0f);
+    if (lane == 0) A.out_bmax[b] = m;
+  }
+}
+
+template <int FMT, int NMAT, int IN>
+int launch_in(const Plan &p, const ProjArgs &A, hipStream_t st) {
+  constexpr int D = NMAT == 2 ? TQ_PROJ_D2 : TQ_PROJ_D1;
+  const dim3 grid((unsigned)(p.NB * p.C)), block(kThreads);
+#define TQ_CASE(G_)                                                                  \
+  case G_:                                                                           \
+    hipLaunchKernelGGL((proj_kernel<FMT, NMAT, IN, G_, D>), grid, block, 0, st, A);  \
+    break;
+  if constexpr (NMAT == 1) {
+    switch (p.gs) {
+      TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5) TQ_CASE(6) TQ_CASE(7) TQ_CASE(8)
+      default: return TQ_ERR_SHAPE;
+    }
+  } else {
+    switch (p.gs) {
+      TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5)
+      default: return TQ_ERR_SHAPE;
+    }
+  }
+#undef TQ_CASE
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+template <int FMT>
+int launch_fmt(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st) {
+  if (nmat == 2) {
+    if (in_kind == kInInt8) return launch_in<FMT, 2, kInInt8>(p, A, st);
+    if (in_kind == kInF32) return launch_in<FMT, 2, kInF32>(p, A, st);
+    return TQ_ERR_DTYPE;
+  }
+  if (in_kind == kInInt8) return launch_in<FMT, 1, kInInt8>(p, A, st);
+  if (in_kind == kInF16) return launch_in<FMT, 1, kInF16>(p, A, st);
+  return launch_in<FMT, 1, kInF32>(p, A, st);
+}
+
+}  // namespace tqproj
