@@ -32,6 +32,7 @@ using tq::Layout;
 #ifndef TQ_GEMV1_PROJ
 #define TQ_GEMV1_PROJ 1
 #endif
+bool tq_internal_proj_fits(int64_t N, int64_t K);
 size_t tq_internal_proj_ws_bytes(int fmt, int64_t N, int64_t K, int nmat);
 int tq_internal_proj_int8(int fmt, int64_t N, int64_t K, const void *W0, const void *W1,
                           const int8_t *q, const float *a_scale, float *y, void *ws,
@@ -787,7 +788,7 @@ int gemv_common(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const 
   if (!aligned16(W0) || (W1 && !aligned16(W1)) || !aligned16(q) || (a && !aligned4(a)) ||
       (out && !aligned4(out)) || (sums && !aligned4(sums)))
     return TQ_ERR_ALIGN;
-  if (TQ_GEMV1_PROJ && !sums && M == 1)
+  if (TQ_GEMV1_PROJ && !sums && M == 1 && tq_internal_proj_fits(N, K))
     return tq_internal_proj_int8(fmt, N, K, W0, nmat == 2 ? W1 : nullptr, q, a, out, ws, ws_bytes,
                                  (hipStream_t)stream);
   const GemvPlan p = gemv_plan(fmt, M, N, K, nmat);
@@ -845,7 +846,7 @@ extern "C" size_t tq_gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t
   if ((fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) || !shape_ok(N, K) || M < 1 || M > TQ_GEMV_MAX_M)
     return 0;
   // covers both tq_gemv and the fused gate/up call (two partial planes)
-  if (TQ_GEMV1_PROJ && M == 1) {
+  if (TQ_GEMV1_PROJ && M == 1 && tq_internal_proj_fits(N, K)) {
     const size_t a = tq_internal_proj_ws_bytes(fmt, N, K, 1), b = tq_internal_proj_ws_bytes(fmt, N, K, 2);
     return a > b ? a : b;
   }

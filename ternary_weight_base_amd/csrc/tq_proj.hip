@@ -15,7 +15,8 @@ namespace {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Split K into C balanced chunks, about `target` workgroups in all but no
+// Split K into C balanced chunks, at most `target` workgroups in all (one
+// round at two workgroups per CU) but no
 // chunk shorter than 8 groups, and give each of the 8 waves
 // gs = ceil(chunk / 8) groups (at most kGsMax1 / kGsMax2, else more chunks).
 Plan plan_proj(int fmt, int64_t N, int64_t K, int nmat) {
@@ -23,7 +24,7 @@ Plan plan_proj(int fmt, int64_t N, int64_t K, int nmat) {
   const int64_t G = L.G, NB = L.NB;
   const int64_t target = nmat == 2 ? TQ_PROJ_TARGET2 : TQ_PROJ_TARGET1;
   const int64_t gsmax = nmat == 2 ? kGsMax2 : kGsMax1;
-  int64_t C = (target + NB / 2) / NB;
+  int64_t C = target / NB;
   if (C > G / kNW) C = G / kNW;  // no chunk shorter than one group per wave
   if (C < 1) C = 1;
   int64_t gs = ((G + C - 1) / C + kNW - 1) / kNW;
@@ -104,6 +105,8 @@ StackWs stack_ws(int fmt, int64_t hidden, int64_t inter, int64_t qkv_out, int64_
 // ---------------------------------------------------------------------
 // One-token GEMV entry points (called by tq_gemv / tq_gemv_gate_up_swiglu)
 // ---------------------------------------------------------------------
+bool tq_internal_proj_fits(int64_t N, int64_t K) { return shape_ok(N, K); }
+
 size_t tq_internal_proj_ws_bytes(int fmt, int64_t N, int64_t K, int nmat) {
   return proj_ws_bytes(fmt, N, K, nmat);
 }

@@ -14,9 +14,10 @@
 // Workgroup (block b, chunk c) owns one 64-row weight block and a balanced
 // chunk of its K groups; each of its 8 waves takes GS consecutive groups of
 // the chunk, one lane per weight row.  Per wave, in program order:
+//   0. fill the B3 digit table (first: it needs nothing);
 //   1. issue the loads of its activation slice (and of what the absmax
-//      needs), then the weight loads of its first D groups;
-//   2. fill the B3 digit table, barrier;
+//      needs); barrier; then the weight loads of its first D groups;
+//   2. fp16 input: absmax pass; barrier;
 //   3. absmax -> quantise its slice in registers (bit-exact with
 //      tq_quant_act; int8 input arrives quantised), move each group's 32
 //      int8 words into SGPRs with v_readlane;
@@ -69,14 +70,18 @@ __device__ __forceinline__ float habs_max8(uint4 u, float m) {
   return m;
 }
 
+// Two workgroups per CU: at most 128 VGPRs.
 template <int FMT, int NMAT, int IN, int GS, int D>
-__global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs A) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void proj_kernel(ProjArgs A) {
   constexpr int WPG = FMT == 0 ? 7 : 9;   // words per (row, group) in registers
   constexpr int NP = (GS + 1) / 2;        // group pairs: one activation word per lane each
   constexpr int D0 = D < GS ? D : GS;
   __shared__ uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
   __shared__ float red[NMAT * kNW * 64];
   __shared__ float wmax[kNW];
+  // The digit table depends on nothing: its LDS stores overlap the kernel
+  // argument loads and the address arithmetic below.
+  if constexpr (FMT == 0) fill_b3_lut(lut);
 
   const Layout L(FMT, A.N, A.K);
   const int G = (int)L.G, N = A.N, K = A.K;
@@ -118,6 +123,12 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs A) {
       xm[i] = reinterpret_cast<const uint4 *>(A.in)[min(tid + kThreads * i, K / 8 - 1)];
   }
 
+  // The CU returns vector loads in issue order, so activation loads issued
+  // behind other waves' weight loads would wait for those weights: every
+  // wave issues its activation loads before any wave of the workgroup
+  // issues weights.
+  __syncthreads();
+
   // ---- 1c. weight loads of the first D groups (dead slots: a live group)
   uint32_t wd[NMAT][GS][WPG];
   auto issue = [&](int i) {
@@ -150,8 +161,7 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs A) {
   for (int i = 0; i < D0; i++) issue(i);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 2. digit table; fp16 input: per-wave maxima of the whole x ----------
-  if constexpr (FMT == 0) fill_b3_lut(lut);
+  // ---- 2. fp16 input: per-wave maxima of the whole x ------------------------
   if constexpr (IN == kInF16) {
     float m = 0.0f;
 #pragma unroll
@@ -211,20 +221,15 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs A) {
 #pragma unroll
   for (int mat = 0; mat < NMAT; mat++) acc[mat] = 0.0f;
   // Empty asm statements (kept in program order) pin the schedule through
-  // data dependences: a group's weights and activation words enter its
-  // iteration through one, so the wait for its loads lands there; each
-  // matrix's table offset enters through one and its accumulator leaves
-  // through another, so one matrix's lookups are in flight at a time; the
-  // loads of issue() take their group index from one.  Without them the
-  // compiler interleaves iterations and holds several groups' lookups at
-  // once.  No memory clobber: the int8 activation words stay scalar loads.
+  // data dependences: a group's activation words enter its iteration
+  // through one; each matrix's weight words enter through one (so the wait
+  // for its loads lands there) and its accumulator leaves through another,
+  // so one matrix's lookups and dots are in flight at a time; the loads of
+  // issue() take their group index from one.  Without them the compiler
+  // interleaves iterations and holds several groups' lookups at once.
 #pragma unroll
   for (int i = 0; i < GS; i++) {
     if (i + D0 < GS) issue(i + D0);
-#pragma unroll
-    for (int mat = 0; mat < NMAT; mat++)
-#pragma unroll
-      for (int k = 0; k < WPG; k++) asm volatile("" : "+v"(wd[mat][i][k]));
     asm volatile("" : "+v"(qv[i >> 1]));
     XRegs<1> xa;
 #pragma unroll
@@ -232,14 +237,14 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs A) {
     const bool live = i < ng;
 #pragma unroll
     for (int mat = 0; mat < NMAT; mat++) {
+#pragma unroll
+      for (int k = 0; k < WPG; k++) asm volatile("" : "+v"(wd[mat][i][k]));  // this matrix starts here
       int S[1] = {0};
       float sc;
       if constexpr (FMT == 0) {
         const uint32_t w[7] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2], wd[mat][i][3],
                                wd[mat][i][4], wd[mat][i][5], wd[mat][i][6]};
-        uint32_t lo = laneoff;
-        asm volatile("" : "+v"(lo));  // this matrix's lookups start here
-        b3_group<1>(lut, lo, w, xa, S);
+        b3_group<1>(lut, laneoff, w, xa, S);
         sc = half_bits(wd[mat][i][6] >> 16);
       } else {
         const uint32_t w[9] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2],
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs A) {
         sc = half_bits(wd[mat][i][8]);
       }
       acc[mat] = fmaf(live ? sc : 0.0f, (float)S[0], acc[mat]);
-      asm volatile("" : "+v"(acc[mat]));  // ... and end here: one matrix at a time
+      asm volatile("" : "+v"(acc[mat]));  // ... and ends here: one matrix at a time
     }
   }
 
