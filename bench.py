@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Decode throughput of the 64-layer 27B-shaped ternary projection stack on one GPU.
 
-One step = one token through all 64 layers.  Per layer: quantise a fresh fp16
-input and run the QKV projection (5120 -> 10240); quantise a fresh fp16 input
-and run O (8192 -> 5120); quantise O's output and run the fused gate/up/SwiGLU
+One step = one token through all 64 layers (tq_decode_stack).  Per layer, in
+order, one launch each: quantise a fresh fp16 input and run the QKV
+projection (5120 -> 10240); quantise a fresh fp16 input and run O
+(8192 -> 5120); quantise O's output and run the fused gate/up/SwiGLU
 (5120 -> 17408, two matrices); quantise h and run down (17408 -> 5120).  All
 weights are distinct per layer (about 5.06 GB of B3-packed trits and fp16
 scales), resident in HBM before timing starts.  Inputs are seeded synthetic
@@ -11,6 +12,11 @@ data with the shapes and distributions of the workload (trits P(0) = 1/2,
 P(+-1) = 1/4; scales uniform in [0.005, 0.05]; activations N(0,1) in fp16).
 
 Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+
+  python bench.py --profile-summary TRACE_DIR FETCH_DIR WRITE_DIR
+turns three rocprofv3 runs of this script (--kernel-trace --stats, then
+--pmc FETCH_SIZE, then --pmc WRITE_SIZE) into the text summary kept under
+profiles/ and the per-launch HBM traffic of the dominant kernel.
 """
 from __future__ import annotations
 
@@ -42,14 +48,19 @@ def parse():
                    help="layers in the stack (the workload is 64; fewer is for quick checks)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    p.add_argument("--profile-summary", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="summarise rocprofv3 output directories of this script and exit")
     return p.parse_args()
 
 
 def kernel_source_sha() -> str:
+    """Hash of every device source: traffic counted on other code is stale."""
     h = hashlib.sha256()
-    for rel in ("ternary_weight_base_amd/csrc/tq_kernels.hip", "ternary_weight_base_amd/csrc/tq_layout.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "ternary_weight_base_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -77,6 +88,9 @@ class Stack:
 
 def main():
     args = parse()
+    if args.profile_summary:
+        profile_summary(*args.profile_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build measures one GPU only; --gpus N with N > 1 is not "
@@ -108,7 +122,7 @@ def main():
     st_bytes = tq.tq_decode_stack_workspace_bytes(fmt, L, HIDDEN, INTER, QKV_OUT, O_IN)
     st_ws = torch.zeros((st_bytes + 15) // 16 * 4, dtype=torch.int32, device=dev)
 
-    # the decode step: tq_decode_stack, 2 launches per layer
+    # the decode step: tq_decode_stack, 4 launches per layer
     def token():
         tq.tq_decode_stack(fmt, L, HIDDEN, INTER, QKV_OUT, O_IN, layers, x_in, a_in,
                            y_qkv, y_o, h, y_dn, st_ws)
@@ -133,10 +147,23 @@ def main():
             tq.tq_quant_act(h1, q17, sc[3:4])
             tq.tq_gemv(fmt, 1, HIDDEN, INTER, stack.W["down"][l], q17, sc[3:4], yd1, ws)
 
+    # The dominant kernel as the stack launches it: gate/up/SwiGLU on O's fp32
+    # output and block maxima (made here once per layer by the same call).
+    nb_o = HIDDEN // 64
+    bmax_o = torch.empty((L, nb_o), dtype=torch.float32, device=dev)
+    yo_l = torch.empty((L, HIDDEN), dtype=torch.float32, device=dev)
+    hq = torch.empty((L, INTER), dtype=torch.float32, device=dev)
+    q_bytes = max(tq.tq_gemv_quant_workspace_bytes(fmt, HIDDEN, O_IN),
+                  tq.tq_gemv_quant_workspace_bytes(fmt, INTER, HIDDEN, True))
+    q_ws = torch.zeros(max(4, (q_bytes + 15) // 16 * 4), dtype=torch.int32, device=dev)
+    for l in range(L):
+        tq.tq_gemv_quant(fmt, HIDDEN, O_IN, stack.W["o"][l], None, a_in[l], yo_l[l],
+                         y_bmax=bmax_o[l], ws=q_ws)
+
     def gate_up_all():
         for l in range(L):
-            tq.tq_gemv_gate_up_swiglu(fmt, 1, INTER, HIDDEN, stack.W["gate"][l],
-                                      stack.W["up"][l], q5, sc[2:3], h1, ws)
+            tq.tq_gemv_quant(fmt, INTER, HIDDEN, stack.W["gate"][l], stack.W["up"][l], yo_l[l],
+                             hq[l], x_bmax=bmax_o[l], ws=q_ws)
 
     # A plain device copy of known size (64 MiB read + 64 MiB written), untimed:
     # profiles of this command use it to calibrate the FETCH_SIZE / WRITE_SIZE
@@ -192,7 +219,8 @@ def main():
             traffic = tr.get("hbm_bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(gu_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(gu_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                "kernel": "proj_kernel<fmt,2> (fused gate/up/SwiGLU, 2 x 17408x5120)",
+                "kernel": "proj_kernel<fmt,2,fp32 input> (fused quantise + gate/up/SwiGLU, "
+                          "2 x 17408x5120), as launched by the stack",
                 "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3)}
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
@@ -261,6 +289,74 @@ def cpu_baseline(synth, budget_s: float, fmt_name: str):
             "sample": f"{done} of {LAYERS} layers of the same stack (unpack+quant+project+SwiGLU "
                       f"from canonical packed blobs, {fmt_name}), {elapsed:.1f} s; tok/s = "
                       f"layers/s / {LAYERS}"}
+
+
+def _rocpd(d):
+    """(per-kernel durations in ns, per-dispatch counter sums) from the rocprofv3
+    SQLite outputs under directory d."""
+    import glob
+    import sqlite3
+    durs, ctrs = {}, {}
+    dbs = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    for db in dbs:
+        c = sqlite3.connect(db)
+        tables = {r[0] for r in c.execute("select name from sqlite_master")}
+        if "kernels" in tables:
+            for name, dur in c.execute("select name, duration from kernels"):
+                durs.setdefault(name, []).append(dur)
+        if "counters_collection" in tables:
+            for name, cn, disp, v in c.execute(
+                    "select kernel_name, counter_name, dispatch_id, sum(value) from "
+                    "counters_collection group by kernel_name, counter_name, dispatch_id"):
+                ctrs.setdefault((name, cn), []).append(v)
+    return durs, ctrs
+
+
+def profile_summary(trace_dir, fetch_dir, write_dir):
+    """Text summary of a profiled bench run (printed) and the dominant kernel's
+    HBM traffic per launch (written to TRAFFIC_FILE).  The traffic counters are
+    scaled by what they read for the 64 MiB device copy the bench makes: its
+    true bytes are 64 MiB read and 64 MiB written."""
+    durs, _ = _rocpd(trace_dir)
+    _, fetch = _rocpd(fetch_dir)
+    _, write = _rocpd(write_dir)
+    calib = 64 << 20
+    dom = [n for n in durs if "proj_kernel<0, 2, 2," in n]
+    print("kernel                                                        calls   avg_us   total_ms")
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:12]:
+        print(f"{name[:60]:60s} {len(v):7d} {sum(v) / len(v) / 1e3:8.3f} {sum(v) / 1e6:10.3f}")
+
+    def per_dispatch(ctrs, cname, pick):
+        vals = [x for (k, cn), v in ctrs.items() if cn == cname and pick(k) for x in v]
+        return vals
+
+    # the calibration copy: the largest copy dispatch (weight blobs are <= 20 MB)
+    fcal = per_dispatch(fetch, "FETCH_SIZE", lambda k: "opy" in k)
+    wcal = per_dispatch(write, "WRITE_SIZE", lambda k: "opy" in k)
+    if not dom or not fcal or not wcal:
+        raise SystemExit("dominant kernel or calibration copy not found in the profiles")
+    fscale = calib / (max(fcal) * 1024)
+    wscale = calib / (max(wcal) * 1024)
+    f = per_dispatch(fetch, "FETCH_SIZE", lambda k: k in dom)
+    w = per_dispatch(write, "WRITE_SIZE", lambda k: k in dom)
+    fb = sum(f) / len(f) * 1024 * fscale
+    wb = sum(w) / len(w) * 1024 * wscale
+    dur = [x for n in dom for x in durs[n]]
+    print(f"\ndominant kernel: {dom[0]}")
+    print(f"  launches traced {len(dur)}, avg duration {sum(dur) / len(dur) / 1e3:.3f} us")
+    print(f"  FETCH_SIZE per launch {sum(f) / len(f):.0f} KiB raw, x{fscale:.3f} (copy calibration) "
+          f"= {fb / 1e6:.3f} MB")
+    print(f"  WRITE_SIZE per launch {sum(w) / len(w):.0f} KiB raw, x{wscale:.3f} (copy calibration) "
+          f"= {wb / 1e6:.3f} MB")
+    print(f"  calibration copy of 64 MiB: FETCH_SIZE {max(fcal):.0f} KiB, WRITE_SIZE {max(wcal):.0f} KiB")
+    out = {"kernel": dom[0], "fmt": "b3", "kernel_source_sha": kernel_source_sha(),
+           "hbm_bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+           "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(f"\nwrote {os.path.relpath(TRAFFIC_FILE, ROOT)}")
 
 
 if __name__ == "__main__":

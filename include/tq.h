@@ -141,6 +141,29 @@ int tq_gemv_gate_up_swiglu(int fmt, int64_t M, int64_t N, int64_t K, const void 
                            const void *Wu, const int8_t *q, const float *a_scale, float *h,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* ---- device: one-token projection with the quantiser fused in -------- */
+
+/* Workspace bytes tq_gemv_quant needs for this shape (gate_up: Wu given);
+ * same zero-fill rule as tq_gemv_workspace_bytes. */
+size_t tq_gemv_quant_workspace_bytes(int fmt, int64_t N, int64_t K, int gate_up);
+
+/* One token in one launch: y[N] = W . quant(x) (fp32), where quant is
+ * tq_quant_act's per-row absmax int8 quantisation (bit-exact with it) and
+ * the product is tq_gemv's.  With Wu != NULL (same shape and format as W),
+ * y = silu(W . quant(x)) * (Wu . quant(x)) as tq_gemv_gate_up_swiglu.
+ *   x_dtype TQ_F16: x is fp16 [K]; its absmax is taken inside the launch
+ *     (x_bmax may be NULL).
+ *   x_dtype TQ_F32: x is fp32 [K]; x_bmax[x_nb], x_nb = K / 64, must hold
+ *     max |x| over each 64-element block of x -- what y_bmax receives from
+ *     the call that produced x, so projections chain without a separate
+ *     quantiser launch.
+ *   y_bmax (optional, ceil(N/64) floats): receives max |y| over each
+ *     64-row block of y.
+ * x and the workspace 16-byte aligned; y, x_bmax, y_bmax 4-byte aligned. */
+int tq_gemv_quant(int fmt, int64_t N, int64_t K, const void *W, const void *Wu, int x_dtype,
+                  const void *x, const float *x_bmax, int64_t x_nb, float *y, float *y_bmax,
+                  void *ws, size_t ws_bytes, void *stream);
+
 /* ---- device: decode stack --------------------------------------------- */
 
 /* Packed weights of one layer (device pointers, tq_pack layout). */

@@ -31,6 +31,7 @@ _STATUS = {0: "TQ_OK", -1: "TQ_ERR_NULL", -2: "TQ_ERR_SHAPE", -3: "TQ_ERR_ALIGN"
 EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant_act",
            "tq_gemv_workspace_bytes", "tq_gemv", "tq_gemv_gate_up_swiglu",
            "tq_gemm_workspace_bytes", "tq_gemm", "tq_debug_unpack", "tq_debug_group_sums",
+           "tq_gemv_quant_workspace_bytes", "tq_gemv_quant",
            "tq_decode_stack_workspace_bytes", "tq_decode_stack")
 
 
@@ -64,6 +65,8 @@ def _load():
         "tq_gemm": ([I, I64, I64, I64, P, P, P, P, P, SZ, P], I),
         "tq_debug_unpack": ([I, I64, I64, P, P, P], I),
         "tq_debug_group_sums": ([I, I64, I64, I64, P, P, P, I, P], I),
+        "tq_gemv_quant_workspace_bytes": ([I, I64, I64, I], SZ),
+        "tq_gemv_quant": ([I, I64, I64, P, P, I, P, P, I64, P, P, P, SZ, P], I),
         "tq_decode_stack_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "tq_decode_stack": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I),
     }
@@ -179,6 +182,21 @@ def tq_debug_unpack(fmt, N, K, W, trits, stream=None) -> None:
 def tq_debug_group_sums(fmt, M, N, K, W, q, S, use_gemm_path=False, stream=None) -> None:
     _check(lib.tq_debug_group_sums(fmt, M, N, K, _ptr(W), _ptr(q), _ptr(S), int(use_gemm_path),
                                    _stream(stream)), "tq_debug_group_sums")
+
+
+def tq_gemv_quant_workspace_bytes(fmt, N, K, gate_up=False) -> int:
+    return int(lib.tq_gemv_quant_workspace_bytes(fmt, N, K, int(bool(gate_up))))
+
+
+def tq_gemv_quant(fmt, N, K, W, Wu, x, y, x_bmax=None, y_bmax=None, ws=None, stream=None) -> None:
+    """y = W . quant(x) (or SwiGLU of W, Wu) for one token x [K] fp16 / fp32
+    (device); fp32 x needs x_bmax, its K/64 block maxima."""
+    import torch
+    dtype = {torch.float16: TQ_F16, torch.float32: TQ_F32}.get(x.dtype, -1)
+    nb = 0 if x_bmax is None else x_bmax.numel()
+    wp, wb = _ws(ws)
+    _check(lib.tq_gemv_quant(fmt, N, K, _ptr(W), _ptr(Wu), dtype, _ptr(x), _ptr(x_bmax), nb,
+                             _ptr(y), _ptr(y_bmax), wp, wb, _stream(stream)), "tq_gemv_quant")
 
 
 def tq_decode_stack_workspace_bytes(fmt, layers, hidden, inter, qkv_out, o_in) -> int:

@@ -53,16 +53,19 @@ __device__ __forceinline__ uint2 b3_entry(int v) {
 }
 
 // Fill the 32 copies.  With a block size that is a multiple of 256 every
-// thread computes one entry v and stores it into 32 / (blockDim / 256) of the
-// copies; lane l starts at copy l % 32, so the 32 lanes of a store hit 32
-// distinct bank pairs.
+// thread computes one entry v and stores it, two adjacent copies per 16-byte
+// store, into 32 / (blockDim / 256) of the copies; lane l starts at copy
+// pair l % 16, so the 8 lanes of a store pass hit 8 distinct bank groups.
 __device__ __forceinline__ void fill_b3_lut(uint2 *lut) {
   if ((blockDim.x & 255u) == 0) {
+    constexpr int kPairs = kLutCopies / 2;
     const int v = threadIdx.x & 255;
     const uint2 e = b3_entry(v);
-    const int per = kLutCopies / (int)(blockDim.x >> 8);
+    const uint4 e2 = make_uint4(e.x, e.y, e.x, e.y);
+    uint4 *lut4 = reinterpret_cast<uint4 *>(lut);
+    const int per = kPairs / (int)(blockDim.x >> 8);
     const int k0 = (int)(threadIdx.x >> 8) * per;
-    for (int k = k0; k < k0 + per; k++) lut[v * kLutCopies + ((threadIdx.x + k) & (kLutCopies - 1))] = e;
+    for (int k = k0; k < k0 + per; k++) lut4[v * kPairs + ((threadIdx.x + k) & (kPairs - 1))] = e2;
   } else {
     for (int idx = threadIdx.x; idx < kLutEntries * kLutCopies; idx += blockDim.x)
       lut[idx] = b3_entry(idx / kLutCopies);

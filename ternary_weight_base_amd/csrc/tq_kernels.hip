@@ -206,7 +206,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(
   constexpr int kXsumStride = kWavesMax * kGsMax;
   constexpr int kXsumSlots = FMT == 1 ? MT * kXsumStride : 1;
   constexpr int WPG = FMT == 0 ? 7 : 9;  // words per (row, group) held in registers
-  __shared__ uint2 lut[kLutSlots];
+  __shared__ __attribute__((aligned(16))) uint2 lut[kLutSlots];
   __shared__ int xsum_lds[kXsumSlots];
   __shared__ float red[SUMS ? 1 : NMAT * MT * kWavesMax * 64];
   __shared__ int last_flag;
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(
 template <int FMT>
 __global__ __launch_bounds__(64) void unpack_kernel(const uint8_t *__restrict__ W,
                                                     int8_t *__restrict__ t, int N, int K) {
-  __shared__ uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
+  __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
   const Layout L(FMT, N, K);
   const int b = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
   if (FMT == 0) fill_b3_lut(lut);
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
                                                    const float *__restrict__ a_scale,
                                                    float *__restrict__ out,
                                                    int32_t *__restrict__ sums, int M, int N, int K) {
-  __shared__ uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
+  __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
   __shared__ __attribute__((aligned(16))) int8_t Bt[64 * kBtStride];
   __shared__ float bscale[64];
 

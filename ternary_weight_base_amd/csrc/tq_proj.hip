@@ -126,6 +126,35 @@ int tq_internal_proj_int8(int fmt, int64_t N, int64_t K, const void *W0, const v
 }
 
 // ---------------------------------------------------------------------
+// C ABI: fused one-token projection
+// ---------------------------------------------------------------------
+extern "C" size_t tq_gemv_quant_workspace_bytes(int fmt, int64_t N, int64_t K, int gate_up) {
+  if ((fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) || !shape_ok(N, K)) return 0;
+  return proj_ws_bytes(fmt, N, K, gate_up ? 2 : 1);
+}
+
+extern "C" int tq_gemv_quant(int fmt, int64_t N, int64_t K, const void *W, const void *Wu,
+                             int x_dtype, const void *x, const float *x_bmax, int64_t x_nb,
+                             float *y, float *y_bmax, void *ws, size_t ws_bytes, void *stream) {
+  if (!W || !x || !y || (x_dtype == TQ_F32 && !x_bmax)) return TQ_ERR_NULL;
+  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
+  if (x_dtype != TQ_F16 && x_dtype != TQ_F32) return TQ_ERR_DTYPE;
+  if (!shape_ok(N, K) || (x_dtype == TQ_F32 && x_nb != K / 64)) return TQ_ERR_SHAPE;
+  if (!aligned16(W) || (Wu && !aligned16(Wu)) || !aligned16(x) || !aligned4(y) ||
+      (x_bmax && !aligned4(x_bmax)) || (y_bmax && !aligned4(y_bmax)))
+    return TQ_ERR_ALIGN;
+  const int nmat = Wu ? 2 : 1;
+  const Plan p = plan_proj(fmt, N, K, nmat);
+  if (p.counters_bytes + p.partials_bytes > 0) {
+    if (!ws) return TQ_ERR_NULL;
+    if (!aligned16(ws)) return TQ_ERR_ALIGN;
+    if (ws_bytes < p.counters_bytes + p.partials_bytes) return TQ_ERR_SIZE;
+  }
+  return launch_proj(fmt, N, K, W, Wu, x_dtype == TQ_F16 ? kInF16 : kInF32, x, x_bmax, (int)x_nb,
+                     y, y_bmax, (char *)ws, (char *)ws + p.counters_bytes, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------
 // C ABI: decode stack
 // ---------------------------------------------------------------------
 extern "C" size_t tq_decode_stack_workspace_bytes(int fmt, int64_t layers, int64_t hidden,

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   constexpr int WPG = FMT == 0 ? 7 : 9;   // words per (row, group) in registers
   constexpr int NP = (GS + 1) / 2;        // group pairs: one activation word per lane each
   constexpr int D0 = D < GS ? D : GS;
-  __shared__ uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
+  __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
   __shared__ float red[NMAT * kNW * 64];
   __shared__ float wmax[kNW];
   // The digit table depends on nothing: its LDS stores overlap the kernel
@@ -339,8 +339,8 @@ template <int FMT>
 int launch_fmt(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st) {
   if (nmat == 2) {
     if (in_kind == kInInt8) return launch_in<FMT, 2, kInInt8>(p, A, st);
-    if (in_kind == kInF32) return launch_in<FMT, 2, kInF32>(p, A, st);
-    return TQ_ERR_DTYPE;
+    if (in_kind == kInF16) return launch_in<FMT, 2, kInF16>(p, A, st);
+    return launch_in<FMT, 2, kInF32>(p, A, st);
   }
   if (in_kind == kInInt8) return launch_in<FMT, 1, kInInt8>(p, A, st);
   if (in_kind == kInF16) return launch_in<FMT, 1, kInF16>(p, A, st);

@@ -1,0 +1,102 @@
+"""GPU parity of tq_gemv_quant (quantiser fused into the one-token
+projection) against the oracle: quantise the same input with the oracle's
+quantiser (bit-exact by construction), then its GEMV / SwiGLU."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import B3, TB, FMTS, assert_close, dev, say, weights
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.set_threads(8)
+
+
+def _block_max(v):
+    v = np.abs(np.asarray(v, dtype=np.float32).ravel())
+    pad = (-v.size) % 64
+    return np.pad(v, (0, pad)).reshape(-1, 64).max(axis=1)
+
+
+def _run(fmt, N, K, x, gate_up, seed, x_bmax=None):
+    import ternary_weight_base_amd as tq
+    tg, sg = weights(N, K, seed)
+    Wg = dev(tq.tq_pack(fmt, tg, sg))
+    Wu, tu, su = None, None, None
+    if gate_up:
+        tu, su = weights(N, K, seed + 1000)
+        Wu = dev(tq.tq_pack(fmt, tu, su))
+    y = torch.full((N,), float("nan"), device="cuda")
+    yb = torch.full(((N + 63) // 64,), float("nan"), device="cuda")
+    nbytes = tq.tq_gemv_quant_workspace_bytes(fmt, N, K, gate_up)
+    ws = torch.zeros(max(4, (nbytes + 15) // 16 * 4), dtype=torch.int32, device="cuda")
+    xb = None if x_bmax is None else dev(x_bmax)
+    tq.tq_gemv_quant(fmt, N, K, Wg, Wu, dev(x), y, x_bmax=xb, y_bmax=yb, ws=ws)
+    torch.cuda.synchronize()
+    y, yb = y.cpu().numpy(), yb.cpu().numpy()
+    q, s = oracle.quant(np.asarray(x).reshape(1, K))
+    ref = oracle.gemv(tg, sg, q, s)
+    if gate_up:
+        ref = oracle.swiglu(ref, oracle.gemv(tu, su, q, s))
+    return y, yb, ref.ravel()
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
+@pytest.mark.parametrize("gate_up", [False, True])
+@pytest.mark.parametrize("N,K", [(640, 1024), (1152, 640), (4160, 2048), (300, 17408)])
+def test_gemv_quant_f16(fmt, gate_up, N, K):
+    say(f"gemv_quant f16 {FMTS[fmt]} gate_up={gate_up} {N}x{K}")
+    x = synth.normal_f16(synth.seed(61, N, K), K)
+    y, yb, ref = _run(fmt, N, K, x, gate_up, 61)
+    assert_close(y, ref, "y")
+    assert np.array_equal(yb, _block_max(y)), "block maxima of y"
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
+@pytest.mark.parametrize("gate_up", [False, True])
+def test_gemv_quant_f32_with_block_maxima(fmt, gate_up):
+    """fp32 input: the absmax comes from the given block maxima; a chained
+    call (the maxima written by the previous projection) matches the oracle
+    on the same fp32 vector."""
+    say(f"gemv_quant f32 {FMTS[fmt]} gate_up={gate_up}")
+    N, K = 1280, 2560
+    x = synth.normal_f32(synth.seed(62, K), K) * np.float32(3.0)
+    y, _, ref = _run(fmt, N, K, x, gate_up, 62, x_bmax=_block_max(x))
+    assert_close(y, ref, "y")
+
+
+def test_gemv_quant_chained():
+    """Two projections chained through y_bmax: the second consumes the
+    first's fp32 output and maxima, as the decode stack does."""
+    import ternary_weight_base_amd as tq
+    say("gemv_quant chained")
+    N1, K1, N2 = 2048, 1024, 640
+    t1, s1 = weights(N1, K1, 63)
+    t2, s2 = weights(N2, N1, 64)
+    W1, W2 = dev(tq.tq_pack(B3, t1, s1)), dev(tq.tq_pack(B3, t2, s2))
+    x = synth.normal_f16(synth.seed(63), K1)
+    y1 = torch.empty(N1, device="cuda")
+    b1 = torch.empty(N1 // 64, device="cuda")
+    y2 = torch.empty(N2, device="cuda")
+    ws = torch.zeros(1 << 18, dtype=torch.int32, device="cuda")
+    tq.tq_gemv_quant(B3, N1, K1, W1, None, dev(x), y1, y_bmax=b1, ws=ws)
+    tq.tq_gemv_quant(B3, N2, N1, W2, None, y1, y2, x_bmax=b1, ws=ws)
+    torch.cuda.synchronize()
+    y1h = y1.cpu().numpy()
+    q, s = oracle.quant(y1h.reshape(1, N1))  # stage-isolated: the GPU's y1
+    assert_close(y2.cpu().numpy(), oracle.gemv(t2, s2, q, s).ravel(), "chained")
+
+
+def test_gemv_quant_zero_input():
+    say("gemv_quant zero input")
+    N, K = 640, 1024
+    x = np.zeros(K, dtype=np.float16)
+    y, yb, ref = _run(B3, N, K, x, True, 65)
+    assert np.all(y == 0) and np.all(yb == 0)

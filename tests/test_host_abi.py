@@ -262,6 +262,36 @@ def test_decode_stack_validates_on_host():
     assert L.tq_decode_stack(5, 2, 640, 1152, 1280, 1024, c(good), FAKE, FAKE, *outs, FAKE, need, None) == -5
 
 
+def test_gemv_quant_validates_on_host():
+    """Every rejection of tq_gemv_quant happens on the host (no GPU here:
+    the device pointers are never dereferenced)."""
+    L = tq.lib
+    F16, F32 = tq.TQ_F16, tq.TQ_F32
+    N, K = 5120, 8192
+    need = tq.tq_gemv_quant_workspace_bytes(B3, N, K)
+    assert need > 0 and tq.tq_gemv_quant_workspace_bytes(B3, N, K, True) > need
+    assert tq.tq_gemv_quant_workspace_bytes(B3, N, 1000) == 0
+    call = lambda fmt=B3, n=N, k=K, W=FAKE, Wu=None, dt=F16, x=FAKE, xb=None, nb=0, y=FAKE, yb=None, \
+        ws=FAKE, wsb=need: L.tq_gemv_quant(fmt, n, k, W, Wu, dt, x, xb, nb, y, yb, ws, wsb, None)
+    assert call(W=None) == -1
+    assert call(x=None) == -1
+    assert call(y=None) == -1
+    assert call(dt=F32) == -1                       # fp32 input needs its block maxima
+    assert call(fmt=4) == -5
+    assert call(dt=7) == -6
+    assert call(k=1000) == -2
+    assert call(dt=F32, xb=FAKE, nb=K // 64 - 1) == -2  # wrong maxima count
+    assert call(x=MIS) == -3
+    assert call(W=MIS) == -3
+    assert call(Wu=MIS) == -3
+    assert call(y=ODD) == -3
+    assert call(dt=F32, xb=ODD, nb=K // 64) == -3
+    assert call(yb=ODD) == -3
+    assert call(ws=None) == -1
+    assert call(ws=MIS) == -3
+    assert call(wsb=need - 1) == -7
+
+
 def test_workspace_sizes():
     assert tq.tq_gemv_workspace_bytes(B3, 1, 1024, 1024) == 0
     for N, K in ((5120, 8192), (5120, 17408), (10240, 5120)):
