@@ -48,6 +48,8 @@ def parse():
                    help="layers in the stack (the workload is 64; fewer is for quick checks)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline (0 = skip)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the prefill GEMM and small-batch measurements")
     p.add_argument("--profile-summary", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="summarise rocprofv3 output directories of this script and exit")
     return p.parse_args()
@@ -208,7 +210,8 @@ def main():
 
     # ---- dominant kernel: the fused gate/up/SwiGLU projection, timed on its
     # own over the same 64 layers' weights (graph of L launches, HIP events)
-    gu_bytes = 2 * stack.bytes["gate"] + HIDDEN + 4 + INTER * 4
+    # weights + fp32 input and its block maxima + fp32 output
+    gu_bytes = 2 * stack.bytes["gate"] + HIDDEN * 4 + (HIDDEN // 64) * 4 + INTER * 4
     gu_us = time_graph(capture(gate_up_all), 5, 1) * 1000.0 / L
     gu_gbps = gu_bytes / (gu_us * 1e-6) / 1e9
     traffic = None
@@ -222,6 +225,9 @@ def main():
                 "kernel": "proj_kernel<fmt,2,fp32 input> (fused quantise + gate/up/SwiGLU, "
                           "2 x 17408x5120), as launched by the stack",
                 "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3)}
+
+    # ---- the other rows of the hot path, measured on the same weights -------
+    extras = measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time_graph)
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     cpu = cpu_baseline(synth, args.cpu_seconds, args.fmt) if args.cpu_seconds > 0 else None
@@ -248,6 +254,7 @@ def main():
         "separate_launch_tok_s": round(1000.0 / sep_ms, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "other_rows": extras,
     }
     print(json.dumps(out))
 
@@ -289,6 +296,58 @@ def cpu_baseline(synth, budget_s: float, fmt_name: str):
             "sample": f"{done} of {LAYERS} layers of the same stack (unpack+quant+project+SwiGLU "
                       f"from canonical packed blobs, {fmt_name}), {elapsed:.1f} s; tok/s = "
                       f"layers/s / {LAYERS}"}
+
+
+def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time_graph):
+    """Prefill GEMM (M = 512 on the layer-0 gate and down matrices) against the
+    int8 MFMA peak, and small-batch decode (M tokens per step through the
+    whole stack: tq_quant_act + tq_gemv per projection, 8 launches a layer)."""
+    if args.no_extras:
+        return None
+    dev = "cuda"
+    out = {}
+    M = 512
+    for name, (N, K) in (("gate", (INTER, HIDDEN)), ("down", (HIDDEN, INTER))):
+        x = torch.from_numpy(synth.normal_f16(synth.seed(4, N, K), M, K)).to(dev)
+        q = torch.empty((M, K), dtype=torch.int8, device=dev)
+        a = torch.empty(M, dtype=torch.float32, device=dev)
+        tq.tq_quant_act(x, q, a)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        W = stack.W[name][0]
+        ms = time_graph(capture(lambda: tq.tq_gemm(fmt, M, N, K, W, q, a, y)), 20, 3)
+        tops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out[f"prefill_gemm_{name}"] = {"M": M, "N": N, "K": K, "us": round(ms * 1e3, 2),
+                                       "TOP/s": round(tops, 1), "peak_int8_mfma_TOP/s": 5000.0,
+                                       "frac": round(tops / 5000.0, 4)}
+    L = stack.layers
+    for Mb in (2, 4, 8, 16):
+        xs = torch.from_numpy(synth.normal_f16(synth.seed(5, Mb, 1), L, Mb, HIDDEN)).to(dev)
+        as_ = torch.from_numpy(synth.normal_f16(synth.seed(5, Mb, 2), L, Mb, O_IN)).to(dev)
+        qh, qo, qi = (torch.empty((Mb, k), dtype=torch.int8, device=dev) for k in (HIDDEN, O_IN, INTER))
+        sc = torch.empty((4, Mb), dtype=torch.float32, device=dev)
+        yq = torch.empty((Mb, QKV_OUT), device=dev)
+        yo = torch.empty((Mb, HIDDEN), device=dev)
+        hh = torch.empty((Mb, INTER), device=dev)
+        yd = torch.empty((Mb, HIDDEN), device=dev)
+        nb = max(tq.tq_gemv_workspace_bytes(fmt, Mb, n, k) for n, k in Stack.SHAPES.values())
+        ws = torch.zeros(max(4, (nb + 15) // 16 * 4), dtype=torch.int32, device=dev)
+        W = stack.W
+
+        def step():
+            for l in range(L):
+                tq.tq_quant_act(xs[l], qh, sc[0])
+                tq.tq_gemv(fmt, Mb, QKV_OUT, HIDDEN, W["qkv"][l], qh, sc[0], yq, ws)
+                tq.tq_quant_act(as_[l], qo, sc[1])
+                tq.tq_gemv(fmt, Mb, HIDDEN, O_IN, W["o"][l], qo, sc[1], yo, ws)
+                tq.tq_quant_act(yo, qh, sc[2])
+                tq.tq_gemv_gate_up_swiglu(fmt, Mb, INTER, HIDDEN, W["gate"][l], W["up"][l], qh,
+                                          sc[2], hh, ws)
+                tq.tq_quant_act(hh, qi, sc[3])
+                tq.tq_gemv(fmt, Mb, HIDDEN, INTER, W["down"][l], qi, sc[3], yd, ws)
+        ms = time_graph(capture(step), 5, 1)
+        out[f"small_batch_M{Mb}"] = {"tok/s": round(Mb * 1000.0 / ms, 1), "ms_per_step": round(ms, 3),
+                                     "weight_stream_GBps": round(stack.step_weight_bytes / (ms * 1e-3) / 1e9, 1)}
+    return out
 
 
 def _rocpd(d):
