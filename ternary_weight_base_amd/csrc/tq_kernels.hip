@@ -32,6 +32,14 @@ using tq::Layout;
 #ifndef TQ_GEMV1_PROJ
 #define TQ_GEMV1_PROJ 1
 #endif
+// 2..16 tokens run on the int8-MFMA GEMV of tq_gemv_mfma.hip.
+#ifndef TQ_GEMV_MFMA
+#define TQ_GEMV_MFMA 1
+#endif
+size_t tq_internal_mgemv_ws_bytes(int fmt, int64_t N, int64_t K, int nmat);
+int tq_internal_mgemv(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const void *W1,
+                      const int8_t *q, const float *a_scale, float *y, void *ws, size_t ws_bytes,
+                      hipStream_t st);
 bool tq_internal_proj_fits(int64_t N, int64_t K);
 size_t tq_internal_proj_ws_bytes(int fmt, int64_t N, int64_t K, int nmat);
 int tq_internal_proj_int8(int fmt, int64_t N, int64_t K, const void *W0, const void *W1,
@@ -791,6 +799,9 @@ int gemv_common(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const 
   if (TQ_GEMV1_PROJ && !sums && M == 1 && tq_internal_proj_fits(N, K))
     return tq_internal_proj_int8(fmt, N, K, W0, nmat == 2 ? W1 : nullptr, q, a, out, ws, ws_bytes,
                                  (hipStream_t)stream);
+  if (TQ_GEMV_MFMA && !sums && M >= 2)
+    return tq_internal_mgemv(fmt, M, N, K, W0, nmat == 2 ? W1 : nullptr, q, a, out, ws, ws_bytes,
+                             (hipStream_t)stream);
   const GemvPlan p = gemv_plan(fmt, M, N, K, nmat);
   if (!sums && p.ws_bytes > 0) {
     if (!ws) return TQ_ERR_NULL;
@@ -848,6 +859,10 @@ extern "C" size_t tq_gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t
   // covers both tq_gemv and the fused gate/up call (two partial planes)
   if (TQ_GEMV1_PROJ && M == 1 && tq_internal_proj_fits(N, K)) {
     const size_t a = tq_internal_proj_ws_bytes(fmt, N, K, 1), b = tq_internal_proj_ws_bytes(fmt, N, K, 2);
+    return a > b ? a : b;
+  }
+  if (TQ_GEMV_MFMA && M >= 2) {
+    const size_t a = tq_internal_mgemv_ws_bytes(fmt, N, K, 1), b = tq_internal_mgemv_ws_bytes(fmt, N, K, 2);
     return a > b ? a : b;
   }
   return gemv_plan(fmt, M, N, K, 2).ws_bytes;

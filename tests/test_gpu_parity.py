@@ -133,7 +133,7 @@ def _gemv_gpu(fmt, M, N, K, W, q, a):
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 1024, 1024), (1, 65, 384), (3, 100, 640),
                                    (1, 10240, 5120), (1, 5120, 8192), (1, 5120, 17408),
                                    (2, 5120, 17408), (4, 1000, 2048), (8, 257, 1024),
-                                   (16, 300, 5120)])
+                                   (16, 300, 5120), (8, 5120, 17408), (16, 10240, 5120)])
 def test_gemv_vs_oracle(fmt, M, N, K):
     say(f"gemv {FMTS[fmt]} M={M} N={N} K={K}")
     t, s = weights(N, K, 4000 + N + K)
@@ -176,12 +176,17 @@ def test_gemv_deterministic_across_runs():
     y1, _ = _gemv_gpu(B3, 1, N, K, W, q, a)
     y2, _ = _gemv_gpu(B3, 1, N, K, W, q, a)
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    q, a = _quant_gpu(acts_f16(8, K, 4446))  # several tokens: the MFMA path
+    y1, _ = _gemv_gpu(B3, 8, N, K, W, q, a)
+    y2, _ = _gemv_gpu(B3, 8, N, K, W, q, a)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
 # ------------------------------------------------------ fused gate/up -----
 
 @pytest.mark.parametrize("fmt", [B3, TB])
-@pytest.mark.parametrize("M,N,K", [(1, 17408, 5120), (1, 130, 640), (4, 1000, 1024), (16, 200, 2048)])
+@pytest.mark.parametrize("M,N,K", [(1, 17408, 5120), (1, 130, 640), (4, 1000, 1024), (16, 200, 2048),
+                                   (8, 17408, 5120)])
 def test_gate_up_swiglu_vs_oracle(fmt, M, N, K):
     say(f"swiglu {FMTS[fmt]} M={M} N={N} K={K}")
     tq = _tq()
