@@ -498,9 +498,13 @@ __global__ __launch_bounds__(64) void unpack_kernel(const uint8_t *__restrict__ 
 // ---------------------------------------------------------------------
 // Prefill GEMM.  grid (NB, ceil(M/128)), 256 threads (4 waves).
 // Per group: the block's 64 weight rows x 128 trits are decoded to int8 in
-// LDS (canonical k order), each wave multiplies its 32 activation rows by
-// them with 2 x 4 x 2 v_mfma_i32_16x16x64_i8, and rescales the int32 group
-// sums by s[n][g] into fp32 accumulators.
+// LDS (canonical k order; lane = row, wave = quarter of the row's bytes, so
+// every branch is uniform per wave and the k-blocks go out as 16-byte
+// stores), each wave multiplies its 32 activation rows by them with
+// 2 x 4 x 2 v_mfma_i32_16x16x64_i8, and rescales the int32 group sums by
+// s[n][g] into fp32 accumulators.  The next group's weights and activation
+// fragments are loaded into registers while the current group is decoded
+// and multiplied.
 // ---------------------------------------------------------------------
 constexpr int kGemmBM = 128;
 constexpr int kBtStride = 144;  // 128 trits + 16 bytes of padding per row
@@ -511,23 +515,58 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
                                                    const float *__restrict__ a_scale,
                                                    float *__restrict__ out,
                                                    int32_t *__restrict__ sums, int M, int N, int K) {
+  constexpr int WPG = FMT == 0 ? 7 : 9;
   __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
   __shared__ __attribute__((aligned(16))) int8_t Bt[64 * kBtStride];
   __shared__ float bscale[64];
 
   const Layout L(FMT, N, K);
   const int G = (int)L.G;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.x, m0 = blockIdx.y * kGemmBM;
   const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
   if (FMT == 0) fill_b3_lut(lut);
 
-  // decode role: row r of the block, part p
-  const int dr = tid >> 2, dp = tid & 3;
+  // decode role: row dr = lane of the block (padding rows past Wb give zero
+  // trits and scale), part dp = wave
+  const int dr = lane, dp = wave, lr = min(dr, Wb - 1);
+  const bool row_live = dr < Wb;
   const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
+  int8_t *brow = Bt + dr * kBtStride;
 
   // MFMA role
   const int li = lane & 15, slot = lane >> 4;
+  const int8_t *qrow[2];
+  bool qok[2];
+#pragma unroll
+  for (int ms = 0; ms < 2; ms++) {
+    const int row = m0 + 32 * wave + 16 * ms + li;
+    qok[ms] = row < M;
+    qrow[ms] = q + (size_t)min(row, M - 1) * K;
+  }
+
+  auto load_w = [&](int g, uint32_t (&w)[WPG]) {
+    const uint8_t *gb = W + L.group_base(b, g);
+    const uint4 P = *reinterpret_cast<const uint4 *>(gb + lr * 16);
+    w[0] = P.x; w[1] = P.y; w[2] = P.z; w[3] = P.w;
+    if constexpr (FMT == 0) {
+      const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + lr * 12);
+      w[4] = pb[0]; w[5] = pb[1]; w[6] = pb[2];
+    } else {
+      const uint4 Q = *reinterpret_cast<const uint4 *>(gb + Wb * 16 + lr * 16);
+      w[4] = Q.x; w[5] = Q.y; w[6] = Q.z; w[7] = Q.w;
+      w[8] = *reinterpret_cast<const uint16_t *>(gb + Wb * 32 + lr * 2);
+    }
+  };
+  auto load_a = [&](int g, v2l (&af)[2][2]) {
+#pragma unroll
+    for (int ms = 0; ms < 2; ms++)
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++)
+        af[ms][ks] = *reinterpret_cast<const v2l *>(qrow[ms] + (size_t)g * 128 + 64 * ks + 16 * slot);
+  };
+
   v4i acc32[2][4];
   float accf[2][4][4];
 #pragma unroll
@@ -537,73 +576,66 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
 #pragma unroll
       for (int v = 0; v < 4; v++) accf[ms][ns][v] = 0.0f;
 
+  uint32_t wcur[WPG], wnext[WPG];
+  v2l acur[2][2], anext[2][2];
+  load_w(0, wcur);
+  load_a(0, acur);
+
   for (int g = 0; g < G; g++) {
+    const int gn = min(g + 1, G - 1);
     __syncthreads();  // previous group's Bt fully consumed (and the table built)
+    load_w(gn, wnext);
     // ---- decode this group's 64 x 128 trits into Bt ---------------------
-    int8_t *brow = Bt + dr * kBtStride;
-    if (dr < Wb) {
-      const uint8_t *gb = W + L.group_base(b, g);
-      if (FMT == 0) {
-        // dwords p and p + 4 of the row's 7: bytes 4p..4p+3 and 16+4p..
-        uint32_t w[7];
-        const uint4 A = *reinterpret_cast<const uint4 *>(gb + dr * 16);
-        const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + dr * 12);
-        w[0] = A.x; w[1] = A.y; w[2] = A.z; w[3] = A.w;
-        w[4] = pb[0]; w[5] = pb[1]; w[6] = pb[2];
-#define TQ_DEC(J)                                                       \
-  {                                                                     \
-    uint2 e = b3_byte<J>(lut, w, laneoff);                              \
-    *reinterpret_cast<uint32_t *>(brow + 4 * (J)) = e.x;                \
-    brow[100 + (J)] = (int8_t)(e.y & 0xff);                             \
+    if constexpr (FMT == 0) {
+      uint32_t w[7];
+#pragma unroll
+      for (int i = 0; i < 7; i++) w[i] = row_live ? wcur[i] : 0x79797979u;  // 0x79: five zero trits
+      // k-block c (16 trits) = digits 0..3 of bytes 4c..4c+3; digit 4 of byte j is k = 100 + j
+#define TQ_BLK(C)                                                                         \
+  {                                                                                       \
+    const uint2 e0 = b3_byte<4 * (C)>(lut, w, laneoff), e1 = b3_byte<4 * (C) + 1>(lut, w, laneoff); \
+    const uint2 e2 = b3_byte<4 * (C) + 2>(lut, w, laneoff), e3 = b3_byte<4 * (C) + 3>(lut, w, laneoff); \
+    *reinterpret_cast<uint4 *>(brow + 16 * (C)) = make_uint4(e0.x, e1.x, e2.x, e3.x);    \
+    *reinterpret_cast<uint32_t *>(brow + 100 + 4 * (C)) =                                 \
+        e0.y | (e1.y << 8) | (e2.y << 16) | (e3.y << 24);                                 \
   }
-        if (dp == 0) { TQ_DEC(0) TQ_DEC(1) TQ_DEC(2) TQ_DEC(3) TQ_DEC(16) TQ_DEC(17) TQ_DEC(18) }
-        if (dp == 1) { TQ_DEC(4) TQ_DEC(5) TQ_DEC(6) TQ_DEC(7) TQ_DEC(19) TQ_DEC(20) TQ_DEC(21) }
-        if (dp == 2) { TQ_DEC(8) TQ_DEC(9) TQ_DEC(10) TQ_DEC(11) TQ_DEC(22) TQ_DEC(23) }
-        if (dp == 3) {
-          TQ_DEC(12) TQ_DEC(13) TQ_DEC(14) TQ_DEC(15) TQ_DEC(24)
-          uint2 e = b3_byte<25>(lut, w, laneoff);
-          brow[125] = (int8_t)((e.x >> 8) & 0xff);
-          brow[126] = (int8_t)((e.x >> 16) & 0xff);
-          brow[127] = (int8_t)(e.x >> 24);
-          bscale[dr] = half_bits(w[6] >> 16);
-        }
-#undef TQ_DEC
-      } else {
-        const uint4 A = *reinterpret_cast<const uint4 *>(gb + dr * 16);
-        const uint4 B = *reinterpret_cast<const uint4 *>(gb + Wb * 16 + dr * 16);
-        const uint32_t w[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
-#pragma unroll
-        for (int cc = 0; cc < 2; cc++) {
-          const int c = dp + 4 * cc;
-#pragma unroll
-          for (int s = 0; s < 4; s++) {
-            const uint32_t code = (w[c] >> (2 * s)) & 0x03030303u;
-            *reinterpret_cast<uint32_t *>(brow + 16 * c + 4 * s) = perm_b32(0u, 0x000100FFu, code);
-          }
-        }
-        if (dp == 0) bscale[dr] = half_bits(*reinterpret_cast<const uint16_t *>(gb + Wb * 32 + dr * 2));
+      if (dp == 0) { TQ_BLK(0) TQ_BLK(4) }
+      if (dp == 1) { TQ_BLK(1) TQ_BLK(5) }
+      if (dp == 2) {
+        TQ_BLK(2)
+        // byte 24: k = 96..99 and 124; byte 25: k = 125..127 (digit 0 a pad)
+        const uint2 e24 = b3_byte<24>(lut, w, laneoff), e25 = b3_byte<25>(lut, w, laneoff);
+        *reinterpret_cast<uint32_t *>(brow + 96) = e24.x;
+        *reinterpret_cast<uint32_t *>(brow + 124) = (e25.x & 0xFFFFFF00u) | e24.y;
       }
+      if (dp == 3) {
+        TQ_BLK(3)
+        bscale[dr] = row_live ? half_bits(wcur[6] >> 16) : 0.0f;
+      }
+#undef TQ_BLK
     } else {
-      for (int k = dp * 32; k < dp * 32 + 32; k += 4) *reinterpret_cast<uint32_t *>(brow + k) = 0;
-      if (dp == 0) bscale[dr] = 0.0f;
+      // byte 4m + c, bits 2s hold k = 16m + 4s + c: word 4m + s of the row is
+      // field s of dword m; part dp writes k-blocks dp and dp + 4
+#pragma unroll
+      for (int cc = 0; cc < 2; cc++) {
+        const int m = dp + 4 * cc;
+        const uint32_t wm = row_live ? wcur[m] : 0x55555555u;  // code 1: zero trits
+        uint32_t t[4];
+#pragma unroll
+        for (int s = 0; s < 4; s++) t[s] = perm_b32(0u, 0x000100FFu, (wm >> (2 * s)) & 0x03030303u);
+        *reinterpret_cast<uint4 *>(brow + 16 * m) = make_uint4(t[0], t[1], t[2], t[3]);
+      }
+      if (dp == 0) bscale[dr] = row_live ? half_bits(wcur[8]) : 0.0f;
     }
+    load_a(gn, anext);
     __syncthreads();
 
     // ---- MFMA: wave rows m0 + 32*wave + 16*ms + i, all 64 columns --------
-    v2l af[2][2];
 #pragma unroll
-    for (int ms = 0; ms < 2; ms++) {
-      const int row = m0 + 32 * wave + 16 * ms + li;
+    for (int ms = 0; ms < 2; ms++)
 #pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
-        if (row < M) {
-          const int8_t *p = q + (size_t)row * K + (size_t)g * 128 + 64 * ks + 16 * slot;
-          af[ms][ks] = *reinterpret_cast<const v2l *>(p);
-        } else {
-          af[ms][ks] = v2l{0, 0};
-        }
-      }
-    }
+      for (int ks = 0; ks < 2; ks++)
+        if (!qok[ms]) acur[ms][ks] = v2l{0, 0};
 #pragma unroll
     for (int ms = 0; ms < 2; ms++)
 #pragma unroll
@@ -618,7 +650,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
       for (int ms = 0; ms < 2; ms++)
 #pragma unroll
         for (int ns = 0; ns < 4; ns++)
-          acc32[ms][ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[ms][ks], bf[ns], acc32[ms][ns], 0, 0, 0);
+          acc32[ms][ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(acur[ms][ks], bf[ns], acc32[ms][ns], 0, 0, 0);
     }
     // ---- output element (row 4*slot + v, column li) of each 16x16 tile ---
 #pragma unroll
@@ -639,6 +671,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < WPG; i++) wcur[i] = wnext[i];
+#pragma unroll
+    for (int ms = 0; ms < 2; ms++)
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) acur[ms][ks] = anext[ms][ks];
   }
   if (SUMS) return;
 #pragma unroll
