@@ -13,7 +13,7 @@
 #define TQ_PROJ_D2 2
 #endif
 #ifndef TQ_PROJ_TARGET1
-#define TQ_PROJ_TARGET1 512
+#define TQ_PROJ_TARGET1 256
 #endif
 #ifndef TQ_PROJ_TARGET2
 #define TQ_PROJ_TARGET2 512
@@ -21,14 +21,27 @@
 
 namespace tqproj {
 
-constexpr int kNW = 8;              // waves per workgroup
+#ifndef TQ_PROJ_NW
+#define TQ_PROJ_NW 8
+#endif
+constexpr int kNW = TQ_PROJ_NW;     // waves per workgroup
 constexpr int kThreads = 64 * kNW;
 constexpr int kGsMax1 = 8;          // groups per wave, one weight matrix
 constexpr int kGsMax2 = 5;          // groups per wave, gate + up
+constexpr int kGsSplit = 6;         // groups per wave, gate + up split over 256 workgroups
 constexpr int kBmaxPerLane = 5;     // producer block maxima per lane in one pass
 constexpr int kXmaxLoads = 2;       // fp16 absmax pass: 16-byte loads per thread in one pass
 
 enum InKind { kInInt8 = 0, kInF16 = 1, kInF32 = 2 };
+
+// Work split.  The (row block, group) items of a projection, in
+// block-major order (item b * G + g), are cut into contiguous ranges, one
+// per workgroup.  split == 0: block b is cut into C chunks of balanced group
+// counts (workgroup b * C + c).  split == 1: the items are cut into W equal
+// ranges, which may start and end inside blocks (at most three blocks per
+// range).  A block cut between workgroups ("pieces") is summed by the last
+// of them to finish, in workgroup order.
+constexpr int kMaxParts = 3;  // blocks touched by one workgroup's range
 
 struct ProjArgs {
   const uint8_t *W0, *W1;
@@ -36,14 +49,14 @@ struct ProjArgs {
   const float *in_aux;   // int8: its activation scale; fp32: block maxima [in_nb]
   float *out;            // [N]
   float *out_bmax;       // optional [NB]: max |out| over each 64-row block
-  float *partials;       // [C][nmat][N] when C > 1
-  uint32_t *counters;    // [NB] when C > 1, zero on entry and on exit
-  int N, K, in_nb, C;
+  float *partials;       // cut blocks: [C][nmat][N], or [workgroups][kMaxParts][nmat][64] (split)
+  uint32_t *counters;    // [NB] when a block is cut, zero on entry and on exit
+  int N, K, in_nb;
+  int split, C, W, I;    // split mode, chunks per block, workgroups and items (mode 1)
 };
 
-// Split of one projection: C chunks of K per 64-row block, gs groups per wave.
 struct Plan {
-  int gs, C, NB;
+  int gs, split, C, W, NB, I, grid;
   size_t counters_bytes, partials_bytes;
 };
 

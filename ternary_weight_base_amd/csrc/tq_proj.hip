@@ -15,29 +15,50 @@ namespace {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Split K into C balanced chunks, at most `target` workgroups in all (one
-// round at two workgroups per CU) but no
-// chunk shorter than 8 groups, and give each of the 8 waves
-// gs = ceil(chunk / 8) groups (at most kGsMax1 / kGsMax2, else more chunks).
+// Work split.  One weight matrix: C balanced K chunks per block, at most
+// `target` workgroups (256: one workgroup per CU measured fastest, with less
+// split-K and one table fill per CU), no chunk shorter than 8 groups, at
+// most kGsMax1 groups per wave.  Gate/up with 256 < NB <= 512 blocks: the
+// items are cut into 256 equal ranges (split 1), because whole blocks would
+// leave NB - 256 CUs with two workgroups and the rest with one; otherwise
+// as one matrix, with up to 512 workgroups and kGsMax2 groups per wave
+// (also when a split range would exceed kGsSplit groups per wave).
 Plan plan_proj(int fmt, int64_t N, int64_t K, int nmat) {
   const Layout L(fmt, N, K);
-  const int64_t G = L.G, NB = L.NB;
-  const int64_t target = nmat == 2 ? TQ_PROJ_TARGET2 : TQ_PROJ_TARGET1;
-  const int64_t gsmax = nmat == 2 ? kGsMax2 : kGsMax1;
-  int64_t C = target / NB;
-  if (C > G / kNW) C = G / kNW;  // no chunk shorter than one group per wave
-  if (C < 1) C = 1;
-  int64_t gs = ((G + C - 1) / C + kNW - 1) / kNW;
-  if (gs > gsmax) {
-    C = (G + kNW * gsmax - 1) / (kNW * gsmax);
-    gs = ((G + C - 1) / C + kNW - 1) / kNW;
-  }
+  const int64_t G = L.G, NB = L.NB, I = NB * G;
   Plan p;
-  p.gs = (int)gs;
-  p.C = (int)C;
   p.NB = (int)NB;
-  p.counters_bytes = C > 1 ? round256((size_t)NB * 4) : 0;
-  p.partials_bytes = C > 1 ? round256((size_t)C * nmat * N * 4) : 0;
+  p.I = (int)I;
+  const int64_t tsplit = (I + 255) / 256;  // items per workgroup, <= 2 G: three blocks at most
+  if (nmat == 2 && NB > 256 && NB <= 512 && tsplit <= kNW * kGsSplit) {
+    const int64_t W = 256, tmax = tsplit;
+    p.split = 1;
+    p.C = 1;
+    p.W = (int)W;
+    p.grid = (int)W;
+    p.gs = (int)((tmax + kNW - 1) / kNW);
+  } else {
+    const int64_t target = nmat == 2 ? TQ_PROJ_TARGET2 : TQ_PROJ_TARGET1;
+    const int64_t gsmax = nmat == 2 ? kGsMax2 : kGsMax1;
+    int64_t C = target / NB;
+    if (C > G / kNW) C = G / kNW;  // no chunk shorter than one group per wave
+    if (C < 1) C = 1;
+    int64_t gs = ((G + C - 1) / C + kNW - 1) / kNW;
+    if (gs > gsmax) {
+      C = (G + kNW * gsmax - 1) / (kNW * gsmax);
+      gs = ((G + C - 1) / C + kNW - 1) / kNW;
+    }
+    p.split = 0;
+    p.C = (int)C;
+    p.W = (int)(NB * C);
+    p.grid = (int)(NB * C);
+    p.gs = (int)gs;
+  }
+  const bool cut = p.split == 1 || p.C > 1;
+  p.counters_bytes = cut ? round256((size_t)NB * 4) : 0;
+  p.partials_bytes = !cut ? 0
+                     : p.split ? round256((size_t)p.grid * kMaxParts * nmat * 64 * 4)
+                               : round256((size_t)p.C * nmat * N * 4);
   return p;
 }
 
@@ -56,12 +77,16 @@ int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, i
   A.in_aux = in_aux;
   A.out = out;
   A.out_bmax = out_bmax;
-  A.counters = p.C > 1 ? reinterpret_cast<uint32_t *>(counters) : nullptr;
-  A.partials = p.C > 1 ? reinterpret_cast<float *>(partials) : nullptr;
+  const bool cut = p.split == 1 || p.C > 1;
+  A.counters = cut ? reinterpret_cast<uint32_t *>(counters) : nullptr;
+  A.partials = cut ? reinterpret_cast<float *>(partials) : nullptr;
   A.N = (int)N;
   A.K = (int)K;
   A.in_nb = in_nb;
+  A.split = p.split;
   A.C = p.C;
+  A.W = p.W;
+  A.I = p.I;
   return fmt == TQ_FMT_B3 ? launch_b3(p, A, nmat, in_kind, st) : launch_2b(p, A, nmat, in_kind, st);
 }
 

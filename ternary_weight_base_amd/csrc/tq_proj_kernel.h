@@ -11,9 +11,12 @@
 // the activation quantiser as its own launch and measures it at about 1.1 us;
 // here it is folded into the projection that consumes it.
 //
-// Workgroup (block b, chunk c) owns one 64-row weight block and a balanced
-// chunk of its K groups; each of its 8 waves takes GS consecutive groups of
-// the chunk, one lane per weight row.  Per wave, in program order:
+// A work item is one (64-row weight block, K group of 128) pair, items in
+// block-major order.  Each workgroup owns a contiguous range of items: a
+// balanced K chunk of one block, or (gate/up over 256 workgroups) an equal
+// share of all items that may span up to three blocks.  Its 8 waves split
+// the range evenly, at most GS consecutive items each, one lane per weight
+// row.  Per wave, in program order:
 //   0. fill the B3 digit table (first: it needs nothing);
 //   1. issue the loads of its activation slice (and of what the absmax
 //      needs); barrier; then the weight loads of its first D groups;
@@ -70,14 +73,39 @@ __device__ __forceinline__ float habs_max8(uint4 u, float m) {
   return m;
 }
 
+// First item of workgroup w (w may be the workgroup count: then the end).
+// Unsigned 32-bit arithmetic: K chunks have C <= 512 and G <= 8192, and
+// split ranges need I <= 256 * kNW * kGsSplit, so no product reaches 2^32.
+__device__ __forceinline__ int wg_first(int w, const ProjArgs &A, int G) {
+  const uint32_t uw = (uint32_t)w, uC = (uint32_t)A.C, uG = (uint32_t)G;
+  if (A.split == 0) {
+    const uint32_t b = uw / uC, c = uw - b * uC;
+    return (int)(b * uG + c * uG / uC);
+  }
+  return (int)(uw * (uint32_t)A.I / (uint32_t)A.W);
+}
+
+// Workgroup whose range holds item j (the inverse of wg_first).
+__device__ __forceinline__ int item_wg(int j, const ProjArgs &A, int G) {
+  const uint32_t uj = (uint32_t)j, uC = (uint32_t)A.C, uG = (uint32_t)G;
+  if (A.split == 0) {
+    const uint32_t b = uj / uG, g = uj - b * uG;
+    return (int)(b * uC + ((g + 1) * uC - 1) / uG);
+  }
+  return (int)(((uj + 1) * (uint32_t)A.W - 1) / (uint32_t)A.I);
+}
+
 // Two workgroups per CU: at most 128 VGPRs.
-template <int FMT, int NMAT, int IN, int GS, int D>
+// SPLIT: the equal item split (ranges may cross blocks); otherwise K chunks
+// of one block.
+template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void proj_kernel(ProjArgs A) {
   constexpr int WPG = FMT == 0 ? 7 : 9;   // words per (row, group) in registers
   constexpr int NP = (GS + 1) / 2;        // group pairs: one activation word per lane each
   constexpr int D0 = D < GS ? D : GS;
+  constexpr int NPART = SPLIT ? kMaxParts : 1;  // blocks a range can touch
   __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
-  __shared__ float red[NMAT * kNW * 64];
+  __shared__ float red[NPART * NMAT * kNW * 64];
   __shared__ float wmax[kNW];
   // The digit table depends on nothing: its LDS stores overlap the kernel
   // argument loads and the address arithmetic below.
@@ -87,13 +115,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int G = (int)L.G, N = A.N, K = A.K;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.x / A.C, c = blockIdx.x - b * A.C;
-  const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
-  const int gbeg = (int)((int64_t)c * G / A.C), gend = (int)((int64_t)(c + 1) * G / A.C);
-  const int g0 = gbeg + wave * GS;               // first group of this wave
-  const int ng = max(0, min(gend - g0, GS));     // live groups of this wave
-  const int glast = gend - 1;                    // dead slots reload this group
-  const int lr = min(lane, Wb - 1);
+  const int wg = blockIdx.x;
+  // Slot j of this wave -> (block sb[j], group sg[j]); slots past the
+  // wave's ns live items reload the range's last item.
+  int bw0, ilast_b, ns, gb, jmax, sb[GS], sg[GS];
+  if constexpr (SPLIT) {
+    const int i0 = wg_first(wg, A, G), i1 = wg_first(wg + 1, A, G);
+    const int ilast = i1 - 1;
+    const int T = i1 - i0;                       // items of the range, <= kNW * GS
+    const int s0 = i0 + (int)((uint32_t)(wave * T) / kNW);  // the waves split the range evenly
+    ns = i0 + (int)((uint32_t)((wave + 1) * T) / kNW) - s0;
+    bw0 = (int)((uint32_t)i0 / (uint32_t)G);     // first block of the range
+    ilast_b = (int)((uint32_t)ilast / (uint32_t)G);
+    // GS <= G, so a wave's slots cross at most one block boundary
+    const int base = min(s0, ilast);
+    const int bb = (int)((uint32_t)base / (uint32_t)G);
+    gb = base - bb * G;
+    jmax = ilast - base;
+#pragma unroll
+    for (int j = 0; j < GS; j++) {
+      const int g = gb + min(j, jmax);
+      sb[j] = g >= G ? bb + 1 : bb;
+      sg[j] = g >= G ? g - G : g;
+    }
+  } else {
+    const int b = wg / A.C, c = wg - b * A.C;
+    const int gbeg = (int)((uint32_t)(c * G) / (uint32_t)A.C);
+    const int gend = (int)((uint32_t)((c + 1) * G) / (uint32_t)A.C);
+    gb = gbeg + wave * GS;                       // first group of this wave
+    ns = max(0, min(gend - gb, GS));
+    jmax = gend - 1 - gb;                        // may be negative: an idle wave
+    bw0 = ilast_b = b;
+#pragma unroll
+    for (int j = 0; j < GS; j++) {
+      sb[j] = b;
+      sg[j] = min(gb + j, gend - 1);
+    }
+  }
   const uint8_t *Wm[2] = {A.W0, A.W1};
 
   // ---- 1a. activation slice: lane l holds word l % 32 of group 2p + l / 32
@@ -104,7 +162,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   uint32_t qv[NP];
 #pragma unroll
   for (int p = 0; p < NP; p++) {
-    const int gp = min(g0 + 2 * p + hsel, glast);
+    // this lane's slot, as arithmetic (an indexed sg[] would be moved to LDS)
+    const int jl = min(2 * p + hsel, GS - 1);
+    const int gl = gb + min(jl, jmax);
+    const int gp = SPLIT && gl >= G ? gl - G : gl;
     const size_t off = (size_t)gp * tq::kGroup + 4 * (size_t)word;
     if constexpr (IN == kInF32) xf[p] = *reinterpret_cast<const float4 *>((const float *)A.in + off);
     else if constexpr (IN == kInF16) xh[p] = *reinterpret_cast<const uint2 *>((const uint16_t *)A.in + off);
@@ -132,28 +193,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // ---- 1c. weight loads of the first D groups (dead slots: a live group)
   uint32_t wd[NMAT][GS][WPG];
   auto issue = [&](int i) {
-    int gi = min(g0 + i, glast);
+    int bi = sb[i], gi = sg[i];
     asm volatile("" : "+v"(gi));  // keeps the loads at this point of the program
+    if constexpr (SPLIT) asm volatile("" : "+v"(bi));
+    const int Wb = (int)L.block_rows(bi), lr = min(lane, Wb - 1);
 #pragma unroll
     for (int mat = 0; mat < NMAT; mat++) {
-      const uint8_t *gb = Wm[mat] + L.group_base(b, gi);
-      const uint4 P = *reinterpret_cast<const uint4 *>(gb + lr * 16);
+      const uint8_t *gp = Wm[mat] + L.group_base(bi, gi);
+      const uint4 P = *reinterpret_cast<const uint4 *>(gp + lr * 16);
       wd[mat][i][0] = P.x;
       wd[mat][i][1] = P.y;
       wd[mat][i][2] = P.z;
       wd[mat][i][3] = P.w;
       if constexpr (FMT == 0) {
-        const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + lr * 12);
+        const uint32_t *pb = reinterpret_cast<const uint32_t *>(gp + Wb * 16 + lr * 12);
         wd[mat][i][4] = pb[0];
         wd[mat][i][5] = pb[1];
         wd[mat][i][6] = pb[2];
       } else {
-        const uint4 Q = *reinterpret_cast<const uint4 *>(gb + Wb * 16 + lr * 16);
+        const uint4 Q = *reinterpret_cast<const uint4 *>(gp + Wb * 16 + lr * 16);
         wd[mat][i][4] = Q.x;
         wd[mat][i][5] = Q.y;
         wd[mat][i][6] = Q.z;
         wd[mat][i][7] = Q.w;
-        wd[mat][i][8] = *reinterpret_cast<const uint16_t *>(gb + Wb * 32 + lr * 2);
+        wd[mat][i][8] = *reinterpret_cast<const uint16_t *>(gp + Wb * 32 + lr * 2);
       }
     }
   };
@@ -217,9 +280,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 
   // ---- 4. pipelined decode + integer dot + scale ---------------------------
   const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
-  float acc[NMAT];
+  float acc[NPART][NMAT];  // [block of the range][matrix]
 #pragma unroll
-  for (int mat = 0; mat < NMAT; mat++) acc[mat] = 0.0f;
+  for (int p = 0; p < NPART; p++)
+#pragma unroll
+    for (int mat = 0; mat < NMAT; mat++) acc[p][mat] = 0.0f;
   // Empty asm statements (kept in program order) pin the schedule through
   // data dependences: a group's activation words enter its iteration
   // through one; each matrix's weight words enter through one (so the wait
@@ -234,7 +299,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     XRegs<1> xa;
 #pragma unroll
     for (int k = 0; k < 32; k++) xa.v[0][k] = __builtin_amdgcn_readlane(qv[i >> 1], 32 * (i & 1) + k);
-    const bool live = i < ng;
+    const bool live = i < ns;
+    const int part = SPLIT ? sb[i] - bw0 : 0;
 #pragma unroll
     for (int mat = 0; mat < NMAT; mat++) {
 #pragma unroll
@@ -254,32 +320,68 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         tb_group<1>(w, xa, xs, S);
         sc = half_bits(wd[mat][i][8]);
       }
-      acc[mat] = fmaf(live ? sc : 0.0f, (float)S[0], acc[mat]);
-      asm volatile("" : "+v"(acc[mat]));  // ... and ends here: one matrix at a time
+      const float s = live ? sc : 0.0f;
+#pragma unroll
+      for (int p = 0; p < NPART; p++) {
+        acc[p][mat] = fmaf(p == part ? s : 0.0f, (float)S[0], acc[p][mat]);
+        asm volatile("" : "+v"(acc[p][mat]));  // ... and ends here: one matrix at a time
+      }
     }
   }
 
-  // ---- 5. reduce: waves in LDS, chunks through the workspace ---------------
+  // ---- 5. reduce: waves in LDS, cut blocks through the workspace ----------
 #pragma unroll
-  for (int mat = 0; mat < NMAT; mat++) red[(mat * kNW + wave) * 64 + lane] = acc[mat];
+  for (int p = 0; p < NPART; p++)
+#pragma unroll
+    for (int mat = 0; mat < NMAT; mat++)
+      red[((p * NMAT + mat) * kNW + wave) * 64 + lane] = acc[p][mat];
   __syncthreads();
-  if (wave != 0) return;
+  // wave p finishes block bw0 + p of the range (if the range reaches it)
+  const int part = wave, b = bw0 + part;
+  if (part >= NPART || b > ilast_b) return;
   float tot[NMAT];
 #pragma unroll
   for (int mat = 0; mat < NMAT; mat++) {
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kNW; w++) s += red[(mat * kNW + w) * 64 + lane];
+    for (int w = 0; w < kNW; w++) s += red[((part * NMAT + mat) * kNW + w) * 64 + lane];
     tot[mat] = s;
   }
   const size_t n = (size_t)b * tq::kBlockRows + lane;
-  const bool row_ok = lane < rows;
-  if (A.C > 1) {
+  const bool row_ok = lane < (int)L.valid_rows(b);
+  // A block cut over several workgroups: each piece publishes its sums,
+  // the last to arrive (agent-scope counter) adds them in workgroup order.
+  if constexpr (SPLIT) {
+    const int wf = item_wg(b * G, A, G), wl = item_wg(b * G + G - 1, A, G);
+    if (wf != wl) {
+#pragma unroll
+      for (int mat = 0; mat < NMAT; mat++)
+        __hip_atomic_store(&A.partials[(((size_t)wg * kMaxParts + part) * NMAT + mat) * 64 + lane],
+                           tot[mat], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);  // the piece has reached device scope
+      uint32_t prev = 0;
+      if (lane == 0)
+        prev = __hip_atomic_fetch_add(&A.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      prev = __shfl(prev, 0, 64);
+      if (prev != (uint32_t)(wl - wf)) return;  // another piece finishes this block
+#pragma unroll
+      for (int mat = 0; mat < NMAT; mat++) tot[mat] = 0.0f;
+      for (int ww = wf; ww <= wl; ww++) {
+        const int pp = b - (int)((uint32_t)wg_first(ww, A, G) / (uint32_t)G);  // the block's part in ww's range
+#pragma unroll
+        for (int mat = 0; mat < NMAT; mat++)
+          tot[mat] += __hip_atomic_load(&A.partials[(((size_t)ww * kMaxParts + pp) * NMAT + mat) * 64 + lane],
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (lane == 0) __hip_atomic_store(&A.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else if (A.C > 1) {
+    const int c = wg - b * A.C;
     if (row_ok) {
 #pragma unroll
       for (int mat = 0; mat < NMAT; mat++)
-        __hip_atomic_store(&A.partials[((size_t)c * NMAT + mat) * N + n], tot[mat],
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&A.partials[((size_t)c * NMAT + mat) * N + n], tot[mat], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the partial sums have reached device scope
     uint32_t prev = 0;
@@ -315,19 +417,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 template <int FMT, int NMAT, int IN>
 int launch_in(const Plan &p, const ProjArgs &A, hipStream_t st) {
   constexpr int D = NMAT == 2 ? TQ_PROJ_D2 : TQ_PROJ_D1;
-  const dim3 grid((unsigned)(p.NB * p.C)), block(kThreads);
-#define TQ_CASE(G_)                                                                  \
-  case G_:                                                                           \
-    hipLaunchKernelGGL((proj_kernel<FMT, NMAT, IN, G_, D>), grid, block, 0, st, A);  \
+  const dim3 grid((unsigned)p.grid), block(kThreads);
+#define TQ_CASE(G_, S_)                                                                  \
+  case G_:                                                                               \
+    hipLaunchKernelGGL((proj_kernel<FMT, NMAT, IN, G_, D, S_>), grid, block, 0, st, A);  \
     break;
   if constexpr (NMAT == 1) {
     switch (p.gs) {
-      TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5) TQ_CASE(6) TQ_CASE(7) TQ_CASE(8)
+      TQ_CASE(1, false) TQ_CASE(2, false) TQ_CASE(3, false) TQ_CASE(4, false)
+      TQ_CASE(5, false) TQ_CASE(6, false) TQ_CASE(7, false) TQ_CASE(8, false)
+      default: return TQ_ERR_SHAPE;
+    }
+  } else if (p.split) {
+    switch (p.gs) {
+      TQ_CASE(1, true) TQ_CASE(2, true) TQ_CASE(3, true) TQ_CASE(4, true) TQ_CASE(5, true) TQ_CASE(6, true)
       default: return TQ_ERR_SHAPE;
     }
   } else {
     switch (p.gs) {
-      TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5)
+      TQ_CASE(1, false) TQ_CASE(2, false) TQ_CASE(3, false) TQ_CASE(4, false) TQ_CASE(5, false)
       default: return TQ_ERR_SHAPE;
     }
   }

@@ -186,8 +186,11 @@ def test_gemv_deterministic_across_runs():
 
 @pytest.mark.parametrize("fmt", [B3, TB])
 @pytest.mark.parametrize("M,N,K", [(1, 17408, 5120), (1, 130, 640), (4, 1000, 1024), (16, 200, 2048),
-                                   (8, 17408, 5120)])
+                                   (8, 17408, 5120), (1, 20000, 640), (1, 30000, 1024), (1, 16448, 128)])
 def test_gate_up_swiglu_vs_oracle(fmt, M, N, K):
+    """One token with 257..512 row blocks takes the equal item split over
+    256 workgroups, whose ranges cross blocks (ragged 20000 rows, 5 and 8
+    groups per row; 257 blocks of one group)."""
     say(f"swiglu {FMTS[fmt]} M={M} N={N} K={K}")
     tq = _tq()
     tg, sg = weights(N, K, 5000 + N)
