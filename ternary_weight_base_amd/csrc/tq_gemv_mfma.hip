@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __shared__ __attribute__((aligned(16))) float smem[kNW * NMAT * kOut * 64 > 16384 ? kNW * NMAT * kOut * 64 : 16384];
   __shared__ int last_flag;
   uint2 *lut = reinterpret_cast<uint2 *>(smem);
-  if constexpr (FMT == 0) fill_b3_lut(lut);
+  if constexpr (FMT == 0) fill_b3_lut<kThreads>(lut);
 
   const Layout L(FMT, A.N, A.K);
   const int G = (int)L.G, N = A.N, K = A.K, M = A.M;

@@ -457,7 +457,7 @@ __global__ __launch_bounds__(64) void unpack_kernel(const uint8_t *__restrict__ 
   __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
   const Layout L(FMT, N, K);
   const int b = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
-  if (FMT == 0) fill_b3_lut(lut);
+  if (FMT == 0) fill_b3_lut<64>(lut);
   __syncthreads();
   const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
   if (lane >= rows) return;
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.x, m0 = blockIdx.y * kGemmBM;
   const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
-  if (FMT == 0) fill_b3_lut(lut);
+  if (FMT == 0) fill_b3_lut<256>(lut);
 
   // decode role: row dr = lane of the block (padding rows past Wb give zero
   // trits and scale), part dp = wave

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __shared__ float wmax[kNW];
   // The digit table depends on nothing: its LDS stores overlap the kernel
   // argument loads and the address arithmetic below.
-  if constexpr (FMT == 0) fill_b3_lut(lut);
+  if constexpr (FMT == 0) fill_b3_lut<kThreads>(lut);
 
   const Layout L(FMT, A.N, A.K);
   const int G = (int)L.G, N = A.N, K = A.K;
@@ -233,8 +233,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       m = habs_max8(reinterpret_cast<const uint4 *>(A.in)[j], m);
     m = wave_max(m);
     if (lane == 0) wmax[wave] = m;
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- 3. absmax, quantise the slice ----------------------------------------
   float a_scale;
