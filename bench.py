@@ -299,13 +299,66 @@ def cpu_baseline(synth, budget_s: float, fmt_name: str):
 
 
 def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time_graph):
-    """Prefill GEMM (M = 512 on the layer-0 gate and down matrices) against the
-    int8 MFMA peak, and small-batch decode (M tokens per step through the
-    whole stack: tq_quant_act + tq_gemv per projection, 8 launches a layer)."""
+    """The other configurations of the hot path, each on weights resident in HBM:
+    - gemv_1k: one-token tq_gemv at N = K = 1024 (229,376 weight bytes, far
+      below what fills the GPU: launch-latency-bound), per call over a graph
+      of 2048 calls on 2048 distinct weight copies (470 MB, beyond the
+      256 MB last-level cache);
+    - ffn_block: quant(x) -> gate/up/SwiGLU -> quant(h) -> down for one token,
+      as two fused launches (tq_gemv_quant), per block over the stack's 64
+      layers of FFN weights;
+    - prefill GEMM (M = 512 on the layer-0 gate and down matrices) against
+      the int8 MFMA peak;
+    - small-batch decode (M tokens per step through the whole stack:
+      tq_quant_act + tq_gemv per projection, 8 launches a layer)."""
     if args.no_extras:
         return None
     dev = "cuda"
     out = {}
+    # gemv_1k: 2048 copies of one packed 1024 x 1024 matrix
+    n1 = 1024
+    t1 = synth.trits(synth.seed(1, n1, n1), n1, n1)
+    s1 = synth.scales(synth.seed(2, n1, n1), n1, n1)
+    blob1 = torch.from_numpy(tq.tq_pack(fmt, t1, s1)).to(dev)
+    copies = 2048
+    W1 = blob1.repeat(copies).view(copies, -1)
+    x1 = torch.from_numpy(synth.normal_f16(synth.seed(1, 7, 1), 1, n1)).to(dev)
+    q1 = torch.empty((1, n1), dtype=torch.int8, device=dev)
+    a1 = torch.empty(1, dtype=torch.float32, device=dev)
+    tq.tq_quant_act(x1, q1, a1)
+    y1 = torch.empty((1, n1), dtype=torch.float32, device=dev)
+    ws1 = torch.zeros(max(4, (tq.tq_gemv_workspace_bytes(fmt, 1, n1, n1) + 15) // 16 * 4),
+                      dtype=torch.int32, device=dev)
+
+    def gemv_all():
+        for c in range(copies):
+            tq.tq_gemv(fmt, 1, n1, n1, W1[c], q1, a1, y1, ws1)
+    us1 = time_graph(capture(gemv_all), 3, 1) * 1000.0 / copies
+    out["gemv_1k"] = {"N": n1, "K": n1, "us_per_call": round(us1, 3),
+                      "weight_GBps": round(blob1.numel() / (us1 * 1e-6) / 1e9, 1),
+                      "bound": "launch latency"}
+    del W1, blob1
+    # ffn_block over the stack's layers
+    L = stack.layers
+    xf = torch.from_numpy(synth.normal_f16(synth.seed(2, 7, 1), L, HIDDEN)).to(dev)
+    hf = torch.empty((L, INTER), dtype=torch.float32, device=dev)
+    bh = torch.empty((L, INTER // 64), dtype=torch.float32, device=dev)
+    yf = torch.empty((L, HIDDEN), dtype=torch.float32, device=dev)
+    nbf = max(tq.tq_gemv_quant_workspace_bytes(fmt, INTER, HIDDEN, True),
+              tq.tq_gemv_quant_workspace_bytes(fmt, HIDDEN, INTER))
+    wsf = torch.zeros(max(4, (nbf + 15) // 16 * 4), dtype=torch.int32, device=dev)
+
+    def ffn_all():
+        for l in range(L):
+            tq.tq_gemv_quant(fmt, INTER, HIDDEN, stack.W["gate"][l], stack.W["up"][l], xf[l], hf[l],
+                             y_bmax=bh[l], ws=wsf)
+            tq.tq_gemv_quant(fmt, HIDDEN, INTER, stack.W["down"][l], None, hf[l], yf[l],
+                             x_bmax=bh[l], ws=wsf)
+    usf = time_graph(capture(ffn_all), 5, 1) * 1000.0 / L
+    ffn_bytes = 2 * stack.bytes["gate"] + stack.bytes["down"]
+    out["ffn_block"] = {"us": round(usf, 3), "weight_bytes": ffn_bytes,
+                        "weight_GBps": round(ffn_bytes / (usf * 1e-6) / 1e9, 1),
+                        "frac_of_8TBps": round(ffn_bytes / (usf * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
     M = 512
     for name, (N, K) in (("gate", (INTER, HIDDEN)), ("down", (HIDDEN, INTER))):
         x = torch.from_numpy(synth.normal_f16(synth.seed(4, N, K), M, K)).to(dev)
@@ -319,7 +372,6 @@ def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time
         out[f"prefill_gemm_{name}"] = {"M": M, "N": N, "K": K, "us": round(ms * 1e3, 2),
                                        "TOP/s": round(tops, 1), "peak_int8_mfma_TOP/s": 5000.0,
                                        "frac": round(tops / 5000.0, 4)}
-    L = stack.layers
     for Mb in (2, 4, 8, 16):
         xs = torch.from_numpy(synth.normal_f16(synth.seed(5, Mb, 1), L, Mb, HIDDEN)).to(dev)
         as_ = torch.from_numpy(synth.normal_f16(synth.seed(5, Mb, 2), L, Mb, O_IN)).to(dev)
@@ -384,7 +436,7 @@ def profile_summary(trace_dir, fetch_dir, write_dir):
     calib = 64 << 20
     dom = [n for n in durs if "proj_kernel<0, 2, 2," in n]
     print("kernel                                                        calls   avg_us   total_ms")
-    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:12]:
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:20]:
         print(f"{name[:60]:60s} {len(v):7d} {sum(v) / len(v) / 1e3:8.3f} {sum(v) / 1e6:10.3f}")
 
     def per_dispatch(ctrs, cname, pick):

@@ -52,9 +52,9 @@ __device__ __forceinline__ uint2 b3_entry(int v) {
   return make_uint2(lo, hi);
 }
 
-// Fill the 32 copies.  With a block size that is a multiple of 256 every
-// thread computes one entry v and stores it, two adjacent copies per 16-byte
-// store, into 32 / (blockDim / 256) of the copies; lane l starts at copy
+// Fill the 32 copies.  With a block size of 256, 512, 1024, 2048 or 4096
+// every thread computes one entry v and stores it, two adjacent copies per
+// 16-byte store, into 32 / (blockDim / 256) of the copies; lane l starts at copy
 // pair l % 16, so the 8 lanes of a store pass hit 8 distinct bank groups.
 // NT: the block size when the caller knows it at compile time (the stores
 // are then unrolled and need no read of the dispatch size: about 0.3 us
@@ -62,7 +62,7 @@ __device__ __forceinline__ uint2 b3_entry(int v) {
 template <int NT = 0>
 __device__ __forceinline__ void fill_b3_lut(uint2 *lut) {
   const int nt = NT ? NT : (int)blockDim.x;
-  if ((nt & 255) == 0) {
+  if ((nt & 255) == 0 && (kLutCopies / 2) % (nt >> 8) == 0) {
     constexpr int kPairs = kLutCopies / 2;
     const int v = threadIdx.x & 255;
     const uint2 e = b3_entry(v);

@@ -117,7 +117,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x;
   // Slot j of this wave -> (block sb[j], group sg[j]); slots past the
-  // wave's ns live items reload the range's last item.
+  // wave's ns live items reload its last live item (a cache hit: no second
+  // trip to HBM), an idle wave's slots the range's last item.
   int bw0, ilast_b, ns, gb, jmax, sb[GS], sg[GS];
   if constexpr (SPLIT) {
     const int i0 = wg_first(wg, A, G), i1 = wg_first(wg + 1, A, G);
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int base = min(s0, ilast);
     const int bb = (int)((uint32_t)base / (uint32_t)G);
     gb = base - bb * G;
-    jmax = ilast - base;
+    jmax = ns > 0 ? ns - 1 : ilast - base;
 #pragma unroll
     for (int j = 0; j < GS; j++) {
       const int g = gb + min(j, jmax);
@@ -144,12 +145,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int gend = (int)((uint32_t)((c + 1) * G) / (uint32_t)A.C);
     gb = gbeg + wave * GS;                       // first group of this wave
     ns = max(0, min(gend - gb, GS));
-    jmax = gend - 1 - gb;                        // may be negative: an idle wave
+    jmax = ns > 0 ? ns - 1 : gend - 1 - gb;      // negative for an idle wave
     bw0 = ilast_b = b;
 #pragma unroll
     for (int j = 0; j < GS; j++) {
       sb[j] = b;
-      sg[j] = min(gb + j, gend - 1);
+      sg[j] = gb + min(j, jmax);
     }
   }
   const uint8_t *Wm[2] = {A.W0, A.W1};
