@@ -70,6 +70,8 @@ def lib():
         L.orc_swiglu.restype = ctypes.c_int
         L.orc_project_packed.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, P]
         L.orc_project_packed.restype = ctypes.c_int
+        L.orc_hadamard_f32.argtypes = [I64, I64, P, P, P]
+        L.orc_hadamard_f32.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
         L.orc_get_threads.restype = ctypes.c_int
         _lib = L
@@ -198,3 +200,21 @@ def project_packed(fmt: int, blob: np.ndarray, N: int, K: int, q, a) -> np.ndarr
     y = np.empty((M, N), dtype=np.float32)
     _check(lib().orc_project_packed(fmt, M, N, K, _p(b), _p(q), _p(a), _p(y)), "project")
     return y
+
+
+HBLOCK = 64
+
+
+def hadamard(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """Rotate each row of x ([M][K] or [K], fp16 widened exactly, or fp32) by
+    the block Hadamard transform and the sign vector signs [K] (+-1)."""
+    x = np.ascontiguousarray(x)
+    squeeze = x.ndim == 1
+    if squeeze:
+        x = x[None, :]
+    x = np.ascontiguousarray(x.astype(np.float32))
+    s = np.ascontiguousarray(signs, dtype=np.int8)
+    M, K = x.shape
+    y = np.empty((M, K), dtype=np.float32)
+    _check(lib().orc_hadamard_f32(M, K, _p(x), _p(s), _p(y)), "hadamard")
+    return y[0] if squeeze else y

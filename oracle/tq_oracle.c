@@ -307,3 +307,37 @@ int orc_project_packed(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t *
   free(s);
   return rc;
 }
+
+/* ---- online Hadamard rotation of the FFN input -------------------------- */
+
+/* Parity of the set bits of v: the sign exponent of Sylvester's Hadamard
+ * matrix, H[i][j] = (-1)^popcount(i & j). */
+static int bit_parity(int64_t v) {
+  int p = 0;
+  while (v) {
+    p ^= 1;
+    v &= v - 1;
+  }
+  return p;
+}
+
+int orc_hadamard_f32(int64_t M, int64_t K, const float *x, const int8_t *signs, float *y) {
+  if (!x || !signs || !y || M < 1 || K < ORC_HBLOCK || K % ORC_HBLOCK) return ORC_ERR_ARG;
+  for (int64_t k = 0; k < K; k++)
+    if (signs[k] != 1 && signs[k] != -1) return ORC_ERR_VALUE;
+  for (int64_t k = 0; k < M * K; k++)
+    if (!isfinite(x[k])) return ORC_ERR_VALUE;
+  for (int64_t m = 0; m < M; m++)
+    for (int64_t b = 0; b < K / ORC_HBLOCK; b++) {
+      const float *u = x + m * K + b * ORC_HBLOCK;
+      for (int64_t i = 0; i < ORC_HBLOCK; i++) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < ORC_HBLOCK; j++)
+          acc += bit_parity(i & j) ? -(double)u[j] : (double)u[j];
+        double v = acc / 8.0;
+        y[m * K + b * ORC_HBLOCK + i] = (float)(signs[b * ORC_HBLOCK + i] * v);
+      }
+    }
+  return ORC_OK;
+}
+

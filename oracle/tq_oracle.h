@@ -101,6 +101,20 @@ int orc_project_packed(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t *
 void orc_set_threads(int n);
 int orc_get_threads(void);
 
+/* Online Hadamard rotation of each row x[m] (K values, K a multiple of
+ * ORC_HBLOCK), block by block: for the 64 values u of a block,
+ *   y_i = s_i * (1/8) * sum_j (-1)^popcount(i & j) u_j,
+ * i.e. Sylvester's Hadamard matrix H_64 (H H = 64 I) scaled to an orthogonal
+ * map, then the per-element sign vector s (+-1, shared by all rows).  Sum in
+ * double over increasing j, rounded once to fp32.  The pages place a shared
+ * Hadamard transform in front of the fused gate/up/SwiGLU kernel with a sign
+ * multiply merged into the path after it ("Ternary Bonsai 2 27B：8GB 显卡硬塞
+ * 27B 三元模型…", section "后面还有没有优化空间"); the block size 64 and the
+ * sign placement are readings (the pages give neither).  Signs other than
+ * +-1, non-finite input or a bad shape are rejected. */
+#define ORC_HBLOCK 64
+int orc_hadamard_f32(int64_t M, int64_t K, const float *x, const int8_t *signs, float *y);
+
 #ifdef __cplusplus
 }
 #endif

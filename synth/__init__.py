@@ -46,6 +46,7 @@ def lib():
         L.synth_scales.argtypes = [U64, I64, P]
         L.synth_normal_f16.argtypes = [U64, I64, P]
         L.synth_normal_f32.argtypes = [U64, I64, P]
+        L.synth_signs.argtypes = [U64, I64, P]
         _lib = L
     return _lib
 
@@ -82,6 +83,13 @@ def normal_f16(seed_: int, *shape: int) -> np.ndarray:
 def normal_f32(seed_: int, *shape: int) -> np.ndarray:
     out = np.empty(shape, dtype=np.float32)
     lib().synth_normal_f32(seed_, out.size, _p(out))
+    return out
+
+
+def signs(seed_: int, n: int) -> np.ndarray:
+    """[n] int8 random signs, +1 or -1 with probability 1/2 each."""
+    out = np.empty(n, dtype=np.int8)
+    lib().synth_signs(seed_, n, _p(out))
     return out
 
 

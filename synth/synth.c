@@ -122,3 +122,10 @@ void synth_normal_f32(uint64_t seed, int64_t n, float *out) {
     if (2 * p + 1 < n) out[2 * p + 1] = (float)z1;
   }
 }
+
+/* Random signs +-1: the top bit of word i (0 -> +1, 1 -> -1). */
+void synth_signs(uint64_t seed, int64_t n, int8_t *out) {
+#pragma omp parallel for
+  for (int64_t i = 0; i < n; i++) out[i] = (word(seed, (uint64_t)i) >> 63) ? -1 : 1;
+}
+

@@ -387,3 +387,100 @@ def test_swiglu_special_values():
     assert h[1] == np.float32(160.0)
     assert h[2] <= 0.0 and abs(h[2]) < 1e-30
     assert abs(h[3] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-7
+
+
+# ------------------------------------------- Hadamard rotation (FFN input) ----
+# Pinned against Sylvester's matrix built by scipy.linalg.hadamard (a library
+# routine), closed forms for one-hot inputs, orthogonality and the invariance
+# of W x under a joint rotation of W's columns and x.
+
+def _sylvester64():
+    from scipy.linalg import hadamard
+    return hadamard(64).astype(np.float64)
+
+
+def test_hadamard_one_hot_closed_form():
+    """e_j -> s_i (-1)^popcount(i & j) / 8 inside j's block, zero elsewhere."""
+    K = 192
+    s = synth.signs(synth.seed(9, 1), K)
+    for j in (0, 1, 5, 63, 64, 100, 191):
+        x = np.zeros(K, dtype=np.float32)
+        x[j] = 1.0
+        y = oracle.hadamard(x, s)
+        b0 = (j // 64) * 64
+        ref = np.zeros(K, dtype=np.float32)
+        for i in range(64):
+            ref[b0 + i] = s[b0 + i] * (-1.0 if bin(i & (j - b0)).count("1") % 2 else 1.0) / 8.0
+        assert np.array_equal(y, ref), j
+
+
+def test_hadamard_vs_scipy_matrix():
+    """Block-diagonal diag(s) H_64 / 8 as a float64 matrix product, rounded once;
+    N(0,1) inputs keep every double sum exact, so the results are equal."""
+    H = _sylvester64()
+    M, K = 3, 320
+    x = synth.normal_f32(synth.seed(9, 2), M, K)
+    s = synth.signs(synth.seed(9, 3), K)
+    y = oracle.hadamard(x, s)
+    ref = np.empty((M, K), dtype=np.float64)
+    for b in range(K // 64):
+        blk = x[:, 64 * b:64 * b + 64].astype(np.float64)
+        ref[:, 64 * b:64 * b + 64] = (blk @ H.T) / 8.0 * s[64 * b:64 * b + 64]
+    assert np.array_equal(y, ref.astype(np.float32))
+
+
+def test_hadamard_fp16_input_widened_exactly():
+    K = 128
+    xh = synth.normal_f16(synth.seed(9, 4), 2, K)
+    s = synth.signs(synth.seed(9, 5), K)
+    assert np.array_equal(oracle.hadamard(xh, s), oracle.hadamard(xh.astype(np.float32), s))
+
+
+def test_hadamard_orthogonal():
+    """Parseval per block, and the inverse H diag(s) / 8 returns the input."""
+    H = _sylvester64()
+    K = 256
+    x = synth.normal_f32(synth.seed(9, 6), K)
+    s = synth.signs(synth.seed(9, 7), K)
+    y = oracle.hadamard(x, s).astype(np.float64)
+    for b in range(K // 64):
+        xb, yb = x[64 * b:64 * b + 64].astype(np.float64), y[64 * b:64 * b + 64]
+        assert math.isclose((yb ** 2).sum(), (xb ** 2).sum(), rel_tol=1e-6)
+        back = H @ (yb * s[64 * b:64 * b + 64]) / 8.0
+        assert np.allclose(back, xb, rtol=0, atol=1e-6)
+    assert np.allclose(H @ H, 64.0 * np.eye(64))
+
+
+def test_hadamard_joint_rotation_invariance():
+    """W x = (W R^T)(R x) for R = diag(s) H / 8 per block."""
+    H = _sylvester64()
+    K, N = 128, 7
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((N, K))
+    x = synth.normal_f32(synth.seed(9, 8), K)
+    s = synth.signs(synth.seed(9, 9), K)
+    R = np.zeros((K, K))
+    for b in range(K // 64):
+        R[64 * b:64 * b + 64, 64 * b:64 * b + 64] = np.diag(s[64 * b:64 * b + 64].astype(np.float64)) @ H / 8.0
+    y = oracle.hadamard(x, s).astype(np.float64)
+    assert np.allclose((W @ R.T) @ y, W @ x.astype(np.float64), rtol=0, atol=1e-5)
+
+
+def test_hadamard_blocks_independent_and_rejects():
+    K = 192
+    s = synth.signs(synth.seed(9, 10), K)
+    x = synth.normal_f32(synth.seed(9, 11), K)
+    x2 = x.copy()
+    x2[70] += 1.0
+    d = oracle.hadamard(x2, s) != oracle.hadamard(x, s)
+    assert d[64:128].any() and not d[:64].any() and not d[128:].any()
+    with pytest.raises(oracle.OracleError):
+        oracle.hadamard(np.zeros(100, np.float32), np.ones(100, np.int8))
+    bad = s.copy()
+    bad[5] = 0
+    with pytest.raises(oracle.OracleError):
+        oracle.hadamard(x, bad)
+    xn = x.copy()
+    xn[3] = np.inf
+    with pytest.raises(oracle.OracleError):
+        oracle.hadamard(xn, s)
