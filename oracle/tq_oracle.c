@@ -331,10 +331,10 @@ int orc_hadamard_f32(int64_t M, int64_t K, const float *x, const int8_t *signs, 
     for (int64_t b = 0; b < K / ORC_HBLOCK; b++) {
       const float *u = x + m * K + b * ORC_HBLOCK;
       for (int64_t i = 0; i < ORC_HBLOCK; i++) {
-        double acc = 0.0;
+        double sum = 0.0;
         for (int64_t j = 0; j < ORC_HBLOCK; j++)
-          acc += bit_parity(i & j) ? -(double)u[j] : (double)u[j];
-        double v = acc / 8.0;
+          sum += bit_parity(i & j) ? -(double)u[j] : (double)u[j];
+        double v = sum / 8.0;
         y[m * K + b * ORC_HBLOCK + i] = (float)(signs[b * ORC_HBLOCK + i] * v);
       }
     }

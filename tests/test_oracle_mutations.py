@@ -29,7 +29,7 @@ MUTATIONS = [
     ("swiglu_sign", "z / (1.0 + exp(-z));", "z / (1.0 + exp(z));"),
     ("half_exponent_bias", "e - 25);", "e - 24);"),
     ("half_subnormal", "ldexp((double)f, -24);", "ldexp((double)f, -25);"),
-    ("hadamard_norm", "double v = acc / 8.0;", "double v = acc / 64.0;"),
+    ("hadamard_norm", "double v = sum / 8.0;", "double v = sum / 64.0;"),
     ("hadamard_parity_or", "bit_parity(i & j)", "bit_parity(i | j)"),
     ("hadamard_negated", "? -(double)u[j] : (double)u[j];", "? (double)u[j] : -(double)u[j];"),
     ("hadamard_sign_index", "(float)(signs[b * ORC_HBLOCK + i] * v)", "(float)(signs[b * ORC_HBLOCK] * v)"),
