@@ -129,6 +129,14 @@ def main():
         tq.tq_decode_stack(fmt, L, HIDDEN, INTER, QKV_OUT, O_IN, layers, x_in, a_in,
                            y_qkv, y_o, h, y_dn, st_ws)
 
+    # the same token with the FFN input rotated online (block-64 Hadamard and
+    # signs, folded into the O projection's epilogue)
+    ffn_signs = torch.from_numpy(synth.signs(synth.seed(3, 7, 3), L * HIDDEN).reshape(L, HIDDEN)).to(dev)
+
+    def token_rot():
+        tq.tq_decode_stack(fmt, L, HIDDEN, INTER, QKV_OUT, O_IN, layers, x_in, a_in,
+                           y_qkv, y_o, h, y_dn, st_ws, ffn_signs=ffn_signs)
+
     # the same token as 8 separate launches per layer (quantiser, then GEMV)
     q5, q8, q17 = (torch.empty((1, k), dtype=torch.int8, device=dev) for k in (HIDDEN, O_IN, INTER))
     sc = torch.empty(4, dtype=torch.float32, device=dev)
@@ -207,6 +215,7 @@ def main():
     tok_s = 1000.0 / ms_per_step
     stream_gbps = stack.step_weight_bytes / (ms_per_step * 1e-3) / 1e9
     sep_ms = time_graph(capture(token_separate), max(3, args.steps // 4), 1)
+    rot_ms = time_graph(capture(token_rot), max(3, args.steps // 4), 1)
 
     # ---- dominant kernel: the fused gate/up/SwiGLU projection, timed on its
     # own over the same 64 layers' weights (graph of L launches, HIP events)
@@ -252,6 +261,7 @@ def main():
         "weight_stream_GBps": round(stream_gbps, 1),
         "weight_stream_frac_of_8TBps": round(stream_gbps / PEAK_HBM_GBPS, 4),
         "separate_launch_tok_s": round(1000.0 / sep_ms, 2),
+        "ffn_hadamard_tok_s": round(1000.0 / rot_ms, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "other_rows": extras,
@@ -304,6 +314,9 @@ def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time
       below what fills the GPU: launch-latency-bound), per call over a graph
       of 2048 calls on 2048 distinct weight copies (470 MB, beyond the
       256 MB last-level cache);
+    - quant_act_5120 / hadamard_quant_act_5120: the activation quantiser of
+      one 5120-element token, alone and with the block-64 Hadamard rotation
+      (per call over 64 calls; launch-latency-bound);
     - ffn_block: quant(x) -> gate/up/SwiGLU -> quant(h) -> down for one token,
       as two fused launches (tq_gemv_quant), per block over the stack's 64
       layers of FFN weights;
@@ -338,6 +351,17 @@ def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time
                       "weight_GBps": round(blob1.numel() / (us1 * 1e-6) / 1e9, 1),
                       "bound": "launch latency"}
     del W1, blob1
+    # the activation quantiser alone, and with the Hadamard rotation (M = 1, K = 5120)
+    xq = torch.from_numpy(synth.normal_f16(synth.seed(1, 7, 2), 64, HIDDEN)).to(dev)
+    qq = torch.empty((64, HIDDEN), dtype=torch.int8, device=dev)
+    aq = torch.empty(64, dtype=torch.float32, device=dev)
+    sq = torch.from_numpy(synth.signs(synth.seed(1, 7, 3), HIDDEN)).to(dev)
+    us_q = time_graph(capture(lambda: [tq.tq_quant_act(xq[i:i + 1], qq[i:i + 1], aq[i:i + 1])
+                                       for i in range(64)]), 5, 1) * 1000.0 / 64
+    us_h = time_graph(capture(lambda: [tq.tq_hadamard_quant_act(xq[i:i + 1], sq, qq[i:i + 1], aq[i:i + 1])
+                                       for i in range(64)]), 5, 1) * 1000.0 / 64
+    out["quant_act_5120"] = {"us_per_call": round(us_q, 3), "bound": "launch latency"}
+    out["hadamard_quant_act_5120"] = {"us_per_call": round(us_h, 3), "bound": "launch latency"}
     # ffn_block over the stack's layers
     L = stack.layers
     xf = torch.from_numpy(synth.normal_f16(synth.seed(2, 7, 1), L, HIDDEN)).to(dev)

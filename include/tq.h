@@ -119,6 +119,27 @@ int tq_unpack(int fmt, int64_t N, int64_t K, const void *src, size_t src_bytes,
 int tq_quant_act(int dtype, int64_t M, int64_t K, const void *x, int8_t *q, float *a_scale,
                  void *stream);
 
+/* Online Hadamard rotation of the FFN input, then tq_quant_act's
+ * quantisation of the rotated rows.  The pages place a Hadamard transform,
+ * shared by gate and up, in front of the fused gate/up/SwiGLU kernel, with a
+ * sign multiply merged into the path after it ("Ternary Bonsai 2 27B：8GB
+ * 显卡硬塞 27B 三元模型…", section "后面还有没有优化空间").  Block size and
+ * signs are not given there; this library rotates each block of 64
+ * consecutive elements of a row:
+ *   r_i = s_i * (1/8) * sum_{j<64} (-1)^popcount(i & j) x_j
+ * (Sylvester's H_64 scaled to an orthogonal map, then the sign of element i,
+ * the same signs[K] for every row), r rounded once to fp32 from an exact
+ * double sum (always for fp16 x; for fp32 x when the magnitudes within a
+ * block span less than 2^23), then q, a_scale from r exactly as
+ * tq_quant_act (bit-exact with the CPU oracle).
+ *   dtype: TQ_F16 or TQ_F32 (x is [M][K]);
+ *   signs: device int8 [K]; a negative value means -1, any other +1;
+ *   q: int8 [M][K]; a_scale: fp32 [M].
+ * x, signs and q 16-byte aligned, a_scale 4-byte aligned.  K a multiple of
+ * 64 (K <= 2^24), M >= 1.  One workgroup per row.  Errors as tq_quant_act. */
+int tq_hadamard_quant_act(int dtype, int64_t M, int64_t K, const void *x, const int8_t *signs,
+                          int8_t *q, float *a_scale, void *stream);
+
 /* ---- device: decode GEMV (M <= 16 tokens) ----------------------------- */
 
 /* Workspace bytes tq_gemv / tq_gemv_gate_up_swiglu need for this shape
@@ -158,11 +179,16 @@ size_t tq_gemv_quant_workspace_bytes(int fmt, int64_t N, int64_t K, int gate_up)
  *     the call that produced x, so projections chain without a separate
  *     quantiser launch.
  *   y_bmax (optional, ceil(N/64) floats): receives max |y| over each
- *     64-row block of y.
+ *     64-row block of y (of the rotated y when y_signs is given).
+ *   y_signs (optional, device int8 [N]; one matrix only, N a multiple of
+ *     64, else TQ_ERR_SHAPE): y is stored rotated, each 64-row block by the
+ *     transform of tq_hadamard_quant_act (r = diag(s) H_64 y / 8, double
+ *     butterflies, one rounding), so that the projection consuming it reads
+ *     the rotated input, with y_bmax as its block maxima.
  * x and the workspace 16-byte aligned; y, x_bmax, y_bmax 4-byte aligned. */
 int tq_gemv_quant(int fmt, int64_t N, int64_t K, const void *W, const void *Wu, int x_dtype,
                   const void *x, const float *x_bmax, int64_t x_nb, float *y, float *y_bmax,
-                  void *ws, size_t ws_bytes, void *stream);
+                  const int8_t *y_signs, void *ws, size_t ws_bytes, void *stream);
 
 /* ---- device: decode stack --------------------------------------------- */
 
@@ -194,11 +220,15 @@ size_t tq_decode_stack_workspace_bytes(int fmt, int64_t layers, int64_t hidden, 
  * 4*layers kernel launches on `stream` (graph-capturable), one per
  * projection, in the order QKV, O, gate/up, down of layer 0, then layer 1,
  * ...: each starts after the previous one ends, as the projections of a
- * decoder must. */
+ * decoder must.
+ * ffn_signs (optional, device int8 [layers][hidden]): the FFN input is
+ * rotated online before gate/up, as tq_gemv_quant's y_signs: y_o[l] holds
+ * the rotated O output, which gate/up quantise and share. */
 int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t inter, int64_t qkv_out,
                     int64_t o_in, const tq_layer *weights /* host array [layers] */,
                     const void *x_in, const void *a_in, float *y_qkv, float *y_o, float *h,
-                    float *y_out, void *ws, size_t ws_bytes, void *stream);
+                    float *y_out, const int8_t *ffn_signs, void *ws, size_t ws_bytes,
+                    void *stream);
 
 /* ---- device: prefill GEMM --------------------------------------------- */
 

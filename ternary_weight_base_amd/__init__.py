@@ -32,7 +32,7 @@ EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant
            "tq_gemv_workspace_bytes", "tq_gemv", "tq_gemv_gate_up_swiglu",
            "tq_gemm_workspace_bytes", "tq_gemm", "tq_debug_unpack", "tq_debug_group_sums",
            "tq_gemv_quant_workspace_bytes", "tq_gemv_quant",
-           "tq_decode_stack_workspace_bytes", "tq_decode_stack")
+           "tq_decode_stack_workspace_bytes", "tq_decode_stack", "tq_hadamard_quant_act")
 
 
 class TqLayer(ctypes.Structure):
@@ -66,9 +66,10 @@ def _load():
         "tq_debug_unpack": ([I, I64, I64, P, P, P], I),
         "tq_debug_group_sums": ([I, I64, I64, I64, P, P, P, I, P], I),
         "tq_gemv_quant_workspace_bytes": ([I, I64, I64, I], SZ),
-        "tq_gemv_quant": ([I, I64, I64, P, P, I, P, P, I64, P, P, P, SZ, P], I),
+        "tq_gemv_quant": ([I, I64, I64, P, P, I, P, P, I64, P, P, P, P, SZ, P], I),
         "tq_decode_stack_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
-        "tq_decode_stack": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I),
+        "tq_decode_stack": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
+        "tq_hadamard_quant_act": ([I, I64, I64, P, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -144,6 +145,16 @@ def tq_quant_act(x, q, a_scale, stream=None) -> None:
            "tq_quant_act")
 
 
+def tq_hadamard_quant_act(x, signs, q, a_scale, stream=None) -> None:
+    """x [M][K] fp16/fp32 (device), signs int8 [K] -> q int8 [M][K], a_scale
+    fp32 [M] of the block-64 Hadamard-rotated rows."""
+    import torch
+    dtype = {torch.float16: TQ_F16, torch.float32: TQ_F32}.get(x.dtype, -1)
+    M, K = x.shape
+    _check(lib.tq_hadamard_quant_act(dtype, M, K, _ptr(x), _ptr(signs), _ptr(q), _ptr(a_scale),
+                                     _stream(stream)), "tq_hadamard_quant_act")
+
+
 def tq_gemv_workspace_bytes(fmt: int, M: int, N: int, K: int) -> int:
     return int(lib.tq_gemv_workspace_bytes(fmt, M, N, K))
 
@@ -188,15 +199,18 @@ def tq_gemv_quant_workspace_bytes(fmt, N, K, gate_up=False) -> int:
     return int(lib.tq_gemv_quant_workspace_bytes(fmt, N, K, int(bool(gate_up))))
 
 
-def tq_gemv_quant(fmt, N, K, W, Wu, x, y, x_bmax=None, y_bmax=None, ws=None, stream=None) -> None:
+def tq_gemv_quant(fmt, N, K, W, Wu, x, y, x_bmax=None, y_bmax=None, ws=None, stream=None,
+                  y_signs=None) -> None:
     """y = W . quant(x) (or SwiGLU of W, Wu) for one token x [K] fp16 / fp32
-    (device); fp32 x needs x_bmax, its K/64 block maxima."""
+    (device); fp32 x needs x_bmax, its K/64 block maxima.  y_signs (int8 [N])
+    stores y Hadamard-rotated per 64-row block."""
     import torch
     dtype = {torch.float16: TQ_F16, torch.float32: TQ_F32}.get(x.dtype, -1)
     nb = 0 if x_bmax is None else x_bmax.numel()
     wp, wb = _ws(ws)
     _check(lib.tq_gemv_quant(fmt, N, K, _ptr(W), _ptr(Wu), dtype, _ptr(x), _ptr(x_bmax), nb,
-                             _ptr(y), _ptr(y_bmax), wp, wb, _stream(stream)), "tq_gemv_quant")
+                             _ptr(y), _ptr(y_bmax), _ptr(y_signs), wp, wb, _stream(stream)),
+           "tq_gemv_quant")
 
 
 def tq_decode_stack_workspace_bytes(fmt, layers, hidden, inter, qkv_out, o_in) -> int:
@@ -204,15 +218,16 @@ def tq_decode_stack_workspace_bytes(fmt, layers, hidden, inter, qkv_out, o_in) -
 
 
 def tq_decode_stack(fmt, layers, hidden, inter, qkv_out, o_in, weights, x_in, a_in,
-                    y_qkv, y_o, h, y_out, ws, stream=None) -> None:
+                    y_qkv, y_o, h, y_out, ws, stream=None, ffn_signs=None) -> None:
     """weights: list of (qkv, o, gate, up, down) device tensors per layer (or a
-    ctypes array of TqLayer built once with stack_layers())."""
+    ctypes array of TqLayer built once with stack_layers()).  ffn_signs (int8
+    [layers][hidden]) rotates the FFN input online."""
     arr = weights if isinstance(weights, ctypes.Array) else stack_layers(weights)
     wp, wb = _ws(ws)
     _check(lib.tq_decode_stack(fmt, layers, hidden, inter, qkv_out, o_in,
                                ctypes.cast(arr, ctypes.c_void_p), _ptr(x_in), _ptr(a_in),
-                               _ptr(y_qkv), _ptr(y_o), _ptr(h), _ptr(y_out), wp, wb,
-                               _stream(stream)), "tq_decode_stack")
+                               _ptr(y_qkv), _ptr(y_o), _ptr(h), _ptr(y_out), _ptr(ffn_signs),
+                               wp, wb, _stream(stream)), "tq_decode_stack")
 
 
 def stack_layers(weights):

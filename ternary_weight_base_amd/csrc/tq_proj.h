@@ -49,6 +49,8 @@ struct ProjArgs {
   const float *in_aux;   // int8: its activation scale; fp32: block maxima [in_nb]
   float *out;            // [N]
   float *out_bmax;       // optional [NB]: max |out| over each 64-row block
+  const int8_t *out_signs;  // optional [N] (one matrix, N % 64 == 0): out is rotated
+                            // block by block, diag(s) H_64 / 8, before it is stored
   float *partials;       // cut blocks: [C][nmat][N], or [workgroups][kMaxParts][nmat][64] (split)
   uint32_t *counters;    // [NB] when a block is cut, zero on entry and on exit
   int N, K, in_nb;

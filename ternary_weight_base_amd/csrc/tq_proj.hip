@@ -67,7 +67,7 @@ Plan plan_proj(int fmt, int64_t N, int64_t K, int nmat) {
 // across the launches of one stream that share them.
 int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, int in_kind,
                 const void *in, const float *in_aux, int in_nb, float *out, float *out_bmax,
-                char *counters, char *partials, hipStream_t st) {
+                char *counters, char *partials, hipStream_t st, const int8_t *out_signs = nullptr) {
   const int nmat = W1 ? 2 : 1;
   const Plan p = plan_proj(fmt, N, K, nmat);
   ProjArgs A;
@@ -77,6 +77,7 @@ int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, i
   A.in_aux = in_aux;
   A.out = out;
   A.out_bmax = out_bmax;
+  A.out_signs = out_signs;
   const bool cut = p.split == 1 || p.C > 1;
   A.counters = cut ? reinterpret_cast<uint32_t *>(counters) : nullptr;
   A.partials = cut ? reinterpret_cast<float *>(partials) : nullptr;
@@ -160,11 +161,13 @@ extern "C" size_t tq_gemv_quant_workspace_bytes(int fmt, int64_t N, int64_t K, i
 
 extern "C" int tq_gemv_quant(int fmt, int64_t N, int64_t K, const void *W, const void *Wu,
                              int x_dtype, const void *x, const float *x_bmax, int64_t x_nb,
-                             float *y, float *y_bmax, void *ws, size_t ws_bytes, void *stream) {
+                             float *y, float *y_bmax, const int8_t *y_signs, void *ws,
+                             size_t ws_bytes, void *stream) {
   if (!W || !x || !y || (x_dtype == TQ_F32 && !x_bmax)) return TQ_ERR_NULL;
   if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
   if (x_dtype != TQ_F16 && x_dtype != TQ_F32) return TQ_ERR_DTYPE;
   if (!shape_ok(N, K) || (x_dtype == TQ_F32 && x_nb != K / 64)) return TQ_ERR_SHAPE;
+  if (y_signs && (Wu || N % 64 != 0)) return TQ_ERR_SHAPE;
   if (!aligned16(W) || (Wu && !aligned16(Wu)) || !aligned16(x) || !aligned4(y) ||
       (x_bmax && !aligned4(x_bmax)) || (y_bmax && !aligned4(y_bmax)))
     return TQ_ERR_ALIGN;
@@ -176,7 +179,8 @@ extern "C" int tq_gemv_quant(int fmt, int64_t N, int64_t K, const void *W, const
     if (ws_bytes < p.counters_bytes + p.partials_bytes) return TQ_ERR_SIZE;
   }
   return launch_proj(fmt, N, K, W, Wu, x_dtype == TQ_F16 ? kInF16 : kInF32, x, x_bmax, (int)x_nb,
-                     y, y_bmax, (char *)ws, (char *)ws + p.counters_bytes, (hipStream_t)stream);
+                     y, y_bmax, (char *)ws, (char *)ws + p.counters_bytes, (hipStream_t)stream,
+                     y_signs);
 }
 
 // ---------------------------------------------------------------------
@@ -193,7 +197,8 @@ extern "C" size_t tq_decode_stack_workspace_bytes(int fmt, int64_t layers, int64
 extern "C" int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t inter,
                                int64_t qkv_out, int64_t o_in, const tq_layer *weights,
                                const void *x_in, const void *a_in, float *y_qkv, float *y_o,
-                               float *h, float *y_out, void *ws, size_t ws_bytes, void *stream) {
+                               float *h, float *y_out, const int8_t *ffn_signs, void *ws,
+                               size_t ws_bytes, void *stream) {
   if (!weights || !x_in || !a_in || !y_qkv || !y_o || !h || !y_out || !ws) return TQ_ERR_NULL;
   if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
   const size_t need = tq_decode_stack_workspace_bytes(fmt, layers, hidden, inter, qkv_out, o_in);
@@ -224,7 +229,8 @@ extern "C" int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t 
                           0, y_qkv + l * qkv_out, nullptr, base, parts, st)) != TQ_OK)
       return rc;
     if ((rc = launch_proj(fmt, hidden, o_in, Lw.o, nullptr, kInF16, a16 + l * o_in, nullptr, 0, yo,
-                          bmax_o, base, parts, st)) != TQ_OK)
+                          bmax_o, base, parts, st, ffn_signs ? ffn_signs + l * hidden : nullptr)) !=
+        TQ_OK)
       return rc;
     if ((rc = launch_proj(fmt, inter, hidden, Lw.gate, Lw.up, kInF32, yo, bmax_o, nb_o, hl, bmax_h,
                           base, parts, st)) != TQ_OK)

@@ -408,6 +408,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const float yg = a_scale * tot[0], yu = a_scale * tot[NMAT - 1];
     y = yg / (1.0f + expf(-yg)) * yu;
   }
+  if constexpr (NMAT == 1) {
+    if (A.out_signs) {
+      // Online Hadamard rotation of the block before the next projection
+      // consumes it ("Ternary Bonsai 2 27B…", section "后面还有没有优化空间"):
+      // Sylvester's H_64 over the 64 rows (lanes), butterflies in double,
+      // scaled by 1/8, then the row's sign.  Every row is valid (N % 64 == 0).
+      double v = (double)y;
+#pragma unroll
+      for (int h = 1; h < 64; h <<= 1) {
+        const double o = __shfl_xor(v, h, 64);
+        v = (lane & h) ? o - v : v + o;
+      }
+      const float r = (float)(v * 0.125);
+      y = A.out_signs[n] < 0 ? -r : r;
+    }
+  }
   if (row_ok) A.out[n] = y;
   if (A.out_bmax) {
     const float m = wave_max(row_ok ? fabsf(y) : 0.0f);

@@ -253,13 +253,17 @@ def test_decode_stack_validates_on_host():
     mis = (tq.TqLayer * 2)(tq.TqLayer(FAKE, FAKE, FAKE, FAKE, FAKE), tq.TqLayer(FAKE, FAKE, MIS, FAKE, FAKE))
     c = lambda a: ctypes.cast(a, ctypes.c_void_p)
     outs = (FAKE,) * 4
-    assert L.tq_decode_stack(*args, c(good), FAKE, FAKE, *outs, FAKE, need - 1, None) == -7
-    assert L.tq_decode_stack(*args, c(bad), FAKE, FAKE, *outs, FAKE, need, None) == -1
-    assert L.tq_decode_stack(*args, c(mis), FAKE, FAKE, *outs, FAKE, need, None) == -3
-    assert L.tq_decode_stack(*args, c(good), MIS, FAKE, *outs, FAKE, need, None) == -3
-    assert L.tq_decode_stack(*args, c(good), FAKE, FAKE, FAKE, ODD, FAKE, FAKE, FAKE, need, None) == -3
-    assert L.tq_decode_stack(*args, None, FAKE, FAKE, *outs, FAKE, need, None) == -1
-    assert L.tq_decode_stack(5, 2, 640, 1152, 1280, 1024, c(good), FAKE, FAKE, *outs, FAKE, need, None) == -5
+    # (..., y_qkv, y_o, h, y_out, ffn_signs, ws, ws_bytes, stream)
+    assert L.tq_decode_stack(*args, c(good), FAKE, FAKE, *outs, None, FAKE, need - 1, None) == -7
+    assert L.tq_decode_stack(*args, c(bad), FAKE, FAKE, *outs, None, FAKE, need, None) == -1
+    assert L.tq_decode_stack(*args, c(mis), FAKE, FAKE, *outs, None, FAKE, need, None) == -3
+    assert L.tq_decode_stack(*args, c(good), MIS, FAKE, *outs, None, FAKE, need, None) == -3
+    assert L.tq_decode_stack(*args, c(good), FAKE, FAKE, FAKE, ODD, FAKE, FAKE, None, FAKE, need,
+                             None) == -3
+    assert L.tq_decode_stack(*args, None, FAKE, FAKE, *outs, None, FAKE, need, None) == -1
+    assert L.tq_decode_stack(5, 2, 640, 1152, 1280, 1024, c(good), FAKE, FAKE, *outs, None, FAKE,
+                             need, None) == -5
+    assert L.tq_decode_stack(*args, c(good), FAKE, FAKE, *outs, FAKE, FAKE, need - 1, None) == -7
 
 
 def test_gemv_quant_validates_on_host():
@@ -272,7 +276,8 @@ def test_gemv_quant_validates_on_host():
     assert need > 0 and tq.tq_gemv_quant_workspace_bytes(B3, N, K, True) > need
     assert tq.tq_gemv_quant_workspace_bytes(B3, N, 1000) == 0
     call = lambda fmt=B3, n=N, k=K, W=FAKE, Wu=None, dt=F16, x=FAKE, xb=None, nb=0, y=FAKE, yb=None, \
-        ws=FAKE, wsb=need: L.tq_gemv_quant(fmt, n, k, W, Wu, dt, x, xb, nb, y, yb, ws, wsb, None)
+        sg=None, ws=FAKE, wsb=need: L.tq_gemv_quant(fmt, n, k, W, Wu, dt, x, xb, nb, y, yb, sg, ws,
+                                                    wsb, None)
     assert call(W=None) == -1
     assert call(x=None) == -1
     assert call(y=None) == -1
@@ -290,6 +295,28 @@ def test_gemv_quant_validates_on_host():
     assert call(ws=None) == -1
     assert call(ws=MIS) == -3
     assert call(wsb=need - 1) == -7
+    assert call(sg=FAKE, Wu=FAKE) == -2             # the rotation takes one matrix
+    assert call(sg=FAKE, n=N - 64 + 32) == -2        # ... and whole 64-row blocks
+    assert call(sg=FAKE, wsb=need - 1) == -7
+
+
+def test_hadamard_quant_validates_on_host():
+    L = tq.lib
+    F16, F32 = tq.TQ_F16, tq.TQ_F32
+    call = lambda dt=F16, m=2, k=5120, x=FAKE, sg=FAKE, q=FAKE, a=FAKE: \
+        L.tq_hadamard_quant_act(dt, m, k, x, sg, q, a, None)
+    assert call(x=None) == -1
+    assert call(sg=None) == -1
+    assert call(q=None) == -1
+    assert call(a=None) == -1
+    assert call(dt=5) == -6
+    assert call(m=0) == -2
+    assert call(k=32) == -2
+    assert call(k=5120 + 32) == -2
+    assert call(x=MIS) == -3
+    assert call(sg=MIS) == -3
+    assert call(q=MIS) == -3
+    assert call(a=ODD) == -3
 
 
 def test_workspace_sizes():
