@@ -70,6 +70,8 @@ def lib():
         L.orc_swiglu.restype = ctypes.c_int
         L.orc_project_packed.argtypes = [ctypes.c_int, I64, I64, I64, P, P, P, P]
         L.orc_project_packed.restype = ctypes.c_int
+        L.orc_ternarize.argtypes = [I64, I64, P, P, P]
+        L.orc_ternarize.restype = ctypes.c_int
         L.orc_hadamard_f32.argtypes = [I64, I64, P, P, P]
         L.orc_hadamard_f32.restype = ctypes.c_int
         L.orc_set_threads.argtypes = [ctypes.c_int]
@@ -218,3 +220,13 @@ def hadamard(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
     y = np.empty((M, K), dtype=np.float32)
     _check(lib().orc_hadamard_f32(M, K, _p(x), _p(s), _p(y)), "hadamard")
     return y[0] if squeeze else y
+
+
+def ternarize(w: np.ndarray):
+    """fp32 weights [N][K] -> (trits int8 [N][K], fp16 scales as uint16 [N][K/128])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    t = np.empty((N, K), dtype=np.int8)
+    s = np.empty((N, K // GROUP), dtype=np.uint16)
+    _check(lib().orc_ternarize(N, K, _p(w), _p(t), _p(s)), "ternarize")
+    return t, s

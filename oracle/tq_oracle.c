@@ -341,3 +341,75 @@ int orc_hadamard_f32(int64_t M, int64_t K, const float *x, const int8_t *signs, 
   return ORC_OK;
 }
 
+/* ---- ternarisation of fp32 weights (before packing) --------------------- */
+
+/* Nearest binary16 (ties to even) of a finite v >= 0, as a bit pattern.
+ * binary16 normal numbers are (1024 + f) * 2^(E - 10) for E in [-14, 15];
+ * below 2^-14 the spacing is 2^-24.  Returns -1 when v rounds past 65504. */
+static int half_from_double(double v, uint16_t *out) {
+  if (v == 0.0) {
+    *out = 0;
+    return 0;
+  }
+  int e;
+  (void)frexp(v, &e); /* v in [2^(e-1), 2^e) */
+  int E = e - 1;
+  if (E < -14) {
+    double r = rint(ldexp(v, 24)); /* multiple of 2^-24; 1024 becomes the smallest normal */
+    *out = (uint16_t)r;
+    return 0;
+  }
+  double r = rint(ldexp(v, 10 - E)); /* in [1024, 2048] */
+  if (r == 2048.0) {
+    r = 1024.0;
+    E += 1;
+  }
+  if (E > 15) return -1;
+  *out = (uint16_t)(((E + 15) << 10) | ((int)r - 1024));
+  return 0;
+}
+
+int orc_ternarize(int64_t N, int64_t K, const float *w, int8_t *t, uint16_t *s) {
+  if (!w || !t || !s || !shape_ok(N, K)) return ORC_ERR_ARG;
+  for (int64_t i = 0; i < N * K; i++)
+    if (!isfinite(w[i])) return ORC_ERR_VALUE;
+  const int64_t G = K / ORC_GROUP;
+  int rc = ORC_OK;
+  for (int64_t n = 0; n < N && rc == ORC_OK; n++)
+    for (int64_t g = 0; g < G && rc == ORC_OK; g++) {
+      const float *wg = w + n * K + g * ORC_GROUP;
+      int8_t *tg = t + n * K + g * ORC_GROUP;
+      /* rank the magnitudes: descending |w|, ties by the lower index */
+      int order[ORC_GROUP];
+      for (int i = 0; i < ORC_GROUP; i++) order[i] = i;
+      for (int i = 1; i < ORC_GROUP; i++) { /* insertion sort, stable */
+        int cur = order[i], j = i - 1;
+        while (j >= 0 && fabsf(wg[order[j]]) < fabsf(wg[cur])) {
+          order[j + 1] = order[j];
+          j--;
+        }
+        order[j + 1] = cur;
+      }
+      /* the support size k maximising (sum of the k largest |w|)^2 / k */
+      double prefix = 0.0, best = 0.0, best_sum = 0.0;
+      int best_k = 0;
+      for (int k = 1; k <= ORC_GROUP; k++) {
+        prefix += (double)fabsf(wg[order[k - 1]]);
+        double obj = prefix * prefix / (double)k;
+        if (obj > best) {
+          best = obj;
+          best_k = k;
+          best_sum = prefix;
+        }
+      }
+      for (int i = 0; i < ORC_GROUP; i++) tg[i] = 0;
+      for (int r = 0; r < best_k; r++) {
+        int i = order[r];
+        tg[i] = wg[i] > 0.0f ? 1 : (wg[i] < 0.0f ? -1 : 0);
+      }
+      double scale = best_k ? best_sum / (double)best_k : 0.0;
+      if (half_from_double(scale, &s[n * G + g]) != 0) rc = ORC_ERR_VALUE;
+    }
+  return rc;
+}
+

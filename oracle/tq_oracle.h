@@ -115,6 +115,22 @@ int orc_get_threads(void);
 #define ORC_HBLOCK 64
 int orc_hadamard_f32(int64_t M, int64_t K, const float *x, const int8_t *signs, float *y);
 
+/* Ternarise fp32 weights w[N][K] group by group (128 consecutive k of one
+ * row), the weight step of a post-training ternary quantiser ("为什么PTQ1_0
+ * 能让27B模型在4090上活得很好", section 1.2: per group two thresholds, values
+ * between them set to zero, the signs kept on either side, and a per-group
+ * scale chosen to shrink the residual).  Here, with one scale per group:
+ * the support is the k largest |w| (ties: lower index first), t = sign(w)
+ * on it and 0 elsewhere, scale = mean |w| over the support -- the least-
+ * squares scale for that support -- and k (0..128) maximises
+ * (sum of the k largest |w|)^2 / k, which minimises sum (w - scale t)^2
+ * (ties: the smaller k; k = 0 gives an all-zero group, scale 0).  Sums in
+ * double in rank order; the scale rounded once to fp16 (ties to even).
+ * Non-finite weights, or a scale beyond fp16 range, are rejected.  The
+ * calibration-driven error compensation the page adds afterwards needs
+ * activation data and is not part of this step. */
+int orc_ternarize(int64_t N, int64_t K, const float *w, int8_t *t, uint16_t *s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,6 +34,13 @@ MUTATIONS = [
     ("hadamard_negated", "? -(double)u[j] : (double)u[j];", "? (double)u[j] : -(double)u[j];"),
     ("hadamard_sign_index", "(float)(signs[b * ORC_HBLOCK + i] * v)", "(float)(signs[b * ORC_HBLOCK] * v)"),
     ("hadamard_block_offset", "const float *u = x + m * K + b * ORC_HBLOCK;", "const float *u = x + m * K;"),
+    ("tern_objective_mean", "double obj = prefix * prefix / (double)k;", "double obj = prefix / (double)k;"),
+    ("tern_scale_over_group", "double scale = best_k ? best_sum / (double)best_k : 0.0;",
+     "double scale = best_k ? best_sum / 128.0 : 0.0;"),
+    ("tern_sign", "tg[i] = wg[i] > 0.0f ? 1 : (wg[i] < 0.0f ? -1 : 0);",
+     "tg[i] = wg[i] > 0.0f ? -1 : (wg[i] < 0.0f ? 1 : 0);"),
+    ("half_round_truncates", "double r = rint(ldexp(v, 10 - E));", "double r = floor(ldexp(v, 10 - E));"),
+    ("half_subnormal_step", "double r = rint(ldexp(v, 24));", "double r = rint(ldexp(v, 23));"),
 ]
 
 

@@ -484,3 +484,103 @@ def test_hadamard_blocks_independent_and_rejects():
     xn[3] = np.inf
     with pytest.raises(oracle.OracleError):
         oracle.hadamard(xn, s)
+
+
+# ------------------------------------------------------- ternarisation ----
+# Pinned against a float64 brute force over every support size (numpy), the
+# closed forms of constant, single-weight and zero groups, sign and scale
+# invariances, and numpy's float16 rounding.
+
+def _brute_ternarize_group(wg):
+    """Least-squares ternary fit of one group: every support size k of the
+    k largest magnitudes (stable order), residual computed directly."""
+    order = np.argsort(-np.abs(wg.astype(np.float64)), kind="stable")
+    w64 = wg.astype(np.float64)
+    best = (np.sum(w64 ** 2), 0, np.zeros(128, np.int8), 0.0)
+    for k in range(1, 129):
+        sup = order[:k]
+        t = np.zeros(128, np.int8)
+        t[sup] = np.sign(w64[sup]).astype(np.int8)
+        s = np.abs(w64[sup]).sum() / k
+        res = np.sum((w64 - s * t) ** 2)
+        if res < best[0]:
+            best = (res, k, t, s)
+    return best[2], np.float16(best[3]).view(np.uint16)
+
+
+def test_ternarize_vs_bruteforce():
+    N, K = 3, 384
+    w = synth.normal_f32(synth.seed(31, 1), N, K) * np.float32(0.02)
+    t, s = oracle.ternarize(w)
+    for n in range(N):
+        for g in range(K // 128):
+            tr, sr = _brute_ternarize_group(w[n, 128 * g:128 * g + 128])
+            assert np.array_equal(t[n, 128 * g:128 * g + 128], tr), (n, g)
+            assert s[n, g] == sr, (n, g)
+
+
+def test_ternarize_heavy_tails_vs_bruteforce():
+    """A few large weights among small ones: a small support wins."""
+    w = synth.normal_f32(synth.seed(31, 2), 2, 128) * np.float32(0.01)
+    w[0, [3, 50, 99]] = [4.0, -5.0, 4.5]
+    w[1, :] = np.float32(0.001)
+    w[1, 7] = -2.0
+    t, s = oracle.ternarize(w)
+    for n in range(2):
+        tr, sr = _brute_ternarize_group(w[n])
+        assert np.array_equal(t[n], tr) and s[n, 0] == sr
+    assert np.count_nonzero(t[1]) == 1 and t[1, 7] == -1
+    assert s[1, 0] == np.float16(2.0).view(np.uint16)
+
+
+def test_ternarize_closed_forms():
+    c = np.float32(0.03125)
+    w = np.zeros((3, 128), np.float32)
+    w[0] = c * np.where(np.arange(128) % 3 == 0, -1, 1)  # constant magnitude: full support
+    w[1, 17] = -0.75                                      # a single weight
+    t, s = oracle.ternarize(w)                            # row 2: all zero
+    assert np.array_equal(t[0], np.where(np.arange(128) % 3 == 0, -1, 1).astype(np.int8))
+    assert s[0, 0] == np.float16(c).view(np.uint16)
+    assert np.count_nonzero(t[1]) == 1 and t[1, 17] == -1 and s[1, 0] == np.float16(0.75).view(np.uint16)
+    assert not t[2].any() and s[2, 0] == 0
+
+
+def test_ternarize_invariances():
+    w = synth.normal_f32(synth.seed(31, 3), 2, 256) * np.float32(0.05)
+    t, s = oracle.ternarize(w)
+    tn, sn = oracle.ternarize(-w)
+    assert np.array_equal(tn, -t) and np.array_equal(sn, s)
+    t2, s2 = oracle.ternarize(w * np.float32(2.0))
+    assert np.array_equal(t2, t)
+    assert np.array_equal(s2.view(np.float16).astype(np.float64), 2.0 * s.view(np.float16).astype(np.float64))
+    perm = np.random.default_rng(5).permutation(128)
+    tp, sp = oracle.ternarize(np.ascontiguousarray(w[:, perm]))
+    assert np.array_equal(tp, t[:, perm]) and np.array_equal(sp[:, 0], s[:, 0])
+
+
+def test_ternarize_scale_rounding_vs_numpy_float16():
+    """The scale of a one-weight group is |w| rounded to fp16: compared with
+    numpy's float16 conversion on exact midpoints (ties to even), subnormals,
+    values near the top of the range, and random values."""
+    rng = np.random.default_rng(7)
+    h = rng.integers(1, 0x7BFF, 400).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    vals = np.concatenate([(lo + hi) / 2, lo, rng.random(200) * 60000, rng.random(100) * 6e-5,
+                           [65504.0, 65519.0, 2.0 ** -24, 2.0 ** -25 * 1.5, 2.0 ** -14]]).astype(np.float32)
+    w = np.zeros((vals.size, 128), np.float32)
+    w[:, 0] = vals
+    t, s = oracle.ternarize(w)
+    ref = vals.astype(np.float64).astype(np.float16).view(np.uint16)
+    assert np.array_equal(s[:, 0], ref)
+
+
+def test_ternarize_rejects():
+    with pytest.raises(oracle.OracleError):
+        oracle.ternarize(np.full((1, 128), np.nan, np.float32))
+    w = np.zeros((1, 128), np.float32)
+    w[0, 0] = 65520.0  # rounds past the largest fp16
+    with pytest.raises(oracle.OracleError):
+        oracle.ternarize(w)
+    with pytest.raises(oracle.OracleError):
+        oracle.ternarize(np.zeros((1, 100), np.float32))
