@@ -102,6 +102,21 @@ size_t tq_packed_bytes(int fmt, int64_t N, int64_t K);
 int tq_pack(int fmt, int64_t N, int64_t K, const int8_t *trits, const uint16_t *scales,
             void *dst, size_t dst_bytes);
 
+/* Ternarise fp32 weights w[N][K] (host memory, row-major) into trits[N][K]
+ * and fp16 scales[N][K/128] for tq_pack: the weight step of a post-training
+ * ternary quantiser ("为什么PTQ1_0能让27B模型在4090上活得很好", section 1.2:
+ * per group two thresholds, values between them zeroed, the signs kept on
+ * either side, a per-group scale that shrinks the residual).  Per group of
+ * 128: the support is the k largest |w| (ranked by descending |w|, ties by
+ * the lower index), t = sign(w) there and 0 elsewhere, scale = the mean |w|
+ * over the support rounded to fp16 (ties to even), with k in 0..128
+ * maximising (sum of the k largest |w|)^2 / k, i.e. minimising
+ * sum (w - scale t)^2 before the rounding (ties: the smaller k; k = 0 is an
+ * all-zero group with scale 0).  Sums in double in rank order.  Host only,
+ * OpenMP over rows.  TQ_ERR_VALUE on a non-finite weight or a scale that
+ * rounds past 65504 (outputs then unspecified); K a multiple of 128. */
+int tq_ternarize(int64_t N, int64_t K, const float *w, int8_t *trits, uint16_t *scales);
+
 /* Exact inverse of tq_pack (host memory).  Rejects with TQ_ERR_FORMAT any
  * byte that tq_pack cannot produce (B3 byte >= 243, bad padding digit, 2B
  * code 3, non-zero padding rows) and with TQ_ERR_VALUE a non-finite scale. */

@@ -32,7 +32,8 @@ EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant
            "tq_gemv_workspace_bytes", "tq_gemv", "tq_gemv_gate_up_swiglu",
            "tq_gemm_workspace_bytes", "tq_gemm", "tq_debug_unpack", "tq_debug_group_sums",
            "tq_gemv_quant_workspace_bytes", "tq_gemv_quant",
-           "tq_decode_stack_workspace_bytes", "tq_decode_stack", "tq_hadamard_quant_act")
+           "tq_decode_stack_workspace_bytes", "tq_decode_stack", "tq_hadamard_quant_act",
+           "tq_ternarize")
 
 
 class TqLayer(ctypes.Structure):
@@ -70,6 +71,7 @@ def _load():
         "tq_decode_stack_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "tq_decode_stack": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
         "tq_hadamard_quant_act": ([I, I64, I64, P, P, P, P, P], I),
+        "tq_ternarize": ([I64, I64, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -122,6 +124,16 @@ def tq_pack(fmt: int, trits: np.ndarray, scales: np.ndarray) -> np.ndarray:
     _check(lib.tq_pack(fmt, N, K, t.ctypes.data, s.ctypes.data, out.ctypes.data, nbytes),
            "tq_pack")
     return out
+
+
+def tq_ternarize(w: np.ndarray):
+    """fp32 weights [N][K] (host) -> (trits int8 [N][K], fp16 scale bits uint16 [N][K/128])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    t = np.empty((N, K), dtype=np.int8)
+    s = np.empty((N, max(K // GROUP, 1)), dtype=np.uint16)
+    _check(lib.tq_ternarize(N, K, w.ctypes.data, t.ctypes.data, s.ctypes.data), "tq_ternarize")
+    return t, s
 
 
 def tq_unpack(fmt: int, blob: np.ndarray, N: int, K: int):

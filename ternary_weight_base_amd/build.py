@@ -46,9 +46,12 @@ def _run_parallel(cmds):
 def build() -> str:
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    host_o = os.path.join(bdir, "tq_host.o")
-    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-fopenmp", "-Wall", "-Wextra", "-I", INC,
-          "-c", os.path.join(CSRC, "tq_host.cpp"), "-o", host_o])
+    host_objs = []
+    for src in ("tq_host.cpp", "tq_ternarize.cpp"):
+        o = os.path.join(bdir, src.replace(".cpp", ".o"))
+        _run(["g++", "-O2", "-std=c++17", "-fPIC", "-fopenmp", "-Wall", "-Wextra", "-I", INC,
+              "-c", os.path.join(CSRC, src), "-o", o])
+        host_objs.append(o)
     objs, cmds = [], []
     for src in ("tq_kernels.hip", "tq_proj.hip", "tq_proj_b3.hip", "tq_proj_2b.hip",
                 "tq_gemv_mfma.hip", "tq_hadamard.hip"):
@@ -58,7 +61,7 @@ def build() -> str:
         objs.append(o)
     _run_parallel(cmds)
     tmp = LIB + ".tmp"
-    _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, host_o,
+    _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *host_objs,
           "-fopenmp=libgomp", "-lgomp"])
     os.replace(tmp, LIB)
     return LIB
