@@ -323,7 +323,9 @@ def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time
     - prefill GEMM (M = 512 on the layer-0 gate and down matrices) against
       the int8 MFMA peak;
     - small-batch decode (M tokens per step through the whole stack:
-      tq_quant_act + tq_gemv per projection, 8 launches a layer)."""
+      tq_quant_act + tq_gemv per projection, 8 launches a layer);
+    - ternarize_host: the host ternariser on one fp32 gate matrix
+      (17408 x 5120, 356 MB), the load-time step before tq_pack."""
     if args.no_extras:
         return None
     dev = "cuda"
@@ -361,6 +363,14 @@ def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time
     us_h = time_graph(capture(lambda: [tq.tq_hadamard_quant_act(xq[i:i + 1], sq, qq[i:i + 1], aq[i:i + 1])
                                        for i in range(64)]), 5, 1) * 1000.0 / 64
     out["quant_act_5120"] = {"us_per_call": round(us_q, 3), "bound": "launch latency"}
+    wt = synth.normal_f32(synth.seed(6, 1), INTER, HIDDEN)
+    t0 = time.time()
+    tq.tq_ternarize(wt)
+    sec = time.time() - t0
+    out["ternarize_host"] = {"N": INTER, "K": HIDDEN, "s": round(sec, 3),
+                             "input_GBps": round(wt.nbytes / sec / 1e9, 2),
+                             "threads": int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))}
+    del wt
     out["hadamard_quant_act_5120"] = {"us_per_call": round(us_h, 3), "bound": "launch latency"}
     # ffn_block over the stack's layers
     L = stack.layers
