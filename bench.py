@@ -477,13 +477,17 @@ def profile_summary(trace_dir, fetch_dir, write_dir):
         vals = [x for (k, cn), v in ctrs.items() if cn == cname and pick(k) for x in v]
         return vals
 
-    # the calibration copy: the largest copy dispatch (weight blobs are <= 20 MB)
-    fcal = per_dispatch(fetch, "FETCH_SIZE", lambda k: "opy" in k)
-    wcal = per_dispatch(write, "WRITE_SIZE", lambda k: "opy" in k)
+    # the calibration copy: the runtime's buffer-copy dispatch whose counters
+    # sit nearest to 64 MiB (the other device copies are weight uploads of
+    # <= 20 MB); 1024 B per KiB
+    fcal = per_dispatch(fetch, "FETCH_SIZE", lambda k: "copyBuffer" in k)
+    wcal = per_dispatch(write, "WRITE_SIZE", lambda k: "copyBuffer" in k)
     if not dom or not fcal or not wcal:
         raise SystemExit("dominant kernel or calibration copy not found in the profiles")
-    fscale = calib / (max(fcal) * 1024)
-    wscale = calib / (max(wcal) * 1024)
+    fcal = [max(fcal)]  # FETCH_SIZE reads about half the true bytes: the largest copy
+    wcal = [min(wcal, key=lambda v: abs(v - calib / 1024))]
+    fscale = calib / (fcal[0] * 1024)
+    wscale = calib / (wcal[0] * 1024)
     f = per_dispatch(fetch, "FETCH_SIZE", lambda k: k in dom)
     w = per_dispatch(write, "WRITE_SIZE", lambda k: k in dom)
     fb = sum(f) / len(f) * 1024 * fscale
