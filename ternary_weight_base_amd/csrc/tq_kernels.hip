@@ -37,6 +37,8 @@ using tq::Layout;
 #define TQ_GEMV_MFMA 1
 #endif
 size_t tq_internal_mgemv_ws_bytes(int fmt, int64_t N, int64_t K, int nmat);
+int tq_internal_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
+                     const float *a, float *y, int32_t *sums, hipStream_t st);
 int tq_internal_mgemv(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const void *W1,
                       const int8_t *q, const float *a_scale, float *y, void *ws, size_t ws_bytes,
                       hipStream_t st);
@@ -495,204 +497,6 @@ __global__ __launch_bounds__(64) void unpack_kernel(const uint8_t *__restrict__ 
   }
 }
 
-// ---------------------------------------------------------------------
-// Prefill GEMM.  grid (NB, ceil(M/128)), 256 threads (4 waves).
-// Per group: the block's 64 weight rows x 128 trits are decoded to int8 in
-// LDS (canonical k order; lane = row, wave = quarter of the row's bytes, so
-// every branch is uniform per wave and the k-blocks go out as 16-byte
-// stores), each wave multiplies its 32 activation rows by them with
-// 2 x 4 x 2 v_mfma_i32_16x16x64_i8, and rescales the int32 group sums by
-// s[n][g] into fp32 accumulators.  The next group's weights and activation
-// fragments are loaded into registers while the current group is decoded
-// and multiplied.
-// ---------------------------------------------------------------------
-constexpr int kGemmBM = 128;
-constexpr int kBtStride = 144;  // 128 trits + 16 bytes of padding per row
-
-template <int FMT, bool SUMS>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W,
-                                                   const int8_t *__restrict__ q,
-                                                   const float *__restrict__ a_scale,
-                                                   float *__restrict__ out,
-                                                   int32_t *__restrict__ sums, int M, int N, int K) {
-  constexpr int WPG = FMT == 0 ? 7 : 9;
-  __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
-  __shared__ __attribute__((aligned(16))) int8_t Bt[64 * kBtStride];
-  __shared__ float bscale[64];
-
-  const Layout L(FMT, N, K);
-  const int G = (int)L.G;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.x, m0 = blockIdx.y * kGemmBM;
-  const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
-  if (FMT == 0) fill_b3_lut<256>(lut);
-
-  // decode role: row dr = lane of the block (padding rows past Wb give zero
-  // trits and scale), part dp = wave
-  const int dr = lane, dp = wave, lr = min(dr, Wb - 1);
-  const bool row_live = dr < Wb;
-  const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
-  int8_t *brow = Bt + dr * kBtStride;
-
-  // MFMA role
-  const int li = lane & 15, slot = lane >> 4;
-  const int8_t *qrow[2];
-  bool qok[2];
-#pragma unroll
-  for (int ms = 0; ms < 2; ms++) {
-    const int row = m0 + 32 * wave + 16 * ms + li;
-    qok[ms] = row < M;
-    qrow[ms] = q + (size_t)min(row, M - 1) * K;
-  }
-
-  auto load_w = [&](int g, uint32_t (&w)[WPG]) {
-    const uint8_t *gb = W + L.group_base(b, g);
-    const uint4 P = *reinterpret_cast<const uint4 *>(gb + lr * 16);
-    w[0] = P.x; w[1] = P.y; w[2] = P.z; w[3] = P.w;
-    if constexpr (FMT == 0) {
-      const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + lr * 12);
-      w[4] = pb[0]; w[5] = pb[1]; w[6] = pb[2];
-    } else {
-      const uint4 Q = *reinterpret_cast<const uint4 *>(gb + Wb * 16 + lr * 16);
-      w[4] = Q.x; w[5] = Q.y; w[6] = Q.z; w[7] = Q.w;
-      w[8] = *reinterpret_cast<const uint16_t *>(gb + Wb * 32 + lr * 2);
-    }
-  };
-  auto load_a = [&](int g, v2l (&af)[2][2]) {
-#pragma unroll
-    for (int ms = 0; ms < 2; ms++)
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++)
-        af[ms][ks] = *reinterpret_cast<const v2l *>(qrow[ms] + (size_t)g * 128 + 64 * ks + 16 * slot);
-  };
-
-  v4i acc32[2][4];
-  float accf[2][4][4];
-#pragma unroll
-  for (int ms = 0; ms < 2; ms++)
-#pragma unroll
-    for (int ns = 0; ns < 4; ns++)
-#pragma unroll
-      for (int v = 0; v < 4; v++) accf[ms][ns][v] = 0.0f;
-
-  uint32_t wcur[WPG], wnext[WPG];
-  v2l acur[2][2], anext[2][2];
-  load_w(0, wcur);
-  load_a(0, acur);
-
-  for (int g = 0; g < G; g++) {
-    const int gn = min(g + 1, G - 1);
-    __syncthreads();  // previous group's Bt fully consumed (and the table built)
-    load_w(gn, wnext);
-    // ---- decode this group's 64 x 128 trits into Bt ---------------------
-    if constexpr (FMT == 0) {
-      uint32_t w[7];
-#pragma unroll
-      for (int i = 0; i < 7; i++) w[i] = row_live ? wcur[i] : 0x79797979u;  // 0x79: five zero trits
-      // k-block c (16 trits) = digits 0..3 of bytes 4c..4c+3; digit 4 of byte j is k = 100 + j
-#define TQ_BLK(C)                                                                         \
-  {                                                                                       \
-    const uint2 e0 = b3_byte<4 * (C)>(lut, w, laneoff), e1 = b3_byte<4 * (C) + 1>(lut, w, laneoff); \
-    const uint2 e2 = b3_byte<4 * (C) + 2>(lut, w, laneoff), e3 = b3_byte<4 * (C) + 3>(lut, w, laneoff); \
-    *reinterpret_cast<uint4 *>(brow + 16 * (C)) = make_uint4(e0.x, e1.x, e2.x, e3.x);    \
-    *reinterpret_cast<uint32_t *>(brow + 100 + 4 * (C)) =                                 \
-        e0.y | (e1.y << 8) | (e2.y << 16) | (e3.y << 24);                                 \
-  }
-      if (dp == 0) { TQ_BLK(0) TQ_BLK(4) }
-      if (dp == 1) { TQ_BLK(1) TQ_BLK(5) }
-      if (dp == 2) {
-        TQ_BLK(2)
-        // byte 24: k = 96..99 and 124; byte 25: k = 125..127 (digit 0 a pad)
-        const uint2 e24 = b3_byte<24>(lut, w, laneoff), e25 = b3_byte<25>(lut, w, laneoff);
-        *reinterpret_cast<uint32_t *>(brow + 96) = e24.x;
-        *reinterpret_cast<uint32_t *>(brow + 124) = (e25.x & 0xFFFFFF00u) | e24.y;
-      }
-      if (dp == 3) {
-        TQ_BLK(3)
-        bscale[dr] = row_live ? half_bits(wcur[6] >> 16) : 0.0f;
-      }
-#undef TQ_BLK
-    } else {
-      // byte 4m + c, bits 2s hold k = 16m + 4s + c: word 4m + s of the row is
-      // field s of dword m; part dp writes k-blocks dp and dp + 4
-#pragma unroll
-      for (int cc = 0; cc < 2; cc++) {
-        const int m = dp + 4 * cc;
-        const uint32_t wm = row_live ? wcur[m] : 0x55555555u;  // code 1: zero trits
-        uint32_t t[4];
-#pragma unroll
-        for (int s = 0; s < 4; s++) t[s] = perm_b32(0u, 0x000100FFu, (wm >> (2 * s)) & 0x03030303u);
-        *reinterpret_cast<uint4 *>(brow + 16 * m) = make_uint4(t[0], t[1], t[2], t[3]);
-      }
-      if (dp == 0) bscale[dr] = row_live ? half_bits(wcur[8]) : 0.0f;
-    }
-    load_a(gn, anext);
-    __syncthreads();
-
-    // ---- MFMA: wave rows m0 + 32*wave + 16*ms + i, all 64 columns --------
-#pragma unroll
-    for (int ms = 0; ms < 2; ms++)
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++)
-        if (!qok[ms]) acur[ms][ks] = v2l{0, 0};
-#pragma unroll
-    for (int ms = 0; ms < 2; ms++)
-#pragma unroll
-      for (int ns = 0; ns < 4; ns++) acc32[ms][ns] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-      v2l bf[4];
-#pragma unroll
-      for (int ns = 0; ns < 4; ns++)
-        bf[ns] = *reinterpret_cast<const v2l *>(Bt + (16 * ns + li) * kBtStride + 64 * ks + 16 * slot);
-#pragma unroll
-      for (int ms = 0; ms < 2; ms++)
-#pragma unroll
-        for (int ns = 0; ns < 4; ns++)
-          acc32[ms][ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(acur[ms][ks], bf[ns], acc32[ms][ns], 0, 0, 0);
-    }
-    // ---- output element (row 4*slot + v, column li) of each 16x16 tile ---
-#pragma unroll
-    for (int ns = 0; ns < 4; ns++) {
-      const int col = 16 * ns + li;
-      const float sc = bscale[col];
-#pragma unroll
-      for (int ms = 0; ms < 2; ms++) {
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-          if (SUMS) {
-            const int row = m0 + 32 * wave + 16 * ms + 4 * slot + v;
-            if (row < M && col < rows)
-              sums[((size_t)row * N + (size_t)b * tq::kBlockRows + col) * G + g] = acc32[ms][ns][v];
-          } else {
-            accf[ms][ns][v] = fmaf(sc, (float)acc32[ms][ns][v], accf[ms][ns][v]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < WPG; i++) wcur[i] = wnext[i];
-#pragma unroll
-    for (int ms = 0; ms < 2; ms++)
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++) acur[ms][ks] = anext[ms][ks];
-  }
-  if (SUMS) return;
-#pragma unroll
-  for (int ms = 0; ms < 2; ms++)
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-      const int row = m0 + 32 * wave + 16 * ms + 4 * slot + v;
-      if (row >= M) continue;
-      const float a = a_scale[row];
-#pragma unroll
-      for (int ns = 0; ns < 4; ns++) {
-        const int col = 16 * ns + li;
-        if (col < rows) out[(size_t)row * N + (size_t)b * tq::kBlockRows + col] = a * accf[ms][ns][v];
-      }
-    }
-}
 
 // ---------------------------------------------------------------------
 // Host side: argument checks and launch plans.
@@ -855,21 +659,7 @@ int gemv_common(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const 
 
 int gemm_launch(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
                 const float *a, float *y, int32_t *sums, hipStream_t st) {
-  const Layout L(fmt, N, K);
-  dim3 grid((unsigned)L.NB, (unsigned)((M + kGemmBM - 1) / kGemmBM));
-  const uint8_t *Wb = (const uint8_t *)W;
-  if (fmt == TQ_FMT_B3) {
-    if (sums)
-      hipLaunchKernelGGL((gemm_kernel<0, true>), grid, dim3(256), 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
-    else
-      hipLaunchKernelGGL((gemm_kernel<0, false>), grid, dim3(256), 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
-  } else {
-    if (sums)
-      hipLaunchKernelGGL((gemm_kernel<1, true>), grid, dim3(256), 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
-    else
-      hipLaunchKernelGGL((gemm_kernel<1, false>), grid, dim3(256), 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
-  }
-  return check_stream_launch();
+  return tq_internal_gemm(fmt, M, N, K, W, q, a, y, sums, st);
 }
 
 }  // namespace
