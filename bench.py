@@ -401,7 +401,8 @@ def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time
         tq.tq_quant_act(x, q, a)
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
         W = stack.W[name][0]
-        ms = time_graph(capture(lambda: tq.tq_gemm(fmt, M, N, K, W, q, a, y)), 20, 3)
+        gws = tq.workspace(fmt, M, N, K)
+        ms = time_graph(capture(lambda: tq.tq_gemm(fmt, M, N, K, W, q, a, y, gws)), 20, 3)
         tops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         out[f"prefill_gemm_{name}"] = {"M": M, "N": N, "K": K, "us": round(ms * 1e3, 2),
                                        "TOP/s": round(tops, 1), "peak_int8_mfma_TOP/s": 5000.0,

@@ -14,7 +14,8 @@
 // 2 x 4 x 2 v_mfma_i32_16x16x64_i8 and rescales the int32 group sums by
 // s[n][g] into fp32 accumulators.  The next group's weights and activation
 // fragments are loaded into registers while the current group is decoded
-// and multiplied.  A two-buffer variant that decodes group g + 1 while group
+// and multiplied.  Grids with few tiles also split K into C chunks
+// (blockIdx.z), finished deterministically by the tile's last chunk.  A two-buffer variant that decodes group g + 1 while group
 // g's MFMAs run measured slower (one workgroup's waves then wait on both).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,7 +59,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
                                                    const int8_t *__restrict__ q,
                                                    const float *__restrict__ a_scale,
                                                    float *__restrict__ out,
-                                                   int32_t *__restrict__ sums, int M, int N, int K) {
+                                                   int32_t *__restrict__ sums, float *__restrict__ partials,
+                                                   uint32_t *__restrict__ counters, int M, int N, int K,
+                                                   int C) {
   constexpr int WPG = FMT == 0 ? 7 : 9;
   __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLut16Copies : 1];
   __shared__ __attribute__((aligned(16))) int8_t Bt[64 * kBtStride];
@@ -68,7 +71,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
   const int G = (int)L.G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.x, m0 = blockIdx.y * kGemmBM;
+  const int b = blockIdx.x, m0 = blockIdx.y * kGemmBM, c = blockIdx.z;
+  // K chunk c of C: groups gbeg .. gend - 1 (unsigned 32-bit: C G < 2^22)
+  const int gbeg = (int)((uint32_t)(c * G) / (uint32_t)C);
+  const int gend = (int)((uint32_t)((c + 1) * G) / (uint32_t)C);
   const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
   if (FMT == 0) fill_lut16(lut);
 
@@ -122,11 +128,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
 
   uint32_t wcur[WPG], wnext[WPG];
   v2l acur[2][2], anext[2][2];
-  load_w(0, wcur);
-  load_a(0, acur);
+  load_w(gbeg, wcur);
+  load_a(gbeg, acur);
 
-  for (int g = 0; g < G; g++) {
-    const int gn = min(g + 1, G - 1);
+  for (int g = gbeg; g < gend; g++) {
+    const int gn = min(g + 1, gend - 1);
     __syncthreads();  // previous group's Bt fully consumed (and the table built)
     load_w(gn, wnext);
     // ---- decode this group's 64 x 128 trits into Bt ---------------------
@@ -223,6 +229,48 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
       for (int ks = 0; ks < 2; ks++) acur[ms][ks] = anext[ms][ks];
   }
   if (SUMS) return;
+  // A tile cut into C K chunks: every chunk publishes its fp32 sums (value i
+  // of thread t at [chunk][tile][i][t], so each store covers 256 contiguous
+  // bytes) with agent-scope stores, the last to arrive (agent-scope counter)
+  // adds the chunks in chunk order.
+  __shared__ int last_flag;
+  if (C > 1) {
+    const size_t tile = (size_t)blockIdx.y * gridDim.x + b, ntiles = (size_t)gridDim.x * gridDim.y;
+    float *mine = partials + ((size_t)c * ntiles + tile) * 256 * 32 + tid;
+#pragma unroll
+    for (int ms = 0; ms < 2; ms++)
+#pragma unroll
+      for (int ns = 0; ns < 4; ns++)
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+          __hip_atomic_store(mine + ((ms * 4 + ns) * 4 + v) * 256, accf[ms][ns][v], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's sums have reached device scope
+    __syncthreads();                // ... and so have every other thread's
+    if (tid == 0)
+      last_flag = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (uint32_t)(C - 1);
+    __syncthreads();
+    if (!last_flag) return;  // another chunk finishes this tile
+#pragma unroll
+    for (int ms = 0; ms < 2; ms++)
+#pragma unroll
+      for (int ns = 0; ns < 4; ns++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) accf[ms][ns][v] = 0.0f;
+    for (int cc = 0; cc < C; cc++) {
+      const float *src = partials + ((size_t)cc * ntiles + tile) * 256 * 32 + tid;
+#pragma unroll
+      for (int ms = 0; ms < 2; ms++)
+#pragma unroll
+        for (int ns = 0; ns < 4; ns++)
+#pragma unroll
+          for (int v = 0; v < 4; v++)
+            accf[ms][ns][v] += __hip_atomic_load(src + ((ms * 4 + ns) * 4 + v) * 256, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 #pragma unroll
   for (int ms = 0; ms < 2; ms++)
 #pragma unroll
@@ -238,24 +286,65 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
     }
 }
 
+struct GemmPlan {
+  int C;
+  size_t counters_bytes, partials_bytes;
+};
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+#ifndef TQ_GEMM_TARGET
+#define TQ_GEMM_TARGET 768
+#endif
+
+// K chunks per tile: enough workgroups for about three per CU
+// (TQ_GEMM_TARGET), at least 8 groups per chunk; the debug group sums take
+// one chunk.
+GemmPlan gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, bool sums) {
+  const Layout L(fmt, N, K);
+  const int64_t tiles = L.NB * ((M + kGemmBM - 1) / kGemmBM);
+  int64_t C = sums ? 1 : TQ_GEMM_TARGET / tiles;
+  if (C > L.G / 8) C = L.G / 8;
+  if (C < 1) C = 1;
+  GemmPlan p;
+  p.C = (int)C;
+  p.counters_bytes = C > 1 ? round256((size_t)tiles * 4) : 0;
+  p.partials_bytes = C > 1 ? round256((size_t)C * tiles * 256 * 32 * 4) : 0;
+  return p;
+}
+
 }  // namespace
 
-// Arguments already checked by the caller (shape, alignment).
+size_t tq_internal_gemm_ws_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
+  const GemmPlan p = gemm_plan(fmt, M, N, K, false);
+  return p.counters_bytes + p.partials_bytes;
+}
+
+// Arguments already checked by the caller (shape, alignment); the workspace
+// (zero-filled before its first use, left zero) is checked here.
 int tq_internal_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
-                     const float *a, float *y, int32_t *sums, hipStream_t st) {
+                     const float *a, float *y, int32_t *sums, void *ws, size_t ws_bytes, hipStream_t st) {
   const Layout L(fmt, N, K);
-  const dim3 grid((unsigned)L.NB, (unsigned)((M + kGemmBM - 1) / kGemmBM)), block(256);
-  const uint8_t *Wb = (const uint8_t *)W;
-  if (fmt == TQ_FMT_B3) {
-    if (sums)
-      hipLaunchKernelGGL((gemm_kernel<0, true>), grid, block, 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
-    else
-      hipLaunchKernelGGL((gemm_kernel<0, false>), grid, block, 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
-  } else {
-    if (sums)
-      hipLaunchKernelGGL((gemm_kernel<1, true>), grid, block, 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
-    else
-      hipLaunchKernelGGL((gemm_kernel<1, false>), grid, block, 0, st, Wb, q, a, y, sums, (int)M, (int)N, (int)K);
+  const GemmPlan p = gemm_plan(fmt, M, N, K, sums != nullptr);
+  if (p.C > 1) {
+    if (!ws) return TQ_ERR_NULL;
+    if (((uintptr_t)ws & 15u) != 0) return TQ_ERR_ALIGN;
+    if (ws_bytes < p.counters_bytes + p.partials_bytes) return TQ_ERR_SIZE;
   }
+  uint32_t *counters = p.C > 1 ? (uint32_t *)ws : nullptr;
+  float *partials = p.C > 1 ? (float *)((char *)ws + p.counters_bytes) : nullptr;
+  const dim3 grid((unsigned)L.NB, (unsigned)((M + kGemmBM - 1) / kGemmBM), (unsigned)p.C), block(256);
+  const uint8_t *Wb = (const uint8_t *)W;
+#define TQ_GEMM(F_, S_)                                                                               \
+  hipLaunchKernelGGL((gemm_kernel<F_, S_>), grid, block, 0, st, Wb, q, a, y, sums, partials, counters, \
+                     (int)M, (int)N, (int)K, p.C)
+  if (fmt == TQ_FMT_B3) {
+    if (sums) TQ_GEMM(0, true);
+    else TQ_GEMM(0, false);
+  } else {
+    if (sums) TQ_GEMM(1, true);
+    else TQ_GEMM(1, false);
+  }
+#undef TQ_GEMM
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }

@@ -38,7 +38,8 @@ using tq::Layout;
 #endif
 size_t tq_internal_mgemv_ws_bytes(int fmt, int64_t N, int64_t K, int nmat);
 int tq_internal_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
-                     const float *a, float *y, int32_t *sums, hipStream_t st);
+                     const float *a, float *y, int32_t *sums, void *ws, size_t ws_bytes, hipStream_t st);
+size_t tq_internal_gemm_ws_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 int tq_internal_mgemv(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const void *W1,
                       const int8_t *q, const float *a_scale, float *y, void *ws, size_t ws_bytes,
                       hipStream_t st);
@@ -658,8 +659,9 @@ int gemv_common(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const 
 }
 
 int gemm_launch(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
-                const float *a, float *y, int32_t *sums, hipStream_t st) {
-  return tq_internal_gemm(fmt, M, N, K, W, q, a, y, sums, st);
+                const float *a, float *y, int32_t *sums, hipStream_t st, void *ws = nullptr,
+                size_t ws_bytes = 0) {
+  return tq_internal_gemm(fmt, M, N, K, W, q, a, y, sums, ws, ws_bytes, st);
 }
 
 }  // namespace
@@ -711,7 +713,9 @@ extern "C" int tq_gemv_gate_up_swiglu(int fmt, int64_t M, int64_t N, int64_t K, 
 
 extern "C" size_t tq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
   if (M >= 1 && M <= TQ_GEMV_MAX_M) return tq_gemv_workspace_bytes(fmt, M, N, K);
-  return 0;
+  if ((fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) || !shape_ok(N, K) || M < 1 || M > ((int64_t)1 << 24))
+    return 0;
+  return tq_internal_gemm_ws_bytes(fmt, M, N, K);
 }
 
 extern "C" int tq_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
@@ -721,7 +725,7 @@ extern "C" int tq_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, 
   if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
   if (!shape_ok(N, K) || M < 1 || M > ((int64_t)1 << 24)) return TQ_ERR_SHAPE;
   if (!aligned16(W) || !aligned16(q) || !aligned4(a_scale) || !aligned4(y)) return TQ_ERR_ALIGN;
-  return gemm_launch(fmt, M, N, K, W, q, a_scale, y, nullptr, (hipStream_t)stream);
+  return gemm_launch(fmt, M, N, K, W, q, a_scale, y, nullptr, (hipStream_t)stream, ws, ws_bytes);
 }
 
 extern "C" int tq_debug_unpack(int fmt, int64_t N, int64_t K, const void *W, int8_t *trits,

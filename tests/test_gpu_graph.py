@@ -103,8 +103,9 @@ def test_graph_gemm_and_hadamard():
     q = torch.empty((M, K), dtype=torch.int8, device="cuda")
     a = torch.empty(M, device="cuda")
     y = torch.empty((M, N), device="cuda")
+    ws = tq.workspace(TB, M, N, K)  # 64 output tiles: K split in chunks
 
     def fn():
         tq.tq_hadamard_quant_act(x, s, q, a)
-        tq.tq_gemm(TB, M, N, K, W, q, a, y)
+        tq.tq_gemm(TB, M, N, K, W, q, a, y, ws)
     _replays_match(fn, [q, a, y])

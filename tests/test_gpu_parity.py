@@ -217,7 +217,7 @@ def test_gemm_vs_oracle(fmt, M, N, K):
     q, a = _quant_gpu(acts_f16(M, K, 6100 + M))
     W = upload_blob(fmt, t, s)
     y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
-    tq.tq_gemm(fmt, M, N, K, W, q, a, y)
+    tq.tq_gemm(fmt, M, N, K, W, q, a, y, tq.workspace(fmt, M, N, K))
     torch.cuda.synchronize()
     assert_close(y.cpu().numpy(), oracle.gemv(t, s, q.cpu().numpy(), a.cpu().numpy()), "gemm")
 
@@ -234,7 +234,7 @@ def test_gemm_prefill_full_size_sampled(fmt, N, K):
     q, a = _quant_gpu(acts_f16(M, K, 6600))
     W = upload_blob(fmt, t, s)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    tq.tq_gemm(fmt, M, N, K, W, q, a, y)
+    tq.tq_gemm(fmt, M, N, K, W, q, a, y, tq.workspace(fmt, M, N, K))
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([[0, 63, 64, N - 1], np.random.default_rng(1).integers(0, N, 44)]))
     ref = oracle.gemv_rows(t, s, q.cpu().numpy(), a.cpu().numpy(), rows)

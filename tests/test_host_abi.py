@@ -233,6 +233,10 @@ def test_device_entry_points_validate_on_host():
     assert L.tq_gemm(B3, 512, 64, 128, FAKE, MIS, FAKE, FAKE, None, 0, None) == -3
     assert L.tq_gemm(B3, 512, 64, 128, FAKE, FAKE, ODD, FAKE, None, 0, None) == -3
     assert L.tq_gemm(4, 512, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
+    gneed = tq.tq_gemm_workspace_bytes(B3, 512, 5120, 17408)  # split K: a workspace is needed
+    assert L.tq_gemm(B3, 512, 5120, 17408, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert L.tq_gemm(B3, 512, 5120, 17408, FAKE, FAKE, FAKE, FAKE, MIS, gneed, None) == -3
+    assert L.tq_gemm(B3, 512, 5120, 17408, FAKE, FAKE, FAKE, FAKE, FAKE, gneed - 1, None) == -7
     # debug hooks
     assert L.tq_debug_unpack(B3, 64, 128, FAKE, None, None) == -1
     assert L.tq_debug_unpack(B3, 0, 128, FAKE, FAKE, None) == -2
@@ -323,5 +327,6 @@ def test_workspace_sizes():
     assert tq.tq_gemv_workspace_bytes(B3, 1, 1024, 1024) == 0
     for N, K in ((5120, 8192), (5120, 17408), (10240, 5120)):
         assert tq.tq_gemv_workspace_bytes(B3, 1, N, K) > 0
-    assert tq.tq_gemm_workspace_bytes(B3, 512, 17408, 5120) == 0
+    assert tq.tq_gemm_workspace_bytes(B3, 512, 17408, 5120) == 0   # 1088 tiles: no K split
+    assert tq.tq_gemm_workspace_bytes(B3, 512, 5120, 17408) > 0    # 320 tiles: K in chunks
     assert tq.tq_gemv_workspace_bytes(B3, 17, 1024, 1024) == 0  # out of range
