@@ -55,14 +55,18 @@ def parse():
     return p.parse_args()
 
 
+# The sources the dominant kernel (the projection kernel) is built from.
+DOMINANT_SOURCES = ("tq_proj.h", "tq_proj_kernel.h", "tq_proj.hip", "tq_proj_b3.hip", "tq_device.h",
+                    "tq_layout.h", "../../include/tq.h")
+
+
 def kernel_source_sha() -> str:
-    """Hash of every device source: traffic counted on other code is stale."""
+    """Hash of the dominant kernel's sources: traffic counted on other code is stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_weight_base_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in DOMINANT_SOURCES:
+        with open(os.path.normpath(os.path.join(csrc, name)), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
