@@ -100,3 +100,24 @@ def test_gemv_quant_zero_input():
     x = np.zeros(K, dtype=np.float16)
     y, yb, ref = _run(B3, N, K, x, True, 65)
     assert np.all(y == 0) and np.all(yb == 0)
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
+@pytest.mark.parametrize("case", ["gate_up_f16", "gate_up_f32", "down_f32"])
+def test_gemv_quant_full_ffn_shapes(fmt, case):
+    """The FFN block's launches at full size: gate/up 2 x 17408 x 5120 (the
+    equal item split over 256 workgroups) on an fp16 or an fp32 input, and
+    down 5120 x 17408 (K chunks) on an fp32 input with block maxima."""
+    say(f"gemv_quant full {FMTS[fmt]} {case}")
+    if case == "down_f32":
+        N, K, gate_up = 5120, 17408, False
+    else:
+        N, K, gate_up = 17408, 5120, True
+    if case == "gate_up_f16":
+        x, xb = synth.normal_f16(synth.seed(66, K), K), None
+    else:
+        x = synth.normal_f32(synth.seed(67, K), K)
+        xb = _block_max(x)
+    y, yb, ref = _run(fmt, N, K, x, gate_up, 68, x_bmax=xb)
+    assert_close(y, ref, "y")
+    assert np.array_equal(yb, _block_max(y)), "block maxima of y"
