@@ -20,6 +20,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 GROUP = 128
 FMT_B3 = 0
 FMT_2B = 1
+FMT_BP = 2
 
 
 class OracleError(RuntimeError):
@@ -54,7 +55,8 @@ def lib():
         for name in ("orc_b3_bytes", "orc_2b_bytes"):
             getattr(L, name).argtypes = [I64, I64]
             getattr(L, name).restype = ctypes.c_size_t
-        for name in ("orc_pack_b3", "orc_unpack_b3", "orc_pack_2b", "orc_unpack_2b"):
+        for name in ("orc_pack_b3", "orc_unpack_b3", "orc_pack_2b", "orc_unpack_2b", "orc_pack_bp",
+                     "orc_unpack_bp"):
             getattr(L, name).argtypes = [I64, I64, P, P, P]
             getattr(L, name).restype = ctypes.c_int
         for name in ("orc_quant_f16", "orc_quant_f32"):
@@ -99,7 +101,7 @@ def half_to_float(h: int) -> float:
 
 
 def packed_bytes(fmt: int, N: int, K: int) -> int:
-    return int((lib().orc_b3_bytes if fmt == FMT_B3 else lib().orc_2b_bytes)(N, K))
+    return int((lib().orc_b3_bytes if fmt == FMT_B3 else lib().orc_2b_bytes)(N, K))  # BP: as 2B
 
 
 def pack(fmt: int, trits: np.ndarray, scales: np.ndarray) -> np.ndarray:
@@ -110,7 +112,7 @@ def pack(fmt: int, trits: np.ndarray, scales: np.ndarray) -> np.ndarray:
     if nbytes == 0:
         raise OracleError("bad shape")
     out = np.empty(nbytes, dtype=np.uint8)
-    fn = lib().orc_pack_b3 if fmt == FMT_B3 else lib().orc_pack_2b
+    fn = {FMT_B3: lib().orc_pack_b3, FMT_2B: lib().orc_pack_2b, FMT_BP: lib().orc_pack_bp}[fmt]
     _check(fn(N, K, _p(t), _p(s), _p(out)), "pack")
     return out
 
@@ -119,7 +121,7 @@ def unpack(fmt: int, blob: np.ndarray, N: int, K: int):
     b = np.ascontiguousarray(blob, dtype=np.uint8)
     t = np.empty((N, K), dtype=np.int8)
     s = np.empty((N, K // GROUP), dtype=np.uint16)
-    fn = lib().orc_unpack_b3 if fmt == FMT_B3 else lib().orc_unpack_2b
+    fn = {FMT_B3: lib().orc_unpack_b3, FMT_2B: lib().orc_unpack_2b, FMT_BP: lib().orc_unpack_bp}[fmt]
     rc = fn(N, K, _p(b), _p(t), _p(s))
     return rc, t, s
 

@@ -175,6 +175,54 @@ int orc_unpack_2b(int64_t N, int64_t K, const uint8_t *src, int8_t *t, uint16_t 
   return ORC_OK;
 }
 
+/* ---- BP: two bit-planes per group, nonzero and sign ---------------------- */
+
+int orc_pack_bp(int64_t N, int64_t K, const int8_t *t, const uint16_t *s, uint8_t *dst) {
+  if (!t || !s || !dst || !shape_ok(N, K)) return ORC_ERR_ARG;
+  int rc = check_trits_scales(N, K, t, s);
+  if (rc) return rc;
+  int64_t G = K / ORC_GROUP;
+  for (int64_t n = 0; n < N; n++) {
+    for (int64_t g = 0; g < G; g++) {
+      const int8_t *tg = t + n * K + g * ORC_GROUP;
+      uint8_t *out = dst + (n * G + g) * 32;
+      for (int b = 0; b < 16; b++) {
+        int nz = 0, neg = 0;
+        for (int i = 0; i < 8; i++) {
+          if (tg[8 * b + i] != 0) nz |= 1 << i;
+          if (tg[8 * b + i] < 0) neg |= 1 << i;
+        }
+        out[b] = (uint8_t)nz;
+        out[16 + b] = (uint8_t)neg;
+      }
+    }
+  }
+  put_scales(dst + N * G * 32, N * G, s);
+  return ORC_OK;
+}
+
+int orc_unpack_bp(int64_t N, int64_t K, const uint8_t *src, int8_t *t, uint16_t *s) {
+  if (!src || !t || !s || !shape_ok(N, K)) return ORC_ERR_ARG;
+  int64_t G = K / ORC_GROUP;
+  for (int64_t n = 0; n < N; n++) {
+    for (int64_t g = 0; g < G; g++) {
+      const uint8_t *in = src + (n * G + g) * 32;
+      int8_t *tg = t + n * K + g * ORC_GROUP;
+      for (int b = 0; b < 16; b++) {
+        if (in[16 + b] & ~in[b]) return ORC_ERR_FORMAT; /* a sign on a zero trit */
+        for (int i = 0; i < 8; i++) {
+          int nz = (in[b] >> i) & 1, neg = (in[16 + b] >> i) & 1;
+          tg[8 * b + i] = (int8_t)(nz ? (neg ? -1 : 1) : 0);
+        }
+      }
+    }
+  }
+  get_scales(src + N * G * 32, N * G, s);
+  for (int64_t i = 0; i < N * G; i++)
+    if (!half_is_finite(s[i])) return ORC_ERR_VALUE;
+  return ORC_OK;
+}
+
 /* ---- activation quantizer ---------------------------------------------- */
 
 /* One row of K fp32 values.  Every operation below is a single IEEE fp32
@@ -294,13 +342,14 @@ int orc_swiglu(int64_t n, const float *g, const float *u, float *h) {
 
 int orc_project_packed(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t *blob,
                        const int8_t *q, const float *a, float *y) {
-  if (!blob || !shape_ok(N, K) || (fmt != 0 && fmt != 1)) return ORC_ERR_ARG;
+  if (!blob || !shape_ok(N, K) || fmt < 0 || fmt > 2) return ORC_ERR_ARG;
   int64_t G = K / ORC_GROUP;
   int8_t *t = (int8_t *)malloc((size_t)(N * K));
   uint16_t *s = (uint16_t *)malloc((size_t)(N * G) * sizeof(uint16_t));
   int rc = ORC_ERR_ARG;
   if (t && s) {
-    rc = fmt == 0 ? orc_unpack_b3(N, K, blob, t, s) : orc_unpack_2b(N, K, blob, t, s);
+    rc = fmt == 0 ? orc_unpack_b3(N, K, blob, t, s)
+                  : fmt == 1 ? orc_unpack_2b(N, K, blob, t, s) : orc_unpack_bp(N, K, blob, t, s);
     if (rc == ORC_OK) rc = orc_gemv(M, N, K, t, s, q, a, y);
   }
   free(t);

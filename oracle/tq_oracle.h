@@ -68,6 +68,15 @@ int orc_unpack_b3(int64_t N, int64_t K, const uint8_t *src, int8_t *t, uint16_t 
 int orc_pack_2b(int64_t N, int64_t K, const int8_t *t, const uint16_t *s, uint8_t *dst);
 int orc_unpack_2b(int64_t N, int64_t K, const uint8_t *src, int8_t *t, uint16_t *s);
 
+/* Canonical BP (two bit-planes, the compute-oriented ternary layout the
+ * Bonsai page names as a next step: "Ternary Bonsai 2 27B…", section "后面还有
+ * 没有优化空间"): 32 bytes per group; bytes 0..15 are the nonzero plane
+ * (trit i of the group at byte i/8, bit i%8: 1 when t != 0), bytes 16..31
+ * the sign plane at the same positions (1 when t = -1, 0 on zero trits;
+ * a sign bit on a zero trit is rejected).  Scales at N*G*32 as in 2B. */
+int orc_pack_bp(int64_t N, int64_t K, const int8_t *t, const uint16_t *s, uint8_t *dst);
+int orc_unpack_bp(int64_t N, int64_t K, const uint8_t *src, int8_t *t, uint16_t *s);
+
 /* Per-row absmax int8 quantizer, fp32 arithmetic:
  *   a = max|x|; a == 0 -> scale 0, q 0;
  *   else scale = a/127, inv = 127/a, q = clamp(rint(x*inv), -127, 127).

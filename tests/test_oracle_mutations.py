@@ -41,6 +41,9 @@ MUTATIONS = [
      "tg[i] = wg[i] > 0.0f ? -1 : (wg[i] < 0.0f ? 1 : 0);"),
     ("half_round_truncates", "double r = rint(ldexp(v, 10 - E));", "double r = floor(ldexp(v, 10 - E));"),
     ("half_subnormal_step", "double r = rint(ldexp(v, 24));", "double r = rint(ldexp(v, 23));"),
+    ("bp_bit_order", "if (tg[8 * b + i] != 0) nz |= 1 << i;", "if (tg[8 * b + i] != 0) nz |= 1 << (7 - i);"),
+    ("bp_sign_of_positive", "if (tg[8 * b + i] < 0) neg |= 1 << i;", "if (tg[8 * b + i] > 0) neg |= 1 << i;"),
+    ("bp_accepts_sign_on_zero", "if (in[16 + b] & ~in[b]) return ORC_ERR_FORMAT;", "if (0) return ORC_ERR_FORMAT;"),
 ]
 
 

@@ -17,7 +17,7 @@ import oracle
 import synth
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
-B3, TB = oracle.FMT_B3, oracle.FMT_2B
+B3, TB, BP = oracle.FMT_B3, oracle.FMT_2B, oracle.FMT_BP
 
 
 def _gold(name):
@@ -138,7 +138,7 @@ def test_pack_rejects_bad_inputs():
     s = np.full((2, 2), 0x3C00, np.uint16)
     bad = t.copy()
     bad[1, 7] = 2
-    for fmt in (B3, TB):
+    for fmt in (B3, TB, BP):
         with pytest.raises(oracle.OracleError):
             oracle.pack(fmt, bad, s)
         for nonfinite in (0x7C00, 0xFC00, 0x7E00):
@@ -180,6 +180,58 @@ def test_2b_random_roundtrip():
     blob = oracle.pack(TB, t, s)
     assert blob.size == N * 3 * 34
     rc, t2, s2 = oracle.unpack(TB, blob, N, K)
+    assert rc == 0 and np.array_equal(t, t2) and np.array_equal(s, s2)
+
+
+# ---------------------------------------------------------------- BP ------
+
+def test_bp_bit_positions_and_fills():
+    """Trit k of a group: nonzero plane byte k // 8, bit k % 8; the sign
+    plane 16 bytes later; fills of 0, +1 and -1."""
+    s1 = np.array([[0x3C00]], np.uint16)
+    for k in (0, 1, 7, 8, 63, 100, 127):
+        for v in (1, -1):
+            t = np.zeros((1, 128), np.int8)
+            t[0, k] = v
+            blob = oracle.pack(BP, t, s1)
+            ref = np.zeros(32, np.uint8)
+            ref[k // 8] = 1 << (k % 8)
+            if v < 0:
+                ref[16 + k // 8] = 1 << (k % 8)
+            assert np.array_equal(blob[:32], ref), (k, v)
+    for fill, nz, sg in ((0, 0x00, 0x00), (1, 0xFF, 0x00), (-1, 0xFF, 0xFF)):
+        blob = oracle.pack(BP, np.full((1, 128), fill, np.int8), s1)
+        assert list(blob[:16]) == [nz] * 16 and list(blob[16:32]) == [sg] * 16
+    assert list(oracle.pack(BP, np.zeros((1, 128), np.int8), s1)[32:34]) == [0x00, 0x3C]
+
+
+def test_bp_all_byte_pairs():
+    """Every (nonzero, sign) byte pair: accepted exactly when no sign bit
+    sits on a zero trit (3^8 = 6561 pairs), decoded bit by bit."""
+    s1 = np.array([[0x3C00]], np.uint16)
+    base = oracle.pack(BP, np.zeros((1, 128), np.int8), s1)
+    valid = 0
+    for nz in range(256):
+        for sg in range(256):
+            blob = base.copy()
+            blob[5], blob[21] = nz, sg
+            rc, t, _ = oracle.unpack(BP, blob, 1, 128)
+            ok = (sg & ~nz) == 0
+            assert (rc == 0) == ok
+            if ok:
+                valid += 1
+                ref = [(-1 if (sg >> i) & 1 else 1) if (nz >> i) & 1 else 0 for i in range(8)]
+                assert list(t[0, 40:48]) == ref
+    assert valid == 6561
+
+
+def test_bp_random_roundtrip():
+    N, K = 5, 384
+    t = synth.trits(synth.seed(95), N, K)
+    s = synth.scales(synth.seed(96), N, K)
+    blob = oracle.pack(BP, t, s)
+    assert blob.size == N * 3 * 34 and blob.size == oracle.packed_bytes(BP, N, K)
+    rc, t2, s2 = oracle.unpack(BP, blob, N, K)
     assert rc == 0 and np.array_equal(t, t2) and np.array_equal(s, s2)
 
 
@@ -358,7 +410,7 @@ def test_gemv_rows_and_packed_agree_with_gemv():
     y = oracle.gemv(t, s, q, a)
     rows = np.array([0, 20, 7, 7])
     assert np.array_equal(oracle.gemv_rows(t, s, q, a, rows), y[:, rows])
-    for fmt in (B3, TB):
+    for fmt in (B3, TB, BP):
         assert np.array_equal(oracle.project_packed(fmt, oracle.pack(fmt, t, s), N, K, q, a), y)
     oracle.set_threads(4)
     try:
