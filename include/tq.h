@@ -33,14 +33,14 @@
  *
  * Packed weight blob ("device layout").  Rows are cut into blocks of 64
  * (the last block holds the remaining w rows, padded up to a multiple of 4
- * rows for B3 and of 8 rows for 2B; padding rows hold zero trits and a zero
- * scale).  Let G = K/128 and Wb the (padded) row count of a block.  Block b
- * starts at byte 64*b*G*P, where P = 28 (B3) or 34 (2B); inside it group g
- * starts at g*Wb*P, and row r of the block owns:
+ * rows for B3 and of 8 rows for 2B and BP; padding rows hold zero trits and
+ * a zero scale).  Let G = K/128 and Wb the (padded) row count of a block.
+ * Block b starts at byte 64*b*G*P, where P = 28 (B3) or 34 (2B, BP); inside
+ * it group g starts at g*Wb*P, and row r of the block owns:
  *   B3: bytes 0..15 of the group at +r*16, bytes 16..25 plus the fp16 scale
  *       (little endian) at +Wb*16 + r*12;
- *   2B: bytes 0..15 at +r*16, bytes 16..31 at +Wb*16 + r*16, the fp16 scale
- *       at +Wb*32 + r*2.
+ *   2B, BP: bytes 0..15 at +r*16, bytes 16..31 at +Wb*16 + r*16, the fp16
+ *       scale at +Wb*32 + r*2.
  * So consecutive lanes (rows) read consecutive 16/12/2-byte pieces.  This is
  * the load-time re-tiling into consumption order that the Bonsai page
  * suggests ("后面还有没有优化空间": reorder codes and scales into the order
@@ -56,6 +56,14 @@
  *   2B (four 2-bit codes per byte, code d = t + 1, code 3 invalid):
  *       byte 4m + c, bits 2s..2s+1 hold k = 16m + 4s + c.
  *       2.125 bit per weight including the scale.
+ *   BP (two bit-planes, the compute-oriented layout the Bonsai page names
+ *       as a next step, "后面还有没有优化空间"): bytes 0..15 the nonzero
+ *       plane (1 when t != 0), bytes 16..31 the sign plane (1 when t = -1,
+ *       0 on zero trits; a sign on a zero trit is non-canonical); in both,
+ *       byte 4w + b, bit s holds k = 32w + 4s + b.  2.125 bit per weight.
+ *       Only the one-token paths take it (tq_gemv and
+ *       tq_gemv_gate_up_swiglu with M = 1, tq_gemv_quant, tq_decode_stack);
+ *       the others return TQ_ERR_FORMAT.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -79,7 +87,7 @@ typedef enum {
   TQ_ERR_HIP = -8     /* the HIP runtime refused a launch */
 } tq_status;
 
-typedef enum { TQ_FMT_B3 = 0, TQ_FMT_2B = 1 } tq_format;
+typedef enum { TQ_FMT_B3 = 0, TQ_FMT_2B = 1, TQ_FMT_BP = 2 } tq_format;
 typedef enum { TQ_F16 = 0, TQ_F32 = 1 } tq_dtype;
 
 #define TQ_GROUP 128

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 
 TQ_FMT_B3 = 0
 TQ_FMT_2B = 1
+TQ_FMT_BP = 2
 TQ_F16 = 0
 TQ_F32 = 1
 GROUP = 128

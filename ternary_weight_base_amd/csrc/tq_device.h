@@ -170,4 +170,28 @@ __device__ __forceinline__ void tb_group(const uint32_t (&w)[9], const XS &x,
   for (int m = 0; m < MT; m++) S[m] = a1[m] + (a4[m] >> 2) + (a16[m] >> 4) - xsum[m];
 }
 
+// Integer core of one BP group (one activation row).  Word c of a plane
+// holds, in byte b bit s, k = 32c + 4s + b: masking bit s of every byte gives
+// four trits' worth of 2^s (bit 7 reads as -128), dotted with activation
+// word 8c + s into an accumulator per s.  With the nonzero plane z (w[0..3])
+// and the sign plane n (w[4..7]): sum t x = sum_z x - 2 sum_n x.
+template <typename XS>
+__device__ __forceinline__ int bp_group(const uint32_t (&w)[9], const XS &x) {
+  int az[8], an[8];
+#pragma unroll
+  for (int s = 0; s < 8; s++) az[s] = an[s] = 0;
+#pragma unroll
+  for (int c = 0; c < 4; c++)
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      const uint32_t m = 0x01010101u << s;
+      az[s] = sdot4(w[c] & m, x.get(0, 8 * c + s), az[s]);
+      an[s] = sdot4(w[4 + c] & m, x.get(0, 8 * c + s), an[s]);
+    }
+  int S = 0;
+#pragma unroll
+  for (int s = 0; s < 7; s++) S += (az[s] >> s) - 2 * (an[s] >> s);
+  return S - (az[7] >> 7) + 2 * (an[7] >> 7);  // bit 7 weighed -128
+}
+
 }  // namespace tqdev

@@ -37,7 +37,7 @@ static bool shape_ok(int64_t N, int64_t K) {
          K <= (int64_t)1 << 30;
 }
 
-static bool fmt_ok(int fmt) { return fmt == TQ_FMT_B3 || fmt == TQ_FMT_2B; }
+static bool fmt_ok(int fmt) { return fmt == TQ_FMT_B3 || fmt == TQ_FMT_2B || fmt == TQ_FMT_BP; }
 
 extern "C" size_t tq_packed_bytes(int fmt, int64_t N, int64_t K) {
   if (!fmt_ok(fmt) || !shape_ok(N, K)) return 0;
@@ -105,6 +105,32 @@ bool tb_decode(const uint8_t *in, int8_t *t) {
   return true;
 }
 
+// ---- BP group <-> 32 device bytes --------------------------------------
+// nonzero plane bytes 0..15, sign plane bytes 16..31; in each, byte 4w + b,
+// bit s holds k = 32w + 4s + b.
+void bp_encode(const int8_t *t, uint8_t *out) {
+  memset(out, 0, 32);
+  for (int w = 0; w < 4; w++)
+    for (int b = 0; b < 4; b++)
+      for (int s = 0; s < 8; s++) {
+        const int8_t v = t[32 * w + 4 * s + b];
+        if (v != 0) out[4 * w + b] |= (uint8_t)(1u << s);
+        if (v < 0) out[16 + 4 * w + b] |= (uint8_t)(1u << s);
+      }
+}
+
+bool bp_decode(const uint8_t *in, int8_t *t) {
+  for (int j = 0; j < 16; j++)
+    if (in[16 + j] & ~in[j]) return false;  // a sign on a zero trit
+  for (int w = 0; w < 4; w++)
+    for (int b = 0; b < 4; b++)
+      for (int s = 0; s < 8; s++) {
+        const int nz = (in[4 * w + b] >> s) & 1, neg = (in[16 + 4 * w + b] >> s) & 1;
+        t[32 * w + 4 * s + b] = (int8_t)(nz ? (neg ? -1 : 1) : 0);
+      }
+  return true;
+}
+
 // Byte addresses of the pieces of (block b, group g, row r).
 struct Pieces {
   int64_t a, b, s;  // first piece, second piece, scale
@@ -152,7 +178,8 @@ extern "C" int tq_pack(int fmt, int64_t N, int64_t K, const int8_t *trits,
           memcpy(out + p.a, buf, 16);
           memcpy(out + p.b, buf + 16, 10);
         } else {
-          tb_encode(t, buf);
+          if (fmt == TQ_FMT_2B) tb_encode(t, buf);
+          else bp_encode(t, buf);
           memcpy(out + p.a, buf, 16);
           memcpy(out + p.b, buf + 16, 16);
         }
@@ -189,7 +216,7 @@ extern "C" int tq_unpack(int fmt, int64_t N, int64_t K, const void *src, size_t 
         } else {
           memcpy(buf, in + p.a, 16);
           memcpy(buf + 16, in + p.b, 16);
-          ok = tb_decode(buf, t);
+          ok = fmt == TQ_FMT_2B ? tb_decode(buf, t) : bp_decode(buf, t);
         }
         uint16_t s = (uint16_t)(in[p.s] | (in[p.s + 1] << 8));
         if (!ok) {

@@ -634,8 +634,10 @@ int gemv_common(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const 
                 const int8_t *q, const float *a, float *out, int32_t *sums, void *ws,
                 size_t ws_bytes, void *stream, int nmat) {
   if (!W0 || !q || (!sums && (!a || !out)) || (nmat == 2 && !W1)) return TQ_ERR_NULL;
-  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
+  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B && fmt != TQ_FMT_BP) return TQ_ERR_FORMAT;
   if (!shape_ok(N, K) || M < 1 || M > TQ_GEMV_MAX_M) return TQ_ERR_SHAPE;
+  // BP runs on the one-token projection kernel only
+  if (fmt == TQ_FMT_BP && (sums || M != 1 || !tq_internal_proj_fits(N, K))) return TQ_ERR_FORMAT;
   if (!aligned16(W0) || (W1 && !aligned16(W1)) || !aligned16(q) || (a && !aligned4(a)) ||
       (out && !aligned4(out)) || (sums && !aligned4(sums)))
     return TQ_ERR_ALIGN;
@@ -684,7 +686,8 @@ extern "C" int tq_quant_act(int dtype, int64_t M, int64_t K, const void *x, int8
 }
 
 extern "C" size_t tq_gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
-  if ((fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) || !shape_ok(N, K) || M < 1 || M > TQ_GEMV_MAX_M)
+  if ((fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B && fmt != TQ_FMT_BP) || !shape_ok(N, K) || M < 1 ||
+      M > TQ_GEMV_MAX_M || (fmt == TQ_FMT_BP && (M != 1 || !tq_internal_proj_fits(N, K))))
     return 0;
   // covers both tq_gemv and the fused gate/up call (two partial planes)
   if (TQ_GEMV1_PROJ && M == 1 && tq_internal_proj_fits(N, K)) {

@@ -66,5 +66,6 @@ struct Plan {
 // in_kind one of InKind).  Returns a tq_status.
 int launch_b3(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st);
 int launch_2b(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st);
+int launch_bp(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st);
 
 }  // namespace tqproj

@@ -88,7 +88,8 @@ int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, i
   A.C = p.C;
   A.W = p.W;
   A.I = p.I;
-  return fmt == TQ_FMT_B3 ? launch_b3(p, A, nmat, in_kind, st) : launch_2b(p, A, nmat, in_kind, st);
+  if (fmt == TQ_FMT_B3) return launch_b3(p, A, nmat, in_kind, st);
+  return fmt == TQ_FMT_2B ? launch_2b(p, A, nmat, in_kind, st) : launch_bp(p, A, nmat, in_kind, st);
 }
 
 size_t proj_ws_bytes(int fmt, int64_t N, int64_t K, int nmat) {
@@ -97,6 +98,8 @@ size_t proj_ws_bytes(int fmt, int64_t N, int64_t K, int nmat) {
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+// The one-token projection takes all three packed formats.
+bool fmt_ok(int fmt) { return fmt == TQ_FMT_B3 || fmt == TQ_FMT_2B || fmt == TQ_FMT_BP; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 bool shape_ok(int64_t N, int64_t K) {
   return N >= 1 && K >= tq::kGroup && K % tq::kGroup == 0 && N <= ((int64_t)1 << 24) &&
@@ -155,7 +158,7 @@ int tq_internal_proj_int8(int fmt, int64_t N, int64_t K, const void *W0, const v
 // C ABI: fused one-token projection
 // ---------------------------------------------------------------------
 extern "C" size_t tq_gemv_quant_workspace_bytes(int fmt, int64_t N, int64_t K, int gate_up) {
-  if ((fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) || !shape_ok(N, K)) return 0;
+  if (!fmt_ok(fmt) || !shape_ok(N, K)) return 0;
   return proj_ws_bytes(fmt, N, K, gate_up ? 2 : 1);
 }
 
@@ -164,7 +167,7 @@ extern "C" int tq_gemv_quant(int fmt, int64_t N, int64_t K, const void *W, const
                              float *y, float *y_bmax, const int8_t *y_signs, void *ws,
                              size_t ws_bytes, void *stream) {
   if (!W || !x || !y || (x_dtype == TQ_F32 && !x_bmax)) return TQ_ERR_NULL;
-  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
+  if (!fmt_ok(fmt)) return TQ_ERR_FORMAT;
   if (x_dtype != TQ_F16 && x_dtype != TQ_F32) return TQ_ERR_DTYPE;
   if (!shape_ok(N, K) || (x_dtype == TQ_F32 && x_nb != K / 64)) return TQ_ERR_SHAPE;
   if (y_signs && (Wu || N % 64 != 0)) return TQ_ERR_SHAPE;
@@ -188,7 +191,7 @@ extern "C" int tq_gemv_quant(int fmt, int64_t N, int64_t K, const void *W, const
 // ---------------------------------------------------------------------
 extern "C" size_t tq_decode_stack_workspace_bytes(int fmt, int64_t layers, int64_t hidden,
                                                   int64_t inter, int64_t qkv_out, int64_t o_in) {
-  if ((fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) || layers < 1 || !shape_ok(qkv_out, hidden) ||
+  if (!fmt_ok(fmt) || layers < 1 || !shape_ok(qkv_out, hidden) ||
       !shape_ok(hidden, o_in) || !shape_ok(inter, hidden) || !shape_ok(hidden, inter))
     return 0;
   return stack_ws(fmt, hidden, inter, qkv_out, o_in).total;
@@ -200,7 +203,7 @@ extern "C" int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t 
                                float *h, float *y_out, const int8_t *ffn_signs, void *ws,
                                size_t ws_bytes, void *stream) {
   if (!weights || !x_in || !a_in || !y_qkv || !y_o || !h || !y_out || !ws) return TQ_ERR_NULL;
-  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B) return TQ_ERR_FORMAT;
+  if (!fmt_ok(fmt)) return TQ_ERR_FORMAT;
   const size_t need = tq_decode_stack_workspace_bytes(fmt, layers, hidden, inter, qkv_out, o_in);
   if (need == 0) return TQ_ERR_SHAPE;
   if (ws_bytes < need) return TQ_ERR_SIZE;

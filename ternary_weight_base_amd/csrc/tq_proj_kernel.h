@@ -317,8 +317,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         const uint32_t w[9] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2],
                                wd[mat][i][3], wd[mat][i][4], wd[mat][i][5],
                                wd[mat][i][6], wd[mat][i][7], wd[mat][i][8]};
-        const int xs[1] = {xsum[i]};
-        tb_group<1>(w, xa, xs, S);
+        if constexpr (FMT == 1) {
+          const int xs[1] = {xsum[i]};
+          tb_group<1>(w, xa, xs, S);
+        } else {
+          S[0] = bp_group(w, xa);
+        }
         sc = half_bits(wd[mat][i][8]);
       }
       const float s = live ? sc : 0.0f;

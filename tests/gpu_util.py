@@ -6,8 +6,8 @@ import numpy as np
 
 import synth
 
-B3, TB = 0, 1
-FMTS = {B3: "b3", TB: "2b"}
+B3, TB, BP = 0, 1, 2
+FMTS = {B3: "b3", TB: "2b", BP: "bp"}
 
 
 def say(*a):

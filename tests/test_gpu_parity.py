@@ -148,6 +148,36 @@ def test_gemv_vs_oracle(fmt, M, N, K):
         assert not ws[:nb].any().item()
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 65, 384), (1, 1024, 1024), (1, 10240, 5120),
+                                   (1, 5120, 8192), (1, 5120, 17408)])
+def test_gemv_bp_one_token(M, N, K):
+    """The bit-plane layout on the one-token projection kernel."""
+    say(f"gemv bp N={N} K={K}")
+    BP = _tq().TQ_FMT_BP
+    t, s = weights(N, K, 4300 + N + K)
+    q, a = _quant_gpu(acts_f16(M, K, 4400 + K))
+    W = upload_blob(BP, t, s)
+    y, _ = _gemv_gpu(BP, M, N, K, W, q, a)
+    assert_close(y, oracle.gemv(t, s, q.cpu().numpy(), a.cpu().numpy()), f"gemv bp {N}x{K}")
+
+
+@pytest.mark.parametrize("N,K", [(17408, 5120), (130, 640)])
+def test_gate_up_swiglu_bp_one_token(N, K):
+    say(f"swiglu bp N={N} K={K}")
+    tq = _tq()
+    BP = tq.TQ_FMT_BP
+    tg, sg = weights(N, K, 4500 + N)
+    tu, su = weights(N, K, 4501 + N)
+    q, a = _quant_gpu(acts_f16(1, K, 4600))
+    qn, an = q.cpu().numpy(), a.cpu().numpy()
+    h = torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda")
+    tq.tq_gemv_gate_up_swiglu(BP, 1, N, K, upload_blob(BP, tg, sg), upload_blob(BP, tu, su), q, a, h,
+                              tq.workspace(BP, 1, N, K))
+    torch.cuda.synchronize()
+    ref = oracle.swiglu(oracle.gemv(tg, sg, qn, an), oracle.gemv(tu, su, qn, an))
+    assert_close(h.cpu().numpy(), ref, "swiglu bp")
+
+
 def test_gemv_zero_weights_and_zero_activations():
     tq = _tq()
     N, K = 70, 512

@@ -13,7 +13,7 @@ import synth
 import ternary_weight_base_amd as tq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-B3, TB = tq.TQ_FMT_B3, tq.TQ_FMT_2B
+B3, TB, BP = tq.TQ_FMT_B3, tq.TQ_FMT_2B, tq.TQ_FMT_BP
 
 
 def _header_functions():
@@ -41,7 +41,7 @@ def _rand(N, K, seed):
     return synth.trits(synth.seed(seed, 1), N, K), synth.scales(synth.seed(seed, 2), N, K)
 
 
-@pytest.mark.parametrize("fmt", [B3, TB])
+@pytest.mark.parametrize("fmt", [B3, TB, BP])
 @pytest.mark.parametrize("N,K", [(1, 128), (3, 256), (64, 1024), (65, 384), (130, 640), (200, 128)])
 def test_pack_roundtrip_and_size(fmt, N, K):
     t, s = _rand(N, K, N * 7 + K)
@@ -94,6 +94,18 @@ def _decode_b3_doc(body):
     return t
 
 
+def _decode_bp_doc(body):
+    """Byte 4w + b, bit s of each plane is k = 32w + 4s + b (include/tq.h)."""
+    t = np.full(128, 99, dtype=np.int64)
+    for j in range(16):
+        w, b = divmod(j, 4)
+        for s in range(8):
+            nz, neg = (int(body[j]) >> s) & 1, (int(body[16 + j]) >> s) & 1
+            assert not (neg and not nz)
+            t[32 * w + 4 * s + b] = (-1 if neg else 1) if nz else 0
+    return t
+
+
 def _decode_2b_doc(body):
     t = np.full(128, 99, dtype=np.int64)
     for byte_idx, v in enumerate(body):
@@ -105,7 +117,7 @@ def _decode_2b_doc(body):
     return t
 
 
-@pytest.mark.parametrize("fmt", [B3, TB])
+@pytest.mark.parametrize("fmt", [B3, TB, BP])
 def test_pack_matches_documented_layout(fmt):
     N, K = 70, 384
     t, s = _rand(N, K, 5 + fmt)
@@ -113,7 +125,7 @@ def test_pack_matches_documented_layout(fmt):
     for n in (0, 1, 63, 64, 69):
         for g in range(K // 128):
             body, sc = _device_group_bytes(fmt, blob, N, K, n, g)
-            dec = _decode_b3_doc(body) if fmt == B3 else _decode_2b_doc(body)
+            dec = {B3: _decode_b3_doc, TB: _decode_2b_doc, BP: _decode_bp_doc}[fmt](body)
             assert np.array_equal(dec, t[n, 128 * g: 128 * g + 128]), (n, g)
             assert sc == s[n, g]
 
@@ -121,7 +133,7 @@ def test_pack_matches_documented_layout(fmt):
 def test_pack_same_information_as_oracle_canonical():
     N, K = 33, 512
     t, s = _rand(N, K, 77)
-    for fmt in (B3, TB):
+    for fmt in (B3, TB, BP):
         rc, t1, s1 = oracle.unpack(fmt, oracle.pack(fmt, t, s), N, K)
         t2, s2 = tq.tq_unpack(fmt, tq.tq_pack(fmt, t, s), N, K)
         assert rc == 0 and np.array_equal(t1, t2) and np.array_equal(s1, s2)
@@ -165,6 +177,13 @@ def test_unpack_rejects_noncanonical():
     bad[3] = 0xFF
     with pytest.raises(tq.TQError):
         tq.tq_unpack(TB, bad, N, K)
+    # BP: a sign bit on a zero trit (row 0, group 0: nonzero byte 2 at 2, sign byte at 8*16 + 2)
+    blobp = tq.tq_pack(BP, np.zeros((N, K), np.int8), s)
+    badp = blobp.copy()
+    badp[8 * 16 + 2] = 0x10
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_unpack(BP, badp, N, K)
+    assert e.value.status == -5
     # non-finite scale
     bad = blob.copy()
     bad[8 * 16 + 1 * 12 + 11] = 0x7C
@@ -227,6 +246,12 @@ def test_device_entry_points_validate_on_host():
                                     need - 1, None) == -7
     assert L.tq_gemv(B3, 1, 5120, 17408, FAKE, FAKE, FAKE, FAKE, MIS, need, None) == -3
     assert L.tq_gemv_gate_up_swiglu(B3, 1, 64, 128, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == -1
+    # BP runs on the one-token kernel only
+    assert L.tq_gemv(BP, 2, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
+    assert L.tq_gemm(BP, 512, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
+    assert L.tq_debug_unpack(BP, 64, 128, FAKE, FAKE, None) == -5
+    assert tq.tq_gemv_workspace_bytes(BP, 2, 5120, 8192) == 0
+    assert tq.tq_gemv_workspace_bytes(BP, 1, 5120, 8192) > 0
     # gemm
     assert L.tq_gemm(B3, 0, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
     assert L.tq_gemm(B3, 512, 64, 96, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
