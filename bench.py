@@ -242,6 +242,29 @@ def main():
     # ---- the other rows of the hot path, measured on the same weights -------
     extras = measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time_graph)
 
+    # ---- layout A/B: the same stack, inputs and seeds in each packed layout
+    if extras is not None:
+        names = {tq.TQ_FMT_B3: "b3", tq.TQ_FMT_2B: "2b", tq.TQ_FMT_BP: "bp"}
+        ab = {names[fmt]: {"tok_s": round(tok_s, 2), "weight_bytes_per_token": stack.step_weight_bytes}}
+        for other in (tq.TQ_FMT_B3, tq.TQ_FMT_2B, tq.TQ_FMT_BP):
+            if other == fmt:
+                continue
+            st2 = Stack(tq, synth, torch, other, L)
+            lay2 = tq.stack_layers([(st2.W["qkv"][l], st2.W["o"][l], st2.W["gate"][l], st2.W["up"][l],
+                                     st2.W["down"][l]) for l in range(L)])
+            nb2 = tq.tq_decode_stack_workspace_bytes(other, L, HIDDEN, INTER, QKV_OUT, O_IN)
+            ws2 = torch.zeros((nb2 + 15) // 16 * 4, dtype=torch.int32, device=dev)
+
+            def token2():
+                tq.tq_decode_stack(other, L, HIDDEN, INTER, QKV_OUT, O_IN, lay2, x_in, a_in,
+                                   y_qkv, y_o, h, y_dn, ws2)
+            ms2 = time_graph(capture(token2), max(3, args.steps // 2), 2)
+            ab[names[other]] = {"tok_s": round(1000.0 / ms2, 2),
+                                "weight_bytes_per_token": st2.step_weight_bytes}
+            del st2, lay2, ws2
+            torch.cuda.empty_cache()
+        extras["layout_ab"] = ab
+
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     cpu = cpu_baseline(synth, args.cpu_seconds, args.fmt) if args.cpu_seconds > 0 else None
 
@@ -329,7 +352,8 @@ def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time
     - small-batch decode (M tokens per step through the whole stack:
       tq_quant_act + tq_gemv per projection, 8 launches a layer);
     - ternarize_host: the host ternariser on one fp32 gate matrix
-      (17408 x 5120, 356 MB), the load-time step before tq_pack."""
+      (17408 x 5120, 356 MB), the load-time step before tq_pack.
+    (main() adds layout_ab: the decode stack in each packed layout.)"""
     if args.no_extras:
         return None
     dev = "cuda"
