@@ -233,11 +233,24 @@ def main():
             tr = json.load(f)
         if tr.get("kernel_source_sha") == kernel_source_sha() and tr.get("fmt") == args.fmt:
             traffic = tr.get("hbm_bytes_per_launch")
+    # ---- measured HBM read ceiling: a plain streaming read of 2 GiB (beyond
+    # the 256 MB MALL), beside which the byte rates above are also reported
+    rd = torch.ones(1 << 29, dtype=torch.int32, device=dev)
+    rd_sink = torch.empty(tq.TQ_STREAM_READ_WGS, dtype=torch.int32, device=dev)
+    rd_ms = time_graph(capture(lambda: tq.tq_debug_stream_read(rd, rd_sink)), 10, 2)
+    read_gbps = rd.numel() * 4 / (rd_ms * 1e-3) / 1e9
+    read_ceiling = {"GBps": round(read_gbps, 1), "bytes": rd.numel() * 4,
+                    "frac_of_8TBps": round(read_gbps / PEAK_HBM_GBPS, 4),
+                    "kernel": "tq_debug_stream_read (8192 workgroups x 256 threads, 16-byte "
+                              "nontemporal loads, 8 in flight per thread)"}
+    del rd, rd_sink
+    torch.cuda.empty_cache()
     roofline = {"bound": "hbm", "achieved": round(gu_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(gu_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
                 "kernel": "proj_kernel<fmt,2,fp32 input> (fused quantise + gate/up/SwiGLU, "
                           "2 x 17408x5120), as launched by the stack",
-                "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3)}
+                "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3),
+                "frac_of_measured_read_ceiling": round(gu_gbps / read_gbps, 4)}
 
     # ---- the other rows of the hot path, measured on the same weights -------
     extras = measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time_graph)
@@ -287,6 +300,8 @@ def main():
                    "weight_bytes_per_token": stack.step_weight_bytes},
         "weight_stream_GBps": round(stream_gbps, 1),
         "weight_stream_frac_of_8TBps": round(stream_gbps / PEAK_HBM_GBPS, 4),
+        "weight_stream_frac_of_measured_read_ceiling": round(stream_gbps / read_gbps, 4),
+        "hbm_read_ceiling": read_ceiling,
         "separate_launch_tok_s": round(1000.0 / sep_ms, 2),
         "ffn_hadamard_tok_s": round(1000.0 / rot_ms, 2),
         "roofline": roofline,

@@ -93,6 +93,7 @@ typedef enum { TQ_F16 = 0, TQ_F32 = 1 } tq_dtype;
 #define TQ_GROUP 128
 #define TQ_BLOCK_ROWS 64
 #define TQ_GEMV_MAX_M 16
+#define TQ_STREAM_READ_WGS 8192 /* workgroups (and sink words) of tq_debug_stream_read */
 
 /* Human-readable name of a status code (static string). */
 const char *tq_status_str(int status);
@@ -278,6 +279,19 @@ int tq_debug_unpack(int fmt, int64_t N, int64_t K, const void *W, int8_t *trits,
  * computes them before scaling. */
 int tq_debug_group_sums(int fmt, int64_t M, int64_t N, int64_t K, const void *W,
                         const int8_t *q, int32_t *S, int use_gemm_path, void *stream);
+
+/* ---- device: measurement hook ----------------------------------------- */
+
+/* A plain streaming read of `bytes` bytes at src (device, 16-byte aligned,
+ * bytes % 16 == 0): the HBM read rate that the projection kernels' byte
+ * rates are compared with, beside the published peak.  Workgroup w of
+ * TQ_STREAM_READ_WGS reads one contiguous chunk once and writes the XOR of
+ * its 32-bit words to sink[w] (0 for an empty chunk), so the XOR of all
+ * sink words equals the XOR of the buffer's words.  sink: device uint32,
+ * sink_words >= TQ_STREAM_READ_WGS (TQ_ERR_SIZE otherwise), 4-byte
+ * aligned. */
+int tq_debug_stream_read(const void *src, size_t bytes, uint32_t *sink, int64_t sink_words,
+                         void *stream);
 
 #ifdef __cplusplus
 }

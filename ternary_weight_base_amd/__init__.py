@@ -22,6 +22,7 @@ TQ_FMT_2B = 1
 TQ_FMT_BP = 2
 TQ_F16 = 0
 TQ_F32 = 1
+TQ_STREAM_READ_WGS = 8192
 GROUP = 128
 GEMV_MAX_M = 16
 
@@ -34,7 +35,7 @@ EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant
            "tq_gemm_workspace_bytes", "tq_gemm", "tq_debug_unpack", "tq_debug_group_sums",
            "tq_gemv_quant_workspace_bytes", "tq_gemv_quant",
            "tq_decode_stack_workspace_bytes", "tq_decode_stack", "tq_hadamard_quant_act",
-           "tq_ternarize")
+           "tq_ternarize", "tq_debug_stream_read")
 
 
 class TqLayer(ctypes.Structure):
@@ -73,6 +74,7 @@ def _load():
         "tq_decode_stack": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
         "tq_hadamard_quant_act": ([I, I64, I64, P, P, P, P, P], I),
         "tq_ternarize": ([I64, I64, P, P, P], I),
+        "tq_debug_stream_read": ([P, SZ, P, I64, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -206,6 +208,14 @@ def tq_debug_unpack(fmt, N, K, W, trits, stream=None) -> None:
 def tq_debug_group_sums(fmt, M, N, K, W, q, S, use_gemm_path=False, stream=None) -> None:
     _check(lib.tq_debug_group_sums(fmt, M, N, K, _ptr(W), _ptr(q), _ptr(S), int(use_gemm_path),
                                    _stream(stream)), "tq_debug_group_sums")
+
+
+def tq_debug_stream_read(src, sink, stream=None) -> None:
+    """Read every byte of src (device tensor, size a multiple of 16) once;
+    sink (int32/uint32 [>= TQ_STREAM_READ_WGS]) receives per-workgroup XORs."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib.tq_debug_stream_read(_ptr(src), nbytes, _ptr(sink), sink.numel(), _stream(stream)),
+           "tq_debug_stream_read")
 
 
 def tq_gemv_quant_workspace_bytes(fmt, N, K, gate_up=False) -> int:

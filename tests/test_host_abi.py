@@ -348,6 +348,18 @@ def test_hadamard_quant_validates_on_host():
     assert call(a=ODD) == -3
 
 
+def test_stream_read_validates_on_host():
+    L = tq.lib
+    W = tq.TQ_STREAM_READ_WGS
+    call = lambda src=FAKE, n=1 << 20, sink=FAKE, sw=W: L.tq_debug_stream_read(src, n, sink, sw, None)
+    assert call(src=None) == -1
+    assert call(sink=None) == -1
+    assert call(n=24) == -2
+    assert call(sw=W - 1) == -7
+    assert call(src=MIS) == -3
+    assert call(sink=ODD) == -3
+
+
 def test_workspace_sizes():
     assert tq.tq_gemv_workspace_bytes(B3, 1, 1024, 1024) == 0
     for N, K in ((5120, 8192), (5120, 17408), (10240, 5120)):
