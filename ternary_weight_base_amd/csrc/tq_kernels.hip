@@ -260,23 +260,23 @@ __global__ __launch_bounds__(512) void gemv_kernel(
     for (int i = 0; i < GS; i++) {
       const int gi = min(g0 + i, G - 1);
       const uint8_t *gb = Wm[mat] + L.group_base(b, gi);
-      const uint4 A = *reinterpret_cast<const uint4 *>(gb + lr * 16);
+      const uint4 A = ld_stream16(gb + lr * 16);
       wd[mat][i][0] = A.x;
       wd[mat][i][1] = A.y;
       wd[mat][i][2] = A.z;
       wd[mat][i][3] = A.w;
       if constexpr (FMT == 0) {
-        const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + lr * 12);
-        wd[mat][i][4] = pb[0];
-        wd[mat][i][5] = pb[1];
-        wd[mat][i][6] = pb[2];
+        const uint3 pb = ld_stream12(gb + Wb * 16 + lr * 12);
+        wd[mat][i][4] = pb.x;
+        wd[mat][i][5] = pb.y;
+        wd[mat][i][6] = pb.z;
       } else {
-        const uint4 B = *reinterpret_cast<const uint4 *>(gb + Wb * 16 + lr * 16);
+        const uint4 B = ld_stream16(gb + Wb * 16 + lr * 16);
         wd[mat][i][4] = B.x;
         wd[mat][i][5] = B.y;
         wd[mat][i][6] = B.z;
         wd[mat][i][7] = B.w;
-        wd[mat][i][8] = *reinterpret_cast<const uint16_t *>(gb + Wb * 32 + lr * 2);
+        wd[mat][i][8] = ld_stream2(gb + Wb * 32 + lr * 2);
       }
     }
   }

@@ -201,23 +201,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
     for (int mat = 0; mat < NMAT; mat++) {
       const uint8_t *gp = Wm[mat] + L.group_base(bi, gi);
-      const uint4 P = *reinterpret_cast<const uint4 *>(gp + lr * 16);
+      const uint4 P = ld_stream16(gp + lr * 16);
       wd[mat][i][0] = P.x;
       wd[mat][i][1] = P.y;
       wd[mat][i][2] = P.z;
       wd[mat][i][3] = P.w;
       if constexpr (FMT == 0) {
-        const uint32_t *pb = reinterpret_cast<const uint32_t *>(gp + Wb * 16 + lr * 12);
-        wd[mat][i][4] = pb[0];
-        wd[mat][i][5] = pb[1];
-        wd[mat][i][6] = pb[2];
+        const uint3 B = ld_stream12(gp + Wb * 16 + lr * 12);
+        wd[mat][i][4] = B.x;
+        wd[mat][i][5] = B.y;
+        wd[mat][i][6] = B.z;
       } else {
-        const uint4 Q = *reinterpret_cast<const uint4 *>(gp + Wb * 16 + lr * 16);
+        const uint4 Q = ld_stream16(gp + Wb * 16 + lr * 16);
         wd[mat][i][4] = Q.x;
         wd[mat][i][5] = Q.y;
         wd[mat][i][6] = Q.z;
         wd[mat][i][7] = Q.w;
-        wd[mat][i][8] = *reinterpret_cast<const uint16_t *>(gp + Wb * 32 + lr * 2);
+        wd[mat][i][8] = ld_stream2(gp + Wb * 32 + lr * 2);
       }
     }
   };
