@@ -169,8 +169,10 @@ int tq_hadamard_quant_act(int dtype, int64_t M, int64_t K, const void *x, const 
 /* Workspace bytes tq_gemv / tq_gemv_gate_up_swiglu need for this shape
  * (0 when the launch does not split K across workgroups).  The workspace
  * is device memory that must be zero-filled once before its first use;
- * every call leaves it zero-filled again.  Reusing one workspace for calls
- * that run concurrently on different streams is not allowed. */
+ * every call leaves it zero-filled again, so one workspace as large as the
+ * largest need serves calls of any shapes and entry points in stream
+ * order.  Reusing one workspace for calls that run concurrently on
+ * different streams is not allowed. */
 size_t tq_gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
 /* y[M][N] (fp32, device) from the packed blob W (device, tq_packed_bytes

@@ -269,6 +269,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
             accf[ms][ns][v] += __hip_atomic_load(src + ((ms * 4 + ns) * 4 + v) * 256, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     }
+    // consumed: leave the workspace zero for the next call, whatever its shape
+    for (int cc = 0; cc < C; cc++) {
+      float *dst = partials + ((size_t)cc * ntiles + tile) * 256 * 32 + tid;
+#pragma unroll
+      for (int k = 0; k < 32; k++)
+        __hip_atomic_store(dst + k * 256, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (tid == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 #pragma unroll

@@ -299,6 +299,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         tot[p][mat] = s;
       }
+    // consumed: leave the workspace zero for the next call, whatever its shape
+#pragma unroll
+    for (int p = 0; p < kPer; p++)
+#pragma unroll
+      for (int mat = 0; mat < NMAT; mat++)
+        for (int cc = 0; cc < A.C; cc++)
+          __hip_atomic_store(&part[(((size_t)cc * NMAT + mat) * L.NB + b) * 64 * kOut + tid + p * kThreads],
+                             0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) __hip_atomic_store(&A.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int rows = (int)L.valid_rows(b);

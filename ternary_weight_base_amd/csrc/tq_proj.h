@@ -39,9 +39,26 @@ enum InKind { kInInt8 = 0, kInF16 = 1, kInF32 = 2 };
 // per workgroup.  split == 0: block b is cut into C chunks of balanced group
 // counts (workgroup b * C + c).  split == 1: the items are cut into W equal
 // ranges, which may start and end inside blocks (at most three blocks per
-// range).  A block cut between workgroups ("pieces") is summed by the last
-// of them to finish, in workgroup order.
+// range).  The pieces of a block cut between workgroups meet in one of the
+// two ways below.
 constexpr int kMaxParts = 3;  // blocks touched by one workgroup's range
+constexpr int kMeetMaxC = 4;  // K chunks per block that still meet by exchange
+
+// Two ways for the pieces of a cut block to meet.
+//  - Counter (K chunks, any count): each piece stores its sums, waits for them
+//    to reach device scope and bumps the block's counter; the last piece to
+//    arrive loads the others and adds them in workgroup order.  Three
+//    dependent memory round trips after the last piece's own work.
+//  - Exchange (the equal split, where a cut block has two pieces; at most
+//    kMeetMaxC K chunks): the pieces meet pairwise along a fixed binary
+//    tree over the piece index.  At each tree node a lane swaps its row's
+//    sums (both matrices in one 64-bit word) into the node's slot; the
+//    piece that finds the other's sums there adds the two (fp32 addition
+//    commutes, so the result does not depend on which arrives first),
+//    empties the slot and carries on up; the other is done with that row.
+//    One round trip per tree level.  Rows can end up finished by different
+//    workgroups when two pieces arrive together; the block maximum then
+//    meets through an atomic maximum and a row count.
 
 struct ProjArgs {
   const uint8_t *W0, *W1;
@@ -51,15 +68,30 @@ struct ProjArgs {
   float *out_bmax;       // optional [NB]: max |out| over each 64-row block
   const int8_t *out_signs;  // optional [N] (one matrix, N % 64 == 0): out is rotated
                             // block by block, diag(s) H_64 / 8, before it is stored
-  float *partials;       // cut blocks: [C][nmat][N], or [workgroups][kMaxParts][nmat][64] (split)
-  uint32_t *counters;    // [NB] when a block is cut, zero on entry and on exit
+  float *partials;       // counter meet (K chunks): [C][nmat][N]
+  uint32_t *counters;    // counter meet: [NB], zero on entry and on exit
+  void *slots;           // exchange meet: [NB][stride][64] words (32-bit one matrix,
+                         // 64-bit gate/up), zero (empty) on entry and on exit
+  uint32_t *meet_max;    // exchange meet: [NB][2] (max bits, finished rows), zero
   int N, K, in_nb;
   int split, C, W, I;    // split mode, chunks per block, workgroups and items (mode 1)
+  int meet;              // 1: exchange meet, 0: counter meet
+  int slot_stride;       // exchange meet: tree nodes per block (pieces - 1)
 };
 
 struct Plan {
   int gs, split, C, W, NB, I, grid;
-  size_t counters_bytes, partials_bytes;
+  int cut;               // some block is cut between workgroups
+  int meet_ok;           // the exchange meet applies (needs no output rotation)
+  int slot_stride;
+  size_t counters_bytes, partials_bytes, meet_bytes, slots_bytes;
+};
+
+// Workspace sections.  Every section is zero on entry and left zero on
+// exit (the piece that consumes partial sums clears them), so launches of
+// any shapes can share one workspace in stream order.
+struct WsLayout {
+  size_t counters, meet, slots, partials, total;
 };
 
 // Launch the kernel of packed format B3 / 2B for this plan (nmat 1 or 2,

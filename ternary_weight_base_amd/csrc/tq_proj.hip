@@ -55,19 +55,43 @@ Plan plan_proj(int fmt, int64_t N, int64_t K, int nmat) {
     p.gs = (int)gs;
   }
   const bool cut = p.split == 1 || p.C > 1;
-  p.counters_bytes = cut ? round256((size_t)NB * 4) : 0;
-  p.partials_bytes = !cut ? 0
-                     : p.split ? round256((size_t)p.grid * kMaxParts * nmat * 64 * 4)
-                               : round256((size_t)p.C * nmat * N * 4);
+  p.cut = cut;
+  // exchange meet: at most two pieces per block (every equal range holds
+  // at least one block's worth of items), or at most kMeetMaxC K chunks
+  // (the equal split has I / W > G items per range: always two pieces)
+  p.meet_ok = cut && (p.split ? I / p.W >= G : p.C <= kMeetMaxC);
+  p.slot_stride = !p.meet_ok ? 0 : p.split ? 1 : p.C - 1;
+  const bool counter = cut && !p.split;  // the rotated output needs the counter meet
+  p.counters_bytes = counter ? round256((size_t)NB * 4) : 0;
+  p.partials_bytes = counter ? round256((size_t)p.C * nmat * N * 4) : 0;
+  p.meet_bytes = p.meet_ok ? round256((size_t)NB * 8) : 0;
+  p.slots_bytes = p.meet_ok ? round256((size_t)NB * p.slot_stride * 64 * 4 * nmat) : 0;
   return p;
 }
 
-// One projection.  Split-K counters at `counters` (zero on entry, left
-// zero), partial sums at `partials`; the two areas must not overlap, also
-// across the launches of one stream that share them.
+// Sections big enough for every plan given, at fixed offsets.
+WsLayout ws_layout(const Plan *ps, int n) {
+  WsLayout w{0, 0, 0, 0, 0};
+  size_t cb = 0, mb = 0, sb = 0, pb = 0;
+  for (int i = 0; i < n; i++) {
+    if (ps[i].counters_bytes > cb) cb = ps[i].counters_bytes;
+    if (ps[i].meet_bytes > mb) mb = ps[i].meet_bytes;
+    if (ps[i].slots_bytes > sb) sb = ps[i].slots_bytes;
+    if (ps[i].partials_bytes > pb) pb = ps[i].partials_bytes;
+  }
+  w.counters = 0;
+  w.meet = cb;
+  w.slots = cb + mb;
+  w.partials = cb + mb + sb;
+  w.total = cb + mb + sb + pb;
+  return w;
+}
+
+// One projection, its cut blocks meeting through the workspace at `ws`
+// laid out as `w` (zero on entry, left zero).
 int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, int in_kind,
                 const void *in, const float *in_aux, int in_nb, float *out, float *out_bmax,
-                char *counters, char *partials, hipStream_t st, const int8_t *out_signs = nullptr) {
+                char *ws, const WsLayout &w, hipStream_t st, const int8_t *out_signs = nullptr) {
   const int nmat = W1 ? 2 : 1;
   const Plan p = plan_proj(fmt, N, K, nmat);
   ProjArgs A;
@@ -78,9 +102,15 @@ int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, i
   A.out = out;
   A.out_bmax = out_bmax;
   A.out_signs = out_signs;
-  const bool cut = p.split == 1 || p.C > 1;
-  A.counters = cut ? reinterpret_cast<uint32_t *>(counters) : nullptr;
-  A.partials = cut ? reinterpret_cast<float *>(partials) : nullptr;
+  // the output rotation needs the whole block in one wave: counter meet
+  // (never with the equal split, which is for gate/up only)
+  if (p.split && (!p.meet_ok || out_signs)) return TQ_ERR_SHAPE;
+  A.meet = p.meet_ok && !out_signs;
+  A.slot_stride = p.slot_stride;
+  A.counters = p.cut ? reinterpret_cast<uint32_t *>(ws + w.counters) : nullptr;
+  A.partials = p.cut ? reinterpret_cast<float *>(ws + w.partials) : nullptr;
+  A.meet_max = A.meet ? reinterpret_cast<uint32_t *>(ws + w.meet) : nullptr;
+  A.slots = A.meet ? (void *)(ws + w.slots) : nullptr;
   A.N = (int)N;
   A.K = (int)K;
   A.in_nb = in_nb;
@@ -92,10 +122,12 @@ int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, i
   return fmt == TQ_FMT_2B ? launch_2b(p, A, nmat, in_kind, st) : launch_bp(p, A, nmat, in_kind, st);
 }
 
-size_t proj_ws_bytes(int fmt, int64_t N, int64_t K, int nmat) {
+WsLayout proj_ws(int fmt, int64_t N, int64_t K, int nmat) {
   const Plan p = plan_proj(fmt, N, K, nmat);
-  return p.counters_bytes + p.partials_bytes;
+  return ws_layout(&p, 1);
 }
+
+size_t proj_ws_bytes(int fmt, int64_t N, int64_t K, int nmat) { return proj_ws(fmt, N, K, nmat).total; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // The one-token projection takes all three packed formats.
@@ -106,24 +138,20 @@ bool shape_ok(int64_t N, int64_t K) {
          K <= ((int64_t)1 << 20);
 }
 
-// Decode-stack workspace: one counters area (every launch leaves it zero),
-// one partial-sum area (each launch's sums are consumed before the next
-// launch starts), then the block maxima of y_o and of h.
+// Decode-stack workspace: the meet sections shared by the four launches of
+// every layer (each launch leaves them zero), then the block maxima of y_o
+// and of h.
 struct StackWs {
-  size_t partials, bmax_o, bmax_h, total;
+  WsLayout meet;
+  size_t bmax_o, bmax_h, total;
 };
 
 StackWs stack_ws(int fmt, int64_t hidden, int64_t inter, int64_t qkv_out, int64_t o_in) {
   const Plan ps[4] = {plan_proj(fmt, qkv_out, hidden, 1), plan_proj(fmt, hidden, o_in, 1),
                       plan_proj(fmt, inter, hidden, 2), plan_proj(fmt, hidden, inter, 1)};
-  size_t cb = 0, pb = 0;
-  for (const Plan &p : ps) {
-    if (p.counters_bytes > cb) cb = p.counters_bytes;
-    if (p.partials_bytes > pb) pb = p.partials_bytes;
-  }
   StackWs w;
-  w.partials = cb;
-  w.bmax_o = cb + pb;
+  w.meet = ws_layout(ps, 4);
+  w.bmax_o = w.meet.total;
   w.bmax_h = w.bmax_o + round256((size_t)Layout(fmt, hidden, o_in).NB * 4);
   w.total = w.bmax_h + round256((size_t)Layout(fmt, inter, hidden).NB * 4);
   return w;
@@ -143,15 +171,13 @@ size_t tq_internal_proj_ws_bytes(int fmt, int64_t N, int64_t K, int nmat) {
 int tq_internal_proj_int8(int fmt, int64_t N, int64_t K, const void *W0, const void *W1,
                           const int8_t *q, const float *a_scale, float *y, void *ws,
                           size_t ws_bytes, hipStream_t st) {
-  const size_t need = proj_ws_bytes(fmt, N, K, W1 ? 2 : 1);
-  if (need > 0) {
+  const WsLayout w = proj_ws(fmt, N, K, W1 ? 2 : 1);
+  if (w.total > 0) {
     if (!ws) return TQ_ERR_NULL;
     if (!aligned16(ws)) return TQ_ERR_ALIGN;
-    if (ws_bytes < need) return TQ_ERR_SIZE;
+    if (ws_bytes < w.total) return TQ_ERR_SIZE;
   }
-  const Plan p = plan_proj(fmt, N, K, W1 ? 2 : 1);
-  return launch_proj(fmt, N, K, W0, W1, kInInt8, q, a_scale, 0, y, nullptr, (char *)ws,
-                     (char *)ws + p.counters_bytes, st);
+  return launch_proj(fmt, N, K, W0, W1, kInInt8, q, a_scale, 0, y, nullptr, (char *)ws, w, st);
 }
 
 // ---------------------------------------------------------------------
@@ -174,16 +200,14 @@ extern "C" int tq_gemv_quant(int fmt, int64_t N, int64_t K, const void *W, const
   if (!aligned16(W) || (Wu && !aligned16(Wu)) || !aligned16(x) || !aligned4(y) ||
       (x_bmax && !aligned4(x_bmax)) || (y_bmax && !aligned4(y_bmax)))
     return TQ_ERR_ALIGN;
-  const int nmat = Wu ? 2 : 1;
-  const Plan p = plan_proj(fmt, N, K, nmat);
-  if (p.counters_bytes + p.partials_bytes > 0) {
+  const WsLayout w = proj_ws(fmt, N, K, Wu ? 2 : 1);
+  if (w.total > 0) {
     if (!ws) return TQ_ERR_NULL;
     if (!aligned16(ws)) return TQ_ERR_ALIGN;
-    if (ws_bytes < p.counters_bytes + p.partials_bytes) return TQ_ERR_SIZE;
+    if (ws_bytes < w.total) return TQ_ERR_SIZE;
   }
   return launch_proj(fmt, N, K, W, Wu, x_dtype == TQ_F16 ? kInF16 : kInF32, x, x_bmax, (int)x_nb,
-                     y, y_bmax, (char *)ws, (char *)ws + p.counters_bytes, (hipStream_t)stream,
-                     y_signs);
+                     y, y_bmax, (char *)ws, w, (hipStream_t)stream, y_signs);
 }
 
 // ---------------------------------------------------------------------
@@ -218,7 +242,7 @@ extern "C" int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t 
       !aligned16(h) || !aligned4(y_qkv) || !aligned4(y_out))
     return TQ_ERR_ALIGN;
   const StackWs w = stack_ws(fmt, hidden, inter, qkv_out, o_in);
-  char *base = (char *)ws, *parts = base + w.partials;
+  char *base = (char *)ws;
   float *bmax_o = reinterpret_cast<float *>(base + w.bmax_o);
   float *bmax_h = reinterpret_cast<float *>(base + w.bmax_h);
   const int nb_o = (int)Layout(fmt, hidden, o_in).NB, nb_h = (int)Layout(fmt, inter, hidden).NB;
@@ -229,17 +253,17 @@ extern "C" int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t 
     const tq_layer &Lw = weights[l];
     float *yo = y_o + l * hidden, *hl = h + l * inter;
     if ((rc = launch_proj(fmt, qkv_out, hidden, Lw.qkv, nullptr, kInF16, x16 + l * hidden, nullptr,
-                          0, y_qkv + l * qkv_out, nullptr, base, parts, st)) != TQ_OK)
+                          0, y_qkv + l * qkv_out, nullptr, base, w.meet, st)) != TQ_OK)
       return rc;
     if ((rc = launch_proj(fmt, hidden, o_in, Lw.o, nullptr, kInF16, a16 + l * o_in, nullptr, 0, yo,
-                          bmax_o, base, parts, st, ffn_signs ? ffn_signs + l * hidden : nullptr)) !=
+                          bmax_o, base, w.meet, st, ffn_signs ? ffn_signs + l * hidden : nullptr)) !=
         TQ_OK)
       return rc;
     if ((rc = launch_proj(fmt, inter, hidden, Lw.gate, Lw.up, kInF32, yo, bmax_o, nb_o, hl, bmax_h,
-                          base, parts, st)) != TQ_OK)
+                          base, w.meet, st)) != TQ_OK)
       return rc;
     if ((rc = launch_proj(fmt, hidden, inter, Lw.down, nullptr, kInF32, hl, bmax_h, nb_h,
-                          y_out + l * hidden, nullptr, base, parts, st)) != TQ_OK)
+                          y_out + l * hidden, nullptr, base, w.meet, st)) != TQ_OK)
       return rc;
   }
   return TQ_OK;

@@ -28,12 +28,15 @@
 // Issuing everything at once stalls each wave on a full memory queue until
 // most of its data has arrived, so decode would only start after the whole
 // transfer; the D-deep pipeline lets decode run while later groups stream.
-// The waves' partial sums meet in LDS; with several K chunks per block, the
-// last chunk to finish (agent-scope counter) adds the partials in chunk
-// order, so results do not depend on timing.
+// The waves' partial sums meet in LDS; the pieces of a block cut between
+// workgroups then meet through the workspace (by exchange along a fixed
+// tree, or through a counter: tq_proj.h), so results do not depend on
+// timing.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "tq.h"
 #include "tq_device.h"
@@ -93,6 +96,44 @@ __device__ __forceinline__ int item_wg(int j, const ProjArgs &A, int G) {
     return (int)(b * uC + ((g + 1) * uC - 1) / uG);
   }
   return (int)(((uj + 1) * (uint32_t)A.W - 1) / (uint32_t)A.I);
+}
+
+// Exchange meet of one row's sums (see tq_proj.h): piece pc of npc walks
+// the fixed binary tree over piece indices; at the node whose right subtree
+// starts at `mid` both children swap their sums into slot mid - 1 of the
+// block.  Slots hold fp32 bits xor the +inf pattern, so the all-zero word
+// (both halves +inf, never a sum of finite terms) means empty.  Returns
+// whether this lane ends up holding the row's total (in tot).
+__device__ __forceinline__ uint32_t meet_enc(float x) { return __float_as_uint(x) ^ 0x7F800000u; }
+__device__ __forceinline__ float meet_dec(uint32_t e) { return __uint_as_float(e ^ 0x7F800000u); }
+
+template <int NMAT>
+__device__ __forceinline__ bool meet_tree(float (&tot)[NMAT], bool live, int pc, int npc,
+                                          void *slots_v, int stride, int b, int lane) {
+  using S = typename std::conditional<NMAT == 1, uint32_t, uint64_t>::type;
+  S *slots = reinterpret_cast<S *>(slots_v) + (size_t)b * stride * 64 + lane;
+  S v = (S)meet_enc(tot[0]);
+  if constexpr (NMAT == 2) v |= (S)meet_enc(tot[1]) << 32;
+  bool holder = live;
+  for (int l = 0; (1 << l) < npc; l++) {
+    const int mid = (((pc >> l) & ~1) + 1) << l;  // first piece of the right subtree
+    if (holder && mid < npc) {
+      S *slot = slots + (size_t)(mid - 1) * 64;
+      const S old = __hip_atomic_exchange(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == 0) {
+        holder = false;  // the other subtree's piece finishes this row
+      } else {
+        S w = (S)meet_enc(meet_dec((uint32_t)old) + meet_dec((uint32_t)v));
+        if constexpr (NMAT == 2)
+          w |= (S)meet_enc(meet_dec((uint32_t)(old >> 32)) + meet_dec((uint32_t)(v >> 32))) << 32;
+        v = w;
+        __hip_atomic_store(slot, (S)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  tot[0] = meet_dec((uint32_t)v);
+  if constexpr (NMAT == 2) tot[1] = meet_dec((uint32_t)(v >> 32));
+  return holder;
 }
 
 // Two workgroups per CU: at most 128 VGPRs.
@@ -354,32 +395,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
   const size_t n = (size_t)b * tq::kBlockRows + lane;
   const bool row_ok = lane < (int)L.valid_rows(b);
-  // A block cut over several workgroups: each piece publishes its sums,
-  // the last to arrive (agent-scope counter) adds them in workgroup order.
+  // The pieces of a block cut over several workgroups meet (tq_proj.h).
+  bool fin = row_ok;  // this lane stores row n
   if constexpr (SPLIT) {
+    // each range holds at least G items, so a cut block has two pieces
     const int wf = item_wg(b * G, A, G), wl = item_wg(b * G + G - 1, A, G);
-    if (wf != wl) {
-#pragma unroll
-      for (int mat = 0; mat < NMAT; mat++)
-        __hip_atomic_store(&A.partials[(((size_t)wg * kMaxParts + part) * NMAT + mat) * 64 + lane],
-                           tot[mat], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);  // the piece has reached device scope
-      uint32_t prev = 0;
-      if (lane == 0)
-        prev = __hip_atomic_fetch_add(&A.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      prev = __shfl(prev, 0, 64);
-      if (prev != (uint32_t)(wl - wf)) return;  // another piece finishes this block
-#pragma unroll
-      for (int mat = 0; mat < NMAT; mat++) tot[mat] = 0.0f;
-      for (int ww = wf; ww <= wl; ww++) {
-        const int pp = b - (int)((uint32_t)wg_first(ww, A, G) / (uint32_t)G);  // the block's part in ww's range
-#pragma unroll
-        for (int mat = 0; mat < NMAT; mat++)
-          tot[mat] += __hip_atomic_load(&A.partials[(((size_t)ww * kMaxParts + pp) * NMAT + mat) * 64 + lane],
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (lane == 0) __hip_atomic_store(&A.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (wf != wl) fin = meet_tree<NMAT>(tot, row_ok, wg - wf, 2, A.slots, A.slot_stride, b, lane);
+  } else if (A.C > 1 && A.meet) {
+    fin = meet_tree<NMAT>(tot, row_ok, wg - b * A.C, A.C, A.slots, A.slot_stride, b, lane);
   } else if (A.C > 1) {
     const int c = wg - b * A.C;
     if (row_ok) {
@@ -397,10 +420,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
     for (int mat = 0; mat < NMAT; mat++) {
       float s = 0.0f;
-      if (row_ok)
+      if (row_ok) {
         for (int cc = 0; cc < A.C; cc++)
           s += __hip_atomic_load(&A.partials[((size_t)cc * NMAT + mat) * N + n], __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
+        // consumed: leave the workspace zero for the next call, whatever its shape
+        for (int cc = 0; cc < A.C; cc++)
+          __hip_atomic_store(&A.partials[((size_t)cc * NMAT + mat) * N + n], 0.0f, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
       tot[mat] = s;
     }
     if (lane == 0) __hip_atomic_store(&A.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -428,10 +456,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       y = A.out_signs[n] < 0 ? -r : r;
     }
   }
-  if (row_ok) A.out[n] = y;
+  if (fin) A.out[n] = y;
   if (A.out_bmax) {
-    const float m = wave_max(row_ok ? fabsf(y) : 0.0f);
-    if (lane == 0) A.out_bmax[b] = m;
+    const float m = wave_max(fin ? fabsf(y) : 0.0f);
+    const uint64_t fm = __ballot(fin), vm = __ballot(row_ok);
+    if (fm == vm) {
+      if (lane == 0) A.out_bmax[b] = m;  // this wave stored every row of the block
+    } else if (fm != 0 && lane == 0) {
+      // exchange meet, rows finished by several workgroups: each adds its
+      // maximum (|y| >= 0, so the bits order as the values) and then, once
+      // that is done, its row count; the one completing the count stores
+      uint32_t *mm = A.meet_max + 2 * (size_t)b;
+      __hip_atomic_fetch_max(&mm[0], __float_as_uint(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      const uint32_t k = (uint32_t)__popcll(fm), rows = (uint32_t)__popcll(vm);
+      const uint32_t prev = __hip_atomic_fetch_add(&mm[1], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev + k == rows) {
+        A.out_bmax[b] = __uint_as_float(__hip_atomic_load(&mm[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        __hip_atomic_store(&mm[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&mm[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
