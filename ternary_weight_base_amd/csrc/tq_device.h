@@ -176,6 +176,33 @@ __device__ __forceinline__ void b3_group(const uint2 *lut, uint32_t laneoff,
   for (int m = 0; m < MT; m++) S[m] = sdot4(e[25].x, x.get(m, 31), S[m]) + S2[m];
 }
 
+// Integer core of one B3 group with the activation words in VGPRs (read
+// from LDS by the caller, the same address in every lane): the dots take
+// VGPR operands, so the fifth trits of bytes 4c..4c+3 are packed into one
+// word (shifts and ors) for a single dot with word 25 + c, where the SGPR
+// form shifts the activation word instead.
+__device__ __forceinline__ int b3_group_v(const uint2 *lut, uint32_t laneoff, const uint32_t (&w)[7],
+                                          const uint32_t (&x)[32]) {
+  uint2 e[26];
+#define TQ_LK(J) e[J] = b3_byte<J>(lut, w, laneoff);
+  TQ_LK(0) TQ_LK(1) TQ_LK(2) TQ_LK(3) TQ_LK(4) TQ_LK(5) TQ_LK(6) TQ_LK(7) TQ_LK(8)
+  TQ_LK(9) TQ_LK(10) TQ_LK(11) TQ_LK(12) TQ_LK(13) TQ_LK(14) TQ_LK(15) TQ_LK(16)
+  TQ_LK(17) TQ_LK(18) TQ_LK(19) TQ_LK(20) TQ_LK(21) TQ_LK(22) TQ_LK(23) TQ_LK(24)
+  TQ_LK(25)
+#undef TQ_LK
+  int S = 0, S2 = 0;
+#pragma unroll
+  for (int j = 0; j < 25; j++) S = sdot4(e[j].x, x[j], S);
+#pragma unroll
+  for (int c = 0; c < 6; c++) {
+    const uint32_t f = e[4 * c].y | (e[4 * c + 1].y << 8) | (e[4 * c + 2].y << 16) | (e[4 * c + 3].y << 24);
+    S2 = sdot4(f, x[25 + c], S2);
+  }
+  // word 31: the fifth trit of byte 24 (byte 0) and digits 1..3 of byte 25
+  S2 = sdot4(e[24].y, x[31], S2);
+  return sdot4(e[25].x, x[31], S) + S2;
+}
+
 // Integer core of one 2B group.  Device byte 4c' + c, bits 2s hold
 // k = 16c' + 4s + c, so field s of word c' pairs with activation word
 // 4c' + s.  Codes d = t + 1 are dotted directly (fields masked in place, so

@@ -139,8 +139,15 @@ __device__ __forceinline__ bool meet_tree(float (&tot)[NMAT], bool live, int pc,
 // Two workgroups per CU: at most 128 VGPRs.
 // SPLIT: the equal item split (ranges may cross blocks); otherwise K chunks
 // of one block.
-template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void proj_kernel(ProjArgs A) {
+// LX (B3 only): the quantised activations go through LDS into VGPRs
+// (b3_group_v) instead of v_readlane into SGPRs: fewer VALU operations per
+// group but about 140 VGPRs, so it is launched only for grids of at most one
+// workgroup per CU (two waves per SIMD, 256 VGPRs); bigger grids keep the
+// SGPR form within 128 VGPRs (two workgroups per CU).
+template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LX ? 2 : 4)))
+void proj_kernel(ProjArgs A) {
+  static_assert(!LX || FMT == 0, "the LDS activation path is for B3");
   constexpr int WPG = FMT == 0 ? 7 : 9;   // words per (row, group) in registers
   constexpr int NP = (GS + 1) / 2;        // group pairs: one activation word per lane each
   constexpr int D0 = D < GS ? D : GS;
@@ -148,6 +155,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
   __shared__ float red[NPART * NMAT * kNW * 64];
   __shared__ float wmax[kNW];
+  __shared__ __attribute__((aligned(16))) uint32_t qs[LX ? kNW : 1][LX ? GS : 1][32];
   // The digit table depends on nothing: its LDS stores overlap the kernel
   // argument loads and the address arithmetic below.
   if constexpr (FMT == 0) fill_b3_lut<kThreads>(lut);
@@ -307,6 +315,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       }
     }
   }
+  if constexpr (LX) {  // the wave's own slice: no barrier needed
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+      const int jl = 2 * p + hsel;
+      if (jl < GS) qs[wave][jl][word] = qv[p];
+    }
+  }
   // 2B: activation sum of every group of the slice (a 32-lane reduction)
   int xsum[GS];
   if constexpr (FMT == 1) {
@@ -339,8 +354,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (i + D0 < GS) issue(i + D0);
     asm volatile("" : "+v"(qv[i >> 1]));
     XRegs<1> xa;
+    uint32_t xv[LX ? 32 : 1];
+    if constexpr (LX) {
+      const uint4 *xq = reinterpret_cast<const uint4 *>(&qs[wave][i][0]);
 #pragma unroll
-    for (int k = 0; k < 32; k++) xa.v[0][k] = __builtin_amdgcn_readlane(qv[i >> 1], 32 * (i & 1) + k);
+      for (int k = 0; k < 8; k++) {
+        const uint4 t = xq[k];
+        xv[4 * k] = t.x;
+        xv[4 * k + 1] = t.y;
+        xv[4 * k + 2] = t.z;
+        xv[4 * k + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 32; k++) xa.v[0][k] = __builtin_amdgcn_readlane(qv[i >> 1], 32 * (i & 1) + k);
+    }
     const bool live = i < ns;
     const int part = SPLIT ? sb[i] - bw0 : 0;
 #pragma unroll
@@ -352,7 +380,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       if constexpr (FMT == 0) {
         const uint32_t w[7] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2], wd[mat][i][3],
                                wd[mat][i][4], wd[mat][i][5], wd[mat][i][6]};
-        b3_group<1>(lut, laneoff, w, xa, S);
+        if constexpr (LX) S[0] = b3_group_v(lut, laneoff, w, xv);
+        else b3_group<1>(lut, laneoff, w, xa, S);
         sc = half_bits(wd[mat][i][6] >> 16);
       } else {
         const uint32_t w[9] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2],
@@ -480,13 +509,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   }
 }
 
-template <int FMT, int NMAT, int IN>
+template <int FMT, int NMAT, int IN, bool LX>
 int launch_in(const Plan &p, const ProjArgs &A, hipStream_t st) {
   constexpr int D = NMAT == 2 ? TQ_PROJ_D2 : TQ_PROJ_D1;
   const dim3 grid((unsigned)p.grid), block(kThreads);
-#define TQ_CASE(G_, S_)                                                                  \
-  case G_:                                                                               \
-    hipLaunchKernelGGL((proj_kernel<FMT, NMAT, IN, G_, D, S_>), grid, block, 0, st, A);  \
+#define TQ_CASE(G_, S_)                                                                      \
+  case G_:                                                                                   \
+    hipLaunchKernelGGL((proj_kernel<FMT, NMAT, IN, G_, D, S_, LX>), grid, block, 0, st, A);  \
     break;
   if constexpr (NMAT == 1) {
     switch (p.gs) {
@@ -509,16 +538,24 @@ int launch_in(const Plan &p, const ProjArgs &A, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
+template <int FMT, bool LX>
+int launch_lx(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st) {
+  if (nmat == 2) {
+    if (in_kind == kInInt8) return launch_in<FMT, 2, kInInt8, LX>(p, A, st);
+    if (in_kind == kInF16) return launch_in<FMT, 2, kInF16, LX>(p, A, st);
+    return launch_in<FMT, 2, kInF32, LX>(p, A, st);
+  }
+  if (in_kind == kInInt8) return launch_in<FMT, 1, kInInt8, LX>(p, A, st);
+  if (in_kind == kInF16) return launch_in<FMT, 1, kInF16, LX>(p, A, st);
+  return launch_in<FMT, 1, kInF32, LX>(p, A, st);
+}
+
 template <int FMT>
 int launch_fmt(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st) {
-  if (nmat == 2) {
-    if (in_kind == kInInt8) return launch_in<FMT, 2, kInInt8>(p, A, st);
-    if (in_kind == kInF16) return launch_in<FMT, 2, kInF16>(p, A, st);
-    return launch_in<FMT, 2, kInF32>(p, A, st);
+  if constexpr (FMT == 0) {
+    if (p.grid <= kLxMaxGrid) return launch_lx<FMT, true>(p, A, nmat, in_kind, st);
   }
-  if (in_kind == kInInt8) return launch_in<FMT, 1, kInInt8>(p, A, st);
-  if (in_kind == kInF16) return launch_in<FMT, 1, kInF16>(p, A, st);
-  return launch_in<FMT, 1, kInF32>(p, A, st);
+  return launch_lx<FMT, false>(p, A, nmat, in_kind, st);
 }
 
 }  // namespace tqproj

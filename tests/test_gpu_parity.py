@@ -134,11 +134,13 @@ def _gemv_gpu(fmt, M, N, K, W, q, a):
                                    (1, 10240, 5120), (1, 5120, 8192), (1, 5120, 17408),
                                    (2, 5120, 17408), (4, 1000, 2048), (8, 257, 1024),
                                    (16, 300, 5120), (8, 5120, 17408), (16, 10240, 5120),
-                                   (1, 8192, 4096), (1, 4096, 8192), (1, 4136, 8192), (1, 2048, 8192)])
+                                   (1, 8192, 4096), (1, 4096, 8192), (1, 4136, 8192), (1, 2048, 8192),
+                                   (1, 20000, 640)])
 def test_gemv_vs_oracle(fmt, M, N, K):
     """One token: the K-chunk splits meet by exchange (2 chunks at 8192 rows,
     a full two-level tree of 4 at 4096, 3 with a ragged 40-row tail block at
-    4136) or through the counter (8 chunks at 2048 rows)."""
+    4136) or through the counter (8 chunks at 2048 rows); 20000 rows take 313
+    workgroups, more than one per CU (B3: the SGPR activation form)."""
     say(f"gemv {FMTS[fmt]} M={M} N={N} K={K}")
     t, s = weights(N, K, 4000 + N + K)
     x = acts_f16(M, K, 4100 + M + K)
