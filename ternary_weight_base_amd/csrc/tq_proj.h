@@ -43,7 +43,7 @@ enum InKind { kInInt8 = 0, kInF16 = 1, kInF32 = 2 };
 // two ways below.
 constexpr int kMaxParts = 3;  // blocks touched by one workgroup's range
 constexpr int kMeetMaxC = 4;  // K chunks per block that still meet by exchange
-constexpr int kLxMaxGrid = 256;  // B3 grids up to one workgroup per CU: LDS activations
+constexpr int kLxMaxGrid = 256;  // grids up to one workgroup per CU: LDS activations
 
 // Two ways for the pieces of a cut block to meet.
 //  - Counter (K chunks, any count): each piece stores its sums, waits for them

@@ -139,15 +139,14 @@ __device__ __forceinline__ bool meet_tree(float (&tot)[NMAT], bool live, int pc,
 // Two workgroups per CU: at most 128 VGPRs.
 // SPLIT: the equal item split (ranges may cross blocks); otherwise K chunks
 // of one block.
-// LX (B3 only): the quantised activations go through LDS into VGPRs
-// (b3_group_v) instead of v_readlane into SGPRs: fewer VALU operations per
-// group but about 140 VGPRs, so it is launched only for grids of at most one
-// workgroup per CU (two waves per SIMD, 256 VGPRs); bigger grids keep the
-// SGPR form within 128 VGPRs (two workgroups per CU).
+// LX: the quantised activations go through LDS into VGPRs instead of
+// v_readlane into SGPRs: fewer VALU operations per group but up to about
+// 140 VGPRs, so it is launched only for grids of at most one workgroup per
+// CU (two waves per SIMD, 256 VGPRs); bigger grids keep the SGPR form
+// within 128 VGPRs (two workgroups per CU).
 template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LX ? 2 : 4)))
 void proj_kernel(ProjArgs A) {
-  static_assert(!LX || FMT == 0, "the LDS activation path is for B3");
   constexpr int WPG = FMT == 0 ? 7 : 9;   // words per (row, group) in registers
   constexpr int NP = (GS + 1) / 2;        // group pairs: one activation word per lane each
   constexpr int D0 = D < GS ? D : GS;
@@ -353,17 +352,16 @@ void proj_kernel(ProjArgs A) {
   for (int i = 0; i < GS; i++) {
     if (i + D0 < GS) issue(i + D0);
     asm volatile("" : "+v"(qv[i >> 1]));
-    XRegs<1> xa;
-    uint32_t xv[LX ? 32 : 1];
+    XRegs<1> xa;  // SGPRs (v_readlane) or, with LX, VGPRs (LDS)
     if constexpr (LX) {
       const uint4 *xq = reinterpret_cast<const uint4 *>(&qs[wave][i][0]);
 #pragma unroll
       for (int k = 0; k < 8; k++) {
         const uint4 t = xq[k];
-        xv[4 * k] = t.x;
-        xv[4 * k + 1] = t.y;
-        xv[4 * k + 2] = t.z;
-        xv[4 * k + 3] = t.w;
+        xa.v[0][4 * k] = t.x;
+        xa.v[0][4 * k + 1] = t.y;
+        xa.v[0][4 * k + 2] = t.z;
+        xa.v[0][4 * k + 3] = t.w;
       }
     } else {
 #pragma unroll
@@ -380,7 +378,7 @@ void proj_kernel(ProjArgs A) {
       if constexpr (FMT == 0) {
         const uint32_t w[7] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2], wd[mat][i][3],
                                wd[mat][i][4], wd[mat][i][5], wd[mat][i][6]};
-        if constexpr (LX) S[0] = b3_group_v(lut, laneoff, w, xv);
+        if constexpr (LX) S[0] = b3_group_v(lut, laneoff, w, xa.v[0]);
         else b3_group<1>(lut, laneoff, w, xa, S);
         sc = half_bits(wd[mat][i][6] >> 16);
       } else {
@@ -552,9 +550,7 @@ int launch_lx(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream
 
 template <int FMT>
 int launch_fmt(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st) {
-  if constexpr (FMT == 0) {
-    if (p.grid <= kLxMaxGrid) return launch_lx<FMT, true>(p, A, nmat, in_kind, st);
-  }
+  if (p.grid <= kLxMaxGrid) return launch_lx<FMT, true>(p, A, nmat, in_kind, st);
   return launch_lx<FMT, false>(p, A, nmat, in_kind, st);
 }
 
