@@ -179,8 +179,8 @@ __device__ __forceinline__ void b3_group(const uint2 *lut, uint32_t laneoff,
 // Integer core of one B3 group with the activation words in VGPRs (read
 // from LDS by the caller, the same address in every lane): the dots take
 // VGPR operands, so the fifth trits of bytes 4c..4c+3 are packed into one
-// word (shifts and ors) for a single dot with word 25 + c, where the SGPR
-// form shifts the activation word instead.
+// word (two byte merges and a shift-or) for a single dot with word 25 + c,
+// where the SGPR form shifts the activation word instead.
 __device__ __forceinline__ int b3_group_v(const uint2 *lut, uint32_t laneoff, const uint32_t (&w)[7],
                                           const uint32_t (&x)[32]) {
   uint2 e[26];
@@ -195,8 +195,10 @@ __device__ __forceinline__ int b3_group_v(const uint2 *lut, uint32_t laneoff, co
   for (int j = 0; j < 25; j++) S = sdot4(e[j].x, x[j], S);
 #pragma unroll
   for (int c = 0; c < 6; c++) {
-    const uint32_t f = e[4 * c].y | (e[4 * c + 1].y << 8) | (e[4 * c + 2].y << 16) | (e[4 * c + 3].y << 24);
-    S2 = sdot4(f, x[25 + c], S2);
+    // byte 0 of each .y: two v_perm merge pairs, one shift-or joins them
+    const uint32_t lo = perm_b32(e[4 * c + 1].y, e[4 * c].y, 0x0C0C0400u);
+    const uint32_t hi = perm_b32(e[4 * c + 3].y, e[4 * c + 2].y, 0x0C0C0400u);
+    S2 = sdot4(lo | (hi << 16), x[25 + c], S2);
   }
   // word 31: the fifth trit of byte 24 (byte 0) and digits 1..3 of byte 25
   S2 = sdot4(e[24].y, x[31], S2);
