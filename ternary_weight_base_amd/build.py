@@ -53,8 +53,9 @@ def build() -> str:
               "-c", os.path.join(CSRC, src), "-o", o])
         host_objs.append(o)
     objs, cmds = [], []
-    for src in ("tq_kernels.hip", "tq_proj.hip", "tq_proj_b3.hip", "tq_proj_2b.hip", "tq_proj_bp.hip",
-                "tq_gemv_mfma.hip", "tq_hadamard.hip", "tq_gemm.hip", "tq_stream.hip"):
+    for src in ("tq_kernels.hip", "tq_proj.hip", "tq_proj_b3.hip", "tq_proj_b3_sg.hip", "tq_proj_2b.hip",
+                "tq_proj_2b_sg.hip", "tq_proj_bp.hip", "tq_proj_bp_sg.hip", "tq_gemv_mfma.hip",
+                "tq_hadamard.hip", "tq_gemm.hip", "tq_stream.hip"):
         o = os.path.join(bdir, src.replace(".hip", ".o"))
         cmds.append(["hipcc", *HIP_FLAGS, "-I", INC, "-I", CSRC, "-c", os.path.join(CSRC, src),
                      "-o", o])

@@ -615,10 +615,14 @@ int launch_gemv_m(const GemvPlan &p, const void *W0, const void *W1, const int8_
                   const float *a, float *out, int32_t *sums, void *ws, int M, int N, int K,
                   hipStream_t st) {
   if (M <= 1) return launch_gemv_t<FMT, 1, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
-  if (M <= 2) return launch_gemv_t<FMT, 2, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
-  if (M <= 4) return launch_gemv_t<FMT, 4, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
-  if (M <= 8) return launch_gemv_t<FMT, 8, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
-  return launch_gemv_t<FMT, 16, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+  if constexpr (!SUMS && TQ_GEMV_MFMA) {
+    return TQ_ERR_SHAPE;  // several tokens run on the MFMA GEMV: not instantiated here
+  } else {
+    if (M <= 2) return launch_gemv_t<FMT, 2, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+    if (M <= 4) return launch_gemv_t<FMT, 4, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+    if (M <= 8) return launch_gemv_t<FMT, 8, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+    return launch_gemv_t<FMT, 16, NMAT, SUMS>(p, W0, W1, q, a, out, sums, ws, M, N, K, st);
+  }
 }
 
 template <int NMAT, bool SUMS>

@@ -95,10 +95,13 @@ struct WsLayout {
   size_t counters, meet, slots, partials, total;
 };
 
-// Launch the kernel of packed format B3 / 2B for this plan (nmat 1 or 2,
-// in_kind one of InKind).  Returns a tq_status.
-int launch_b3(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st);
-int launch_2b(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st);
-int launch_bp(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st);
+// Launch the kernel of packed format FMT (0 B3, 1 2B, 2 BP) for this plan
+// (nmat 1 or 2, in_kind one of InKind), with the activations in VGPRs
+// through LDS (LX, grids of at most kLxMaxGrid workgroups) or in SGPRs.
+// Returns a tq_status.  Instantiated one (FMT, LX) pair per source file
+// (tq_proj_b3.hip, tq_proj_b3_sg.hip, ...), so that they compile in
+// parallel.
+template <int FMT, bool LX>
+int launch_lx(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st);
 
 }  // namespace tqproj

@@ -118,8 +118,12 @@ int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, i
   A.C = p.C;
   A.W = p.W;
   A.I = p.I;
-  if (fmt == TQ_FMT_B3) return launch_b3(p, A, nmat, in_kind, st);
-  return fmt == TQ_FMT_2B ? launch_2b(p, A, nmat, in_kind, st) : launch_bp(p, A, nmat, in_kind, st);
+  const bool lx = p.grid <= kLxMaxGrid;
+  if (fmt == TQ_FMT_B3)
+    return lx ? launch_lx<0, true>(p, A, nmat, in_kind, st) : launch_lx<0, false>(p, A, nmat, in_kind, st);
+  if (fmt == TQ_FMT_2B)
+    return lx ? launch_lx<1, true>(p, A, nmat, in_kind, st) : launch_lx<1, false>(p, A, nmat, in_kind, st);
+  return lx ? launch_lx<2, true>(p, A, nmat, in_kind, st) : launch_lx<2, false>(p, A, nmat, in_kind, st);
 }
 
 WsLayout proj_ws(int fmt, int64_t N, int64_t K, int nmat) {

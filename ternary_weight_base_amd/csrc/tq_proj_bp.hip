@@ -1,7 +1,6 @@
-// tq_proj_bp.hip -- instantiations of the projection kernel for the BP
-// (nonzero and sign bit-planes) packed format.
+// tq_proj_bp.hip -- instantiations of the projection kernel for the
+// BP (nonzero and sign bit-planes) packed format, activations in VGPRs through LDS (grids of at most one
+// workgroup per CU).
 #include "tq_proj_kernel.h"
 
-int tqproj::launch_bp(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st) {
-  return launch_fmt<2>(p, A, nmat, in_kind, st);
-}
+template int tqproj::launch_lx<2, true>(const Plan &, const ProjArgs &, int, int, hipStream_t);

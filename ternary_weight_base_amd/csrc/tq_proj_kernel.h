@@ -1,6 +1,6 @@
 // tq_proj_kernel.h -- the one-token projection kernel: activation quantiser
 // fused in, weight stream software-pipelined.  Included by the per-format
-// instantiation units tq_proj_b3.hip and tq_proj_2b.hip.
+// instantiation units tq_proj_{b3,2b,bp}.hip and tq_proj_{b3,2b,bp}_sg.hip.
 //
 // What is computed is the decode GEMV of include/tq.h: per group of 128
 // weights an integer dot of decoded trits with int8 activations, scaled by
@@ -548,10 +548,5 @@ int launch_lx(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream
   return launch_in<FMT, 1, kInF32, LX>(p, A, st);
 }
 
-template <int FMT>
-int launch_fmt(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st) {
-  if (p.grid <= kLxMaxGrid) return launch_lx<FMT, true>(p, A, nmat, in_kind, st);
-  return launch_lx<FMT, false>(p, A, nmat, in_kind, st);
-}
 
 }  // namespace tqproj
