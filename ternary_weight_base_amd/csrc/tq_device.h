@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tq_layout.h"
 
 namespace tqdev {
@@ -203,6 +205,49 @@ __device__ __forceinline__ int b3_group_v(const uint2 *lut, uint32_t laneoff, co
   // word 31: the fifth trit of byte 24 (byte 0) and digits 1..3 of byte 25
   S2 = sdot4(e[24].y, x[31], S2);
   return sdot4(e[25].x, x[31], S) + S2;
+}
+
+// Exchange meet of one output's sums between the pieces of a block cut
+// between workgroups: piece pc of npc walks the fixed binary tree over piece
+// indices; at the node whose right subtree starts at `mid` both children
+// swap their sums into that node's slot (slot0 + (mid - 1) * node_stride)
+// with one agent-scope atomic exchange.  The piece that gets the other's
+// sums back adds them (fp32 addition commutes, so the total does not depend
+// on which arrives first), empties the slot and goes on up; the other is
+// done with this output.  Slots hold fp32 bits xor the +inf pattern, so the
+// all-zero word (both halves +inf, never a sum of finite terms) means empty.
+// NMAT 2 carries both matrices' sums in one 64-bit word.  Returns whether
+// this thread ends up holding the total (in tot).
+__device__ __forceinline__ uint32_t meet_enc(float x) { return __float_as_uint(x) ^ 0x7F800000u; }
+__device__ __forceinline__ float meet_dec(uint32_t e) { return __uint_as_float(e ^ 0x7F800000u); }
+
+template <int NMAT>
+__device__ __forceinline__ bool meet_tree(float (&tot)[NMAT], bool live, int pc, int npc, void *slot0_v,
+                                          size_t node_stride) {
+  using S = typename std::conditional<NMAT == 1, uint32_t, uint64_t>::type;
+  S *slot0 = reinterpret_cast<S *>(slot0_v);
+  S v = (S)meet_enc(tot[0]);
+  if constexpr (NMAT == 2) v |= (S)meet_enc(tot[1]) << 32;
+  bool holder = live;
+  for (int l = 0; (1 << l) < npc; l++) {
+    const int mid = (((pc >> l) & ~1) + 1) << l;  // first piece of the right subtree
+    if (holder && mid < npc) {
+      S *slot = slot0 + (size_t)(mid - 1) * node_stride;
+      const S old = __hip_atomic_exchange(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == 0) {
+        holder = false;
+      } else {
+        S w = (S)meet_enc(meet_dec((uint32_t)old) + meet_dec((uint32_t)v));
+        if constexpr (NMAT == 2)
+          w |= (S)meet_enc(meet_dec((uint32_t)(old >> 32)) + meet_dec((uint32_t)(v >> 32))) << 32;
+        v = w;
+        __hip_atomic_store(slot, (S)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  tot[0] = meet_dec((uint32_t)v);
+  if constexpr (NMAT == 2) tot[1] = meet_dec((uint32_t)(v >> 32));
+  return holder;
 }
 
 // Integer core of one 2B group.  Device byte 4c' + c, bits 2s hold

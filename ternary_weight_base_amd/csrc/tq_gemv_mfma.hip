@@ -43,10 +43,15 @@ struct MArgs {
   const int8_t *q;        // [M][K]
   const float *a_scale;   // [M]
   float *out;             // [M][N]
-  float *partials;        // [C][nmat][NB][64 * kOut] when C > 1
-  uint32_t *counters;     // [NB] when C > 1, zero on entry and on exit
+  float *partials;        // counter meet: [C][nmat][NB][64 * kOut]
+  uint32_t *counters;     // counter meet: [NB], zero on entry and on exit
+  void *slots;            // exchange meet: [NB][C - 1][64 * kOut] words (32-bit one
+                          // matrix, 64-bit gate/up), zero on entry and on exit
   int M, N, K, C;
+  int meet;               // 1: exchange meet (C <= kMeetMaxC), 0: counter meet
 };
+
+constexpr int kMeetMaxC = 4;  // K chunks per block that meet by exchange
 
 // Slot q of lane group g receives what slot g of lane group q held
 // (16-lane groups; four registers).
@@ -272,7 +277,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       tot[p][mat] = s;
     }
   }
-  if (A.C > 1) {
+  bool fin[kPer];  // this thread stores output p
+#pragma unroll
+  for (int p = 0; p < kPer; p++) fin[p] = true;
+  if (A.C > 1 && A.meet) {
+    // K chunks meet pairwise along a fixed tree, one output per slot
+    using S = typename std::conditional<NMAT == 1, uint32_t, uint64_t>::type;
+#pragma unroll
+    for (int p = 0; p < kPer; p++) {
+      S *slot0 = reinterpret_cast<S *>(A.slots) + (size_t)b * (A.C - 1) * 64 * kOut + tid + p * kThreads;
+      fin[p] = meet_tree<NMAT>(tot[p], true, c, A.C, slot0, 64 * kOut);
+    }
+  } else if (A.C > 1) {
     float *part = A.partials;
 #pragma unroll
     for (int p = 0; p < kPer; p++)
@@ -314,7 +330,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   for (int p = 0; p < kPer; p++) {
     const int o = tid + p * kThreads, j = o >> 6, l = o & 63;
     const int m = 4 * (l >> 4) + (j & 3), r = 16 * (j >> 2) + (l & 15);
-    if (m >= M || r >= rows) continue;
+    if (!fin[p] || m >= M || r >= rows) continue;
     const float a = A.a_scale[m];
     float yv;
     if (NMAT == 1) {
@@ -329,7 +345,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 
 struct MPlan {
   int gs, C, NB;
-  size_t counters_bytes, partials_bytes;
+  bool meet;
+  size_t counters_bytes, partials_bytes, slots_bytes;
+  size_t ws_bytes() const { return counters_bytes + partials_bytes + slots_bytes; }
 };
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -356,8 +374,11 @@ MPlan plan(int fmt, int64_t N, int64_t K, int nmat) {
   p.gs = (int)gs;
   p.C = (int)C;
   p.NB = (int)NB;
-  p.counters_bytes = C > 1 ? round256((size_t)NB * 4) : 0;
-  p.partials_bytes = C > 1 ? round256((size_t)C * nmat * NB * 64 * kOut * 4) : 0;
+  p.meet = C > 1 && C <= kMeetMaxC;  // exchange; more chunks: the counter
+  const bool counter = C > 1 && !p.meet;
+  p.counters_bytes = counter ? round256((size_t)NB * 4) : 0;
+  p.partials_bytes = counter ? round256((size_t)C * nmat * NB * 64 * kOut * 4) : 0;
+  p.slots_bytes = p.meet ? round256((size_t)NB * (C - 1) * 64 * kOut * 4 * nmat) : 0;
   return p;
 }
 
@@ -380,7 +401,7 @@ int launch(const MPlan &p, const MArgs &A, hipStream_t st) {
 
 size_t tq_internal_mgemv_ws_bytes(int fmt, int64_t N, int64_t K, int nmat) {
   const MPlan p = plan(fmt, N, K, nmat);
-  return p.counters_bytes + p.partials_bytes;
+  return p.ws_bytes();
 }
 
 // 2 <= M <= 16; arguments already checked by the caller (shape, alignment).
@@ -392,7 +413,7 @@ int tq_internal_mgemv(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, 
   if (p.C > 1) {
     if (!ws) return TQ_ERR_NULL;
     if (((uintptr_t)ws & 15u) != 0) return TQ_ERR_ALIGN;
-    if (ws_bytes < p.counters_bytes + p.partials_bytes) return TQ_ERR_SIZE;
+    if (ws_bytes < p.ws_bytes()) return TQ_ERR_SIZE;
   }
   MArgs A;
   A.W0 = (const uint8_t *)W0;
@@ -400,8 +421,10 @@ int tq_internal_mgemv(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, 
   A.q = q;
   A.a_scale = a_scale;
   A.out = y;
-  A.counters = p.C > 1 ? reinterpret_cast<uint32_t *>(ws) : nullptr;
-  A.partials = p.C > 1 ? reinterpret_cast<float *>((char *)ws + p.counters_bytes) : nullptr;
+  A.meet = p.meet ? 1 : 0;
+  A.counters = p.counters_bytes ? reinterpret_cast<uint32_t *>(ws) : nullptr;
+  A.partials = p.partials_bytes ? reinterpret_cast<float *>((char *)ws + p.counters_bytes) : nullptr;
+  A.slots = p.slots_bytes ? (void *)((char *)ws + p.counters_bytes + p.partials_bytes) : nullptr;
   A.M = (int)M;
   A.N = (int)N;
   A.K = (int)K;

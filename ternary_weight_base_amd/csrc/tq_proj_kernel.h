@@ -36,8 +36,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "tq.h"
 #include "tq_device.h"
 #include "tq_layout.h"
@@ -98,47 +96,13 @@ __device__ __forceinline__ int item_wg(int j, const ProjArgs &A, int G) {
   return (int)(((uj + 1) * (uint32_t)A.W - 1) / (uint32_t)A.I);
 }
 
-// Exchange meet of one row's sums (see tq_proj.h): piece pc of npc walks
-// the fixed binary tree over piece indices; at the node whose right subtree
-// starts at `mid` both children swap their sums into slot mid - 1 of the
-// block.  Slots hold fp32 bits xor the +inf pattern, so the all-zero word
-// (both halves +inf, never a sum of finite terms) means empty.  Returns
-// whether this lane ends up holding the row's total (in tot).
-__device__ __forceinline__ uint32_t meet_enc(float x) { return __float_as_uint(x) ^ 0x7F800000u; }
-__device__ __forceinline__ float meet_dec(uint32_t e) { return __uint_as_float(e ^ 0x7F800000u); }
-
+// Node-0 slot of row `lane` of block b: slots [NB][slot_stride][64] words.
 template <int NMAT>
-__device__ __forceinline__ bool meet_tree(float (&tot)[NMAT], bool live, int pc, int npc,
-                                          void *slots_v, int stride, int b, int lane) {
+__device__ __forceinline__ void *meet_slot0(const ProjArgs &A, int b, int lane) {
   using S = typename std::conditional<NMAT == 1, uint32_t, uint64_t>::type;
-  S *slots = reinterpret_cast<S *>(slots_v) + (size_t)b * stride * 64 + lane;
-  S v = (S)meet_enc(tot[0]);
-  if constexpr (NMAT == 2) v |= (S)meet_enc(tot[1]) << 32;
-  bool holder = live;
-  for (int l = 0; (1 << l) < npc; l++) {
-    const int mid = (((pc >> l) & ~1) + 1) << l;  // first piece of the right subtree
-    if (holder && mid < npc) {
-      S *slot = slots + (size_t)(mid - 1) * 64;
-      const S old = __hip_atomic_exchange(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == 0) {
-        holder = false;  // the other subtree's piece finishes this row
-      } else {
-        S w = (S)meet_enc(meet_dec((uint32_t)old) + meet_dec((uint32_t)v));
-        if constexpr (NMAT == 2)
-          w |= (S)meet_enc(meet_dec((uint32_t)(old >> 32)) + meet_dec((uint32_t)(v >> 32))) << 32;
-        v = w;
-        __hip_atomic_store(slot, (S)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-  tot[0] = meet_dec((uint32_t)v);
-  if constexpr (NMAT == 2) tot[1] = meet_dec((uint32_t)(v >> 32));
-  return holder;
+  return reinterpret_cast<S *>(A.slots) + (size_t)b * A.slot_stride * 64 + lane;
 }
 
-// Two workgroups per CU: at most 128 VGPRs.
-// SPLIT: the equal item split (ranges may cross blocks); otherwise K chunks
-// of one block.
 // LX: the quantised activations go through LDS into VGPRs instead of
 // v_readlane into SGPRs: fewer VALU operations per group but up to about
 // 140 VGPRs, so it is launched only for grids of at most one workgroup per
@@ -427,9 +391,9 @@ void proj_kernel(ProjArgs A) {
   if constexpr (SPLIT) {
     // each range holds at least G items, so a cut block has two pieces
     const int wf = item_wg(b * G, A, G), wl = item_wg(b * G + G - 1, A, G);
-    if (wf != wl) fin = meet_tree<NMAT>(tot, row_ok, wg - wf, 2, A.slots, A.slot_stride, b, lane);
+    if (wf != wl) fin = meet_tree<NMAT>(tot, row_ok, wg - wf, 2, meet_slot0<NMAT>(A, b, lane), 64);
   } else if (A.C > 1 && A.meet) {
-    fin = meet_tree<NMAT>(tot, row_ok, wg - b * A.C, A.C, A.slots, A.slot_stride, b, lane);
+    fin = meet_tree<NMAT>(tot, row_ok, wg - b * A.C, A.C, meet_slot0<NMAT>(A, b, lane), 64);
   } else if (A.C > 1) {
     const int c = wg - b * A.C;
     if (row_ok) {
