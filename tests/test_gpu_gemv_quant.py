@@ -121,3 +121,37 @@ def test_gemv_quant_full_ffn_shapes(fmt, case):
     y, yb, ref = _run(fmt, N, K, x, gate_up, 68, x_bmax=xb)
     assert_close(y, ref, "y")
     assert np.array_equal(yb, _block_max(y)), "block maxima of y"
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
+@pytest.mark.parametrize("N,K,gate_up", [(17408, 5120, True), (5120, 17408, False)])
+def test_exchange_meet_deterministic(fmt, N, K, gate_up):
+    """The pieces of a cut block meet by exchange in whatever order they
+    arrive; 20 runs of the 27B gate/up (two pieces per block, equal split)
+    and down (three K chunks, a two-level tree) give the same y and block
+    maxima bit for bit, the maxima are those of y, and the workspace ends
+    zero."""
+    import ternary_weight_base_amd as tq
+    say(f"exchange determinism {FMTS[fmt]} {N}x{K}")
+    Wg = dev(tq.tq_pack(fmt, *weights(N, K, 63)))
+    Wu = dev(tq.tq_pack(fmt, *weights(N, K, 64))) if gate_up else None
+    x = synth.normal_f32(synth.seed(65, K), K)
+    xb = dev(_block_max(x))
+    x = dev(x)
+    nbytes = tq.tq_gemv_quant_workspace_bytes(fmt, N, K, gate_up)
+    assert nbytes > 0
+    ws = torch.zeros(max(4, (nbytes + 15) // 16 * 4), dtype=torch.int32, device="cuda")
+    ys, bs = [], []
+    for _ in range(20):
+        y = torch.full((N,), float("nan"), device="cuda")
+        yb = torch.full(((N + 63) // 64,), float("nan"), device="cuda")
+        tq.tq_gemv_quant(fmt, N, K, Wg, Wu, x, y, x_bmax=xb, y_bmax=yb, ws=ws)
+        ys.append(y)
+        bs.append(yb)
+    torch.cuda.synchronize()
+    y0, b0 = ys[0].cpu().numpy(), bs[0].cpu().numpy()
+    assert np.array_equal(b0, _block_max(y0))
+    for y, yb in zip(ys[1:], bs[1:]):
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), y0.view(np.uint32))
+        assert np.array_equal(yb.cpu().numpy().view(np.uint32), b0.view(np.uint32))
+    assert not ws.any().item()
