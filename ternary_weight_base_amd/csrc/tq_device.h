@@ -178,6 +178,14 @@ __device__ __forceinline__ void b3_group(const uint2 *lut, uint32_t laneoff,
   for (int m = 0; m < MT; m++) S[m] = sdot4(e[25].x, x.get(m, 31), S[m]) + S2[m];
 }
 
+// Byte 0 of each of four words (the fifth trits of four B3 bytes, from the
+// digit table's .y) packed into one word: two v_perm byte merges and one
+// shift-or.
+__device__ __forceinline__ uint32_t pack_y4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t lo = perm_b32(b, a, 0x0C0C0400u), hi = perm_b32(d, c, 0x0C0C0400u);
+  return lo | (hi << 16);
+}
+
 // Integer core of one B3 group with the activation words in VGPRs (read
 // from LDS by the caller, the same address in every lane): the dots take
 // VGPR operands, so the fifth trits of bytes 4c..4c+3 are packed into one
@@ -197,10 +205,7 @@ __device__ __forceinline__ int b3_group_v(const uint2 *lut, uint32_t laneoff, co
   for (int j = 0; j < 25; j++) S = sdot4(e[j].x, x[j], S);
 #pragma unroll
   for (int c = 0; c < 6; c++) {
-    // byte 0 of each .y: two v_perm merge pairs, one shift-or joins them
-    const uint32_t lo = perm_b32(e[4 * c + 1].y, e[4 * c].y, 0x0C0C0400u);
-    const uint32_t hi = perm_b32(e[4 * c + 3].y, e[4 * c + 2].y, 0x0C0C0400u);
-    S2 = sdot4(lo | (hi << 16), x[25 + c], S2);
+    S2 = sdot4(pack_y4(e[4 * c].y, e[4 * c + 1].y, e[4 * c + 2].y, e[4 * c + 3].y), x[25 + c], S2);
   }
   // word 31: the fifth trit of byte 24 (byte 0) and digits 1..3 of byte 25
   S2 = sdot4(e[24].y, x[31], S2);

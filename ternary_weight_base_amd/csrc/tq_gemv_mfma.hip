@@ -98,7 +98,7 @@ __device__ __forceinline__ void decode_half(const uint2 *lut, uint32_t laneoff, 
       // digit 4 of byte j (one trit in byte 0 of .y): k = 100 + j
 #pragma unroll
       for (int i = 0; i < 4; i++)
-        T[25 + i] = e[4 * i].y | (e[4 * i + 1].y << 8) | (e[4 * i + 2].y << 16) | (e[4 * i + 3].y << 24);
+        T[25 + i] = pack_y4(e[4 * i].y, e[4 * i + 1].y, e[4 * i + 2].y, e[4 * i + 3].y);
     } else {
       uint2 e[10];
 #define TQ_LK(J) e[J - 16] = b3_byte<J>(lut, w, laneoff);
@@ -109,8 +109,7 @@ __device__ __forceinline__ void decode_half(const uint2 *lut, uint32_t laneoff, 
       for (int j = 16; j < 25; j++) T[j] = e[j - 16].x;
 #pragma unroll
       for (int i = 4; i < 6; i++)
-        T[25 + i] = e[4 * i - 16].y | (e[4 * i - 15].y << 8) | (e[4 * i - 14].y << 16) |
-                    (e[4 * i - 13].y << 24);
+        T[25 + i] = pack_y4(e[4 * i - 16].y, e[4 * i - 15].y, e[4 * i - 14].y, e[4 * i - 13].y);
       // k = 124 (digit 4 of byte 24) and 125..127 (digits 1..3 of byte 25,
       // whose digit 0 is a zero-trit pad)
       T[31] = (e[9].x & 0xFFFFFF00u) | e[8].y;
