@@ -16,7 +16,9 @@ Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
   python bench.py --profile-summary TRACE_DIR FETCH_DIR WRITE_DIR
 turns three rocprofv3 runs of this script (--kernel-trace --stats, then
 --pmc FETCH_SIZE, then --pmc WRITE_SIZE) into the text summary kept under
-profiles/ and the per-launch HBM traffic of the dominant kernel.
+profiles/ and the per-launch HBM traffic of the dominant kernel;
+  python bench.py --counter-summary PMC_DIR...
+prints per-kernel averages of the SQ counters of --pmc runs of this script.
 """
 from __future__ import annotations
 
@@ -52,6 +54,10 @@ def parse():
                    help="skip the prefill GEMM and small-batch measurements")
     p.add_argument("--profile-summary", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="summarise rocprofv3 output directories of this script and exit")
+    p.add_argument("--counter-summary", nargs="+", metavar="PMC_DIR",
+                   help="per-kernel averages of the counters in rocprofv3 --pmc directories "
+                        "of this script (the stack's four projections, the prefill GEMM, the "
+                        "small-batch GEMV), and exit")
     return p.parse_args()
 
 
@@ -96,6 +102,9 @@ def main():
     args = parse()
     if args.profile_summary:
         profile_summary(*args.profile_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -501,6 +510,31 @@ def _rocpd(d):
                     "counters_collection group by kernel_name, counter_name, dispatch_id"):
                 ctrs.setdefault((name, cn), []).append(v)
     return durs, ctrs
+
+
+# Kernels whose counters counter_summary reports (name prefixes, B3 instantiations).
+COUNTER_KERNELS = (("QKV", "proj_kernel<0, 1, 1, 5,"), ("O", "proj_kernel<0, 1, 1, 3,"),
+                   ("gate/up", "proj_kernel<0, 2, 2, 6,"), ("down", "proj_kernel<0, 1, 2, 6,"),
+                   ("prefill GEMM", "gemm_kernel<0, false>"),
+                   ("small-batch gate/up", "mgemv_kernel<0, 2, 5>"))
+
+
+def counter_summary(dirs):
+    """Per-dispatch averages (whole GPU) of every counter collected in the given
+    rocprofv3 --pmc directories, for the kernels of COUNTER_KERNELS."""
+    agg = {}
+    for d in dirs:
+        _, ctrs = _rocpd(d)
+        for (kname, cname), vals in ctrs.items():
+            for label, prefix in COUNTER_KERNELS:
+                if prefix in kname:
+                    agg.setdefault(label, {})[cname] = sum(vals) / len(vals)
+    for label, _ in COUNTER_KERNELS:
+        if label not in agg:
+            continue
+        print(label)
+        for cname, v in sorted(agg[label].items()):
+            print(f"  {cname:28s} {v:16.1f}")
 
 
 def profile_summary(trace_dir, fetch_dir, write_dir):
