@@ -39,30 +39,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3), aligned(4)));
 
 __device__ __forceinline__ uint4 ld_stream16(const uint8_t *p) {
-#ifndef TQ_PLAIN_WEIGHT_LOADS
   const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   return make_uint4(t.x, t.y, t.z, t.w);
-#else
-  return *reinterpret_cast<const uint4 *>(p);
-#endif
 }
 
 __device__ __forceinline__ uint3 ld_stream12(const uint8_t *p) {
-#ifndef TQ_PLAIN_WEIGHT_LOADS
   const u32x3 t = __builtin_nontemporal_load(reinterpret_cast<const u32x3 *>(p));
   return make_uint3(t.x, t.y, t.z);
-#else
-  const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
-  return make_uint3(q[0], q[1], q[2]);
-#endif
 }
 
 __device__ __forceinline__ uint32_t ld_stream2(const uint8_t *p) {
-#ifndef TQ_PLAIN_WEIGHT_LOADS
   return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
-#else
-  return *reinterpret_cast<const uint16_t *>(p);
-#endif
 }
 
 // ---------------------------------------------------------------------

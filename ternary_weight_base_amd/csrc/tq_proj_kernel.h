@@ -22,9 +22,11 @@
 //      needs); barrier; then the weight loads of its first D groups;
 //   2. fp16 input: absmax pass; barrier;
 //   3. absmax -> quantise its slice in registers (bit-exact with
-//      tq_quant_act; int8 input arrives quantised), move each group's 32
-//      int8 words into SGPRs with v_readlane;
+//      tq_quant_act; int8 input arrives quantised); with LX the slice goes
+//      to LDS, and each group's 32 int8 words are read back as VGPR dot
+//      operands, else they move into SGPRs with v_readlane;
 //   4. for each group i: issue group i + D, then decode + dot group i.
+// Weight loads are nontemporal: each weight byte is read once per call.
 // Issuing everything at once stalls each wave on a full memory queue until
 // most of its data has arrived, so decode would only start after the whole
 // transfer; the D-deep pipeline lets decode run while later groups stream.
