@@ -1,0 +1,83 @@
+"""Host logic of bench.py's profile summaries (CPU): the dominant kernel's HBM
+traffic is its FETCH_SIZE / WRITE_SIZE per dispatch scaled by what the same
+counters read for the bench's 64 MiB device copy, and the counter summary
+averages each counter per dispatch.  Synthetic rocprofv3-style databases."""
+import json
+import os
+import sqlite3
+
+import pytest
+
+import bench
+
+DOM = "void tqproj::proj_kernel<0, 2, 2, 6, 2, true, true>(tqproj::ProjArgs)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _db(path, kernels=(), counters=()):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    c = sqlite3.connect(path)
+    if kernels:
+        c.execute("create table kernels (name text, duration integer)")
+        c.executemany("insert into kernels values (?, ?)", kernels)
+    if counters:
+        c.execute("create table counters_collection (kernel_name text, counter_name text, "
+                  "dispatch_id integer, value real)")
+        c.executemany("insert into counters_collection values (?, ?, ?, ?)", counters)
+    c.commit()
+    c.close()
+
+
+def test_profile_summary_scales_traffic_by_the_copy(tmp_path, monkeypatch, capsys):
+    kt, fe, wr = (str(tmp_path / d) for d in ("kt", "fetch", "write"))
+    _db(os.path.join(kt, "a", "kt.db"),
+        kernels=[(DOM, 12000), (DOM, 13000), ("other_kernel", 5000)])
+    # per dispatch the counter arrives split over instances (summed per dispatch);
+    # the copy reads half its true bytes (scale 2) and writes them all (scale 1)
+    _db(os.path.join(fe, "f.db"),
+        counters=[(COPY, "FETCH_SIZE", 1, 16384), (COPY, "FETCH_SIZE", 1, 16384),
+                  (COPY, "FETCH_SIZE", 2, 1000),              # a small upload copy
+                  (DOM, "FETCH_SIZE", 3, 9000), (DOM, "FETCH_SIZE", 3, 10000),
+                  (DOM, "FETCH_SIZE", 4, 21000)])
+    _db(os.path.join(wr, "w.db"),
+        counters=[(COPY, "WRITE_SIZE", 1, 65536), (COPY, "WRITE_SIZE", 2, 20000),
+                  (DOM, "WRITE_SIZE", 3, 300), (DOM, "WRITE_SIZE", 4, 500)])
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    bench.profile_summary(kt, fe, wr)
+    rec = json.loads(out.read_text())
+    assert rec["kernel"] == DOM
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["fetch_bytes"] == 20000 * 1024 * 2      # mean of 19000 and 21000 KiB, x2
+    assert rec["write_bytes"] == 400 * 1024            # mean of 300 and 500 KiB
+    assert rec["hbm_bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
+    assert rec["kernel_source_sha"] == bench.kernel_source_sha()
+    text = capsys.readouterr().out
+    assert "avg duration 12.500 us" in text
+
+
+def test_profile_summary_needs_the_calibration_copy(tmp_path, monkeypatch):
+    kt, fe, wr = (str(tmp_path / d) for d in ("kt", "fetch", "write"))
+    _db(os.path.join(kt, "kt.db"), kernels=[(DOM, 12000)])
+    _db(os.path.join(fe, "f.db"), counters=[(DOM, "FETCH_SIZE", 1, 9000)])
+    _db(os.path.join(wr, "w.db"), counters=[(DOM, "WRITE_SIZE", 1, 300)])
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "t.json"))
+    with pytest.raises(SystemExit):
+        bench.profile_summary(kt, fe, wr)
+    assert not (tmp_path / "t.json").exists()
+
+
+def test_counter_summary_averages_per_dispatch(tmp_path, capsys):
+    d = str(tmp_path / "pmc")
+    _db(os.path.join(d, "p.db"),
+        counters=[(DOM, "SQ_INSTS_VALU", 1, 100), (DOM, "SQ_INSTS_VALU", 1, 50),
+                  (DOM, "SQ_INSTS_VALU", 2, 250),
+                  ("void (anonymous namespace)::gemm_kernel<0, false>(...)", "SQ_INSTS_MFMA", 7, 64),
+                  ("unrelated", "SQ_INSTS_VALU", 9, 1)])
+    bench.counter_summary([d])
+    text = capsys.readouterr().out.splitlines()
+    assert text[0] == "gate/up"
+    assert text[1].split() == ["SQ_INSTS_VALU", "200.0"]   # (150 + 250) / 2 dispatches
+    assert text[2] == "prefill GEMM"
+    assert text[3].split() == ["SQ_INSTS_MFMA", "64.0"]
+    assert len(text) == 4
