@@ -81,3 +81,13 @@ def test_counter_summary_averages_per_dispatch(tmp_path, capsys):
     assert text[2] == "prefill GEMM"
     assert text[3].split() == ["SQ_INSTS_MFMA", "64.0"]
     assert len(text) == 4
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """--gpus N > 1 exits with a message: this build measures one GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
