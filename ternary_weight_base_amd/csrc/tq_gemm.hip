@@ -10,13 +10,19 @@
 // grid (NB, ceil(M / 128)), 256 threads (4 waves).  Per group the block's
 // 64 weight rows x 128 trits are decoded to int8 in LDS (canonical k order;
 // lane = row, wave = a quarter of the row's bytes, uniform branches, 16-byte
-// stores); each wave multiplies its 32 token rows by them with
+// stores), and the tile's 128 token rows x 128 activation bytes are staged
+// in LDS too; each wave multiplies its 32 token rows by the weights with
 // 2 x 4 x 2 v_mfma_i32_16x16x64_i8 and rescales the int32 group sums by
-// s[n][g] into fp32 accumulators.  The next group's weights and activation
-// fragments are loaded into registers while the current group is decoded
+// s[n][g] into fp32 accumulators.  The activations go through LDS because
+// the MFMA operand layout (lane l on token row l % 16) read straight from
+// memory puts every lane of a load on a different row: 64 vector-L1
+// accesses per instruction, and the L1 then bounds the loop.  Loaded 8
+// lanes to a 128-byte row they take 8.  The next group's weights and
+// activations are loaded into registers while the current group is decoded
 // and multiplied.  Grids with few tiles also split K into C chunks
-// (blockIdx.z), finished deterministically by the tile's last chunk.  A two-buffer variant that decodes group g + 1 while group
-// g's MFMAs run measured slower (one workgroup's waves then wait on both).
+// (blockIdx.z), finished deterministically by the tile's last chunk.  A
+// two-buffer variant that decodes group g + 1 while group g's MFMAs run
+// measured slower (one workgroup's waves then wait on both).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,26 +39,32 @@ using namespace tqdev;
 constexpr int kGemmBM = 128;    // token rows per workgroup: 4 waves x 32
 constexpr int kBtStride = 144;  // 128 trits + 16 bytes of padding per row
 
-// A 16-copy digit table (32 KB; the decode here is a small share of the
-// work, so two-way bank conflicts cost little): with the B tile, 41 KB per
-// workgroup, three workgroups per CU instead of two with the 64 KB table.  Entry v of copy c at byte
-// v * 128 + c * 8; lane l reads copy l % 16.
-constexpr int kLut16Copies = 16;
+// An 8-copy digit table (16 KB; the decode is a small share of the work,
+// so its bank conflicts cost little): with the B tile and the activation
+// tile, 41 KB per workgroup, three workgroups per CU.  Entry v of copy c at
+// byte v * 64 + c * 8; lane l reads copy l % 8.
+constexpr int kLut8Copies = 8;
 
-__device__ __forceinline__ void fill_lut16(uint2 *lut) {
-  // 256 threads: thread v fills the 16 copies of entry v, two per 16-byte store
+__device__ __forceinline__ void fill_lut8(uint2 *lut) {
+  // 256 threads: thread v fills the 8 copies of entry v, two per 16-byte store
   const int v = threadIdx.x;
   const uint2 e = b3_entry(v);
-  uint4 *row = reinterpret_cast<uint4 *>(lut + v * kLut16Copies);
+  uint4 *row = reinterpret_cast<uint4 *>(lut + v * kLut8Copies);
 #pragma unroll
-  for (int k = 0; k < kLut16Copies / 2; k++) row[(k + v) & (kLut16Copies / 2 - 1)] = make_uint4(e.x, e.y, e.x, e.y);
+  for (int k = 0; k < kLut8Copies / 2; k++) row[(k + v) & (kLut8Copies / 2 - 1)] = make_uint4(e.x, e.y, e.x, e.y);
 }
 
 template <int j>
-__device__ __forceinline__ uint2 lut16_byte(const uint2 *lut, const uint32_t (&w)[7], uint32_t laneoff) {
+__device__ __forceinline__ uint2 lut8_byte(const uint2 *lut, const uint32_t (&w)[7], uint32_t laneoff) {
   const uint32_t byte = __builtin_amdgcn_ubfe(w[j >> 2], 8 * (j & 3), 8);
-  return *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(lut) + ((byte << 7) | laneoff));
+  return *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(lut) + ((byte << 6) | laneoff));
 }
+
+// The activation tile of one group, 128 token rows x 128 bytes, in LDS.
+// 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7) of the row, so
+// that both the coalesced fill (8 lanes per row) and the MFMA operand reads
+// (16 lanes on 16 rows, one chunk each) touch all 64 banks once.
+__device__ __forceinline__ int as_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 template <int FMT, bool SUMS>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W,
@@ -63,8 +75,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
                                                    uint32_t *__restrict__ counters, int M, int N, int K,
                                                    int C) {
   constexpr int WPG = FMT == 0 ? 7 : 9;
-  __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLut16Copies : 1];
+  __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLut8Copies : 1];
   __shared__ __attribute__((aligned(16))) int8_t Bt[64 * kBtStride];
+  __shared__ __attribute__((aligned(16))) int8_t As[kGemmBM * 128];
   __shared__ float bscale[64];
 
   const Layout L(FMT, N, K);
@@ -76,24 +89,30 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
   const int gbeg = (int)((uint32_t)(c * G) / (uint32_t)C);
   const int gend = (int)((uint32_t)((c + 1) * G) / (uint32_t)C);
   const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
-  if (FMT == 0) fill_lut16(lut);
+  if (FMT == 0) fill_lut8(lut);
 
   // decode role: row dr = lane of the block (padding rows past Wb give zero
   // trits and scale), part dp = wave
   const int dr = lane, dp = wave, lr = min(dr, Wb - 1);
   const bool row_live = dr < Wb;
-  const uint32_t laneoff = (uint32_t)(lane & 15) * 8u;
+  const uint32_t laneoff = (uint32_t)(lane & 7) * 8u;
   int8_t *brow = Bt + dr * kBtStride;
 
   // MFMA role
   const int li = lane & 15, slot = lane >> 4;
-  const int8_t *qrow[2];
-  bool qok[2];
+
+  // activation fill role: chunk i * 256 + tid of the tile is row r = that / 8,
+  // stored chunk that % 8 (global chunk ac = stored ^ ((r >> 1) & 7)), so the
+  // 8 lanes of a row read its 128 bytes together.  Rows past M read row
+  // M - 1: MFMA output row i depends on activation row i alone, and those
+  // rows are never stored.
+  const int8_t *arow[4];
+  int aoff[4];
 #pragma unroll
-  for (int ms = 0; ms < 2; ms++) {
-    const int row = m0 + 32 * wave + 16 * ms + li;
-    qok[ms] = row < M;
-    qrow[ms] = q + (size_t)min(row, M - 1) * K;
+  for (int i = 0; i < 4; i++) {
+    const int idx = i * 256 + tid, r = idx >> 3, cs = idx & 7, ac = cs ^ ((r >> 1) & 7);
+    arow[i] = q + (size_t)min(m0 + r, M - 1) * K + ac * 16;
+    aoff[i] = r * 128 + cs * 16;
   }
 
   auto load_w = [&](int g, uint32_t (&w)[WPG]) {
@@ -109,12 +128,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
       w[8] = *reinterpret_cast<const uint16_t *>(gb + Wb * 32 + lr * 2);
     }
   };
-  auto load_a = [&](int g, v2l (&af)[2][2]) {
+  auto load_a = [&](int g, v2l (&st)[4]) {
 #pragma unroll
-    for (int ms = 0; ms < 2; ms++)
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++)
-        af[ms][ks] = *reinterpret_cast<const v2l *>(qrow[ms] + (size_t)g * 128 + 64 * ks + 16 * slot);
+    for (int i = 0; i < 4; i++) st[i] = *reinterpret_cast<const v2l *>(arow[i] + (size_t)g * 128);
   };
 
   v4i acc32[2][4];
@@ -127,9 +143,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
       for (int v = 0; v < 4; v++) accf[ms][ns][v] = 0.0f;
 
   uint32_t wcur[WPG], wnext[WPG];
-  v2l acur[2][2], anext[2][2];
+  v2l ast[4];  // the activation tile's chunks of this thread, one group ahead of As
   load_w(gbeg, wcur);
-  load_a(gbeg, acur);
+  load_a(gbeg, ast);
 
   for (int g = gbeg; g < gend; g++) {
     const int gn = min(g + 1, gend - 1);
@@ -143,8 +159,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
       // k-block c (16 trits) = digits 0..3 of bytes 4c..4c+3; digit 4 of byte j is k = 100 + j
 #define TQ_BLK(C)                                                                         \
   {                                                                                       \
-    const uint2 e0 = lut16_byte<4 * (C)>(lut, w, laneoff), e1 = lut16_byte<4 * (C) + 1>(lut, w, laneoff); \
-    const uint2 e2 = lut16_byte<4 * (C) + 2>(lut, w, laneoff), e3 = lut16_byte<4 * (C) + 3>(lut, w, laneoff); \
+    const uint2 e0 = lut8_byte<4 * (C)>(lut, w, laneoff), e1 = lut8_byte<4 * (C) + 1>(lut, w, laneoff); \
+    const uint2 e2 = lut8_byte<4 * (C) + 2>(lut, w, laneoff), e3 = lut8_byte<4 * (C) + 3>(lut, w, laneoff); \
     *reinterpret_cast<uint4 *>(brow + 16 * (C)) = make_uint4(e0.x, e1.x, e2.x, e3.x);    \
     *reinterpret_cast<uint32_t *>(brow + 100 + 4 * (C)) =                                 \
         e0.y | (e1.y << 8) | (e2.y << 16) | (e3.y << 24);                                 \
@@ -154,7 +170,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
       if (dp == 2) {
         TQ_BLK(2)
         // byte 24: k = 96..99 and 124; byte 25: k = 125..127 (digit 0 a pad)
-        const uint2 e24 = lut16_byte<24>(lut, w, laneoff), e25 = lut16_byte<25>(lut, w, laneoff);
+        const uint2 e24 = lut8_byte<24>(lut, w, laneoff), e25 = lut8_byte<25>(lut, w, laneoff);
         *reinterpret_cast<uint32_t *>(brow + 96) = e24.x;
         *reinterpret_cast<uint32_t *>(brow + 124) = (e25.x & 0xFFFFFF00u) | e24.y;
       }
@@ -177,15 +193,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
       }
       if (dp == 0) bscale[dr] = row_live ? half_bits(wcur[8]) : 0.0f;
     }
-    load_a(gn, anext);
+#pragma unroll
+    for (int i = 0; i < 4; i++) *reinterpret_cast<v2l *>(As + aoff[i]) = ast[i];
+    load_a(gn, ast);
     __syncthreads();
 
     // ---- MFMA: wave rows m0 + 32*wave + 16*ms + i, all 64 columns --------
+    v2l acur[2][2];
 #pragma unroll
     for (int ms = 0; ms < 2; ms++)
 #pragma unroll
       for (int ks = 0; ks < 2; ks++)
-        if (!qok[ms]) acur[ms][ks] = v2l{0, 0};
+        acur[ms][ks] = *reinterpret_cast<const v2l *>(As + as_off(32 * wave + 16 * ms + li, 4 * ks + slot));
 #pragma unroll
     for (int ms = 0; ms < 2; ms++)
 #pragma unroll
@@ -223,10 +242,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
     }
 #pragma unroll
     for (int i = 0; i < WPG; i++) wcur[i] = wnext[i];
-#pragma unroll
-    for (int ms = 0; ms < 2; ms++)
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++) acur[ms][ks] = anext[ms][ks];
   }
   if (SUMS) return;
   // A tile cut into C K chunks: every chunk publishes its fp32 sums (value i
