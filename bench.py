@@ -515,7 +515,8 @@ def _rocpd(d):
 # Kernels whose counters counter_summary reports (name prefixes, B3 instantiations).
 COUNTER_KERNELS = (("QKV", "proj_kernel<0, 1, 1, 5,"), ("O", "proj_kernel<0, 1, 1, 3,"),
                    ("gate/up", "proj_kernel<0, 2, 2, 6,"), ("down", "proj_kernel<0, 1, 2, 6,"),
-                   ("prefill GEMM", "gemm_kernel<0, false>"),
+                   ("prefill GEMM, 128-row tiles (gate shape)", "gemm_kernel<0, false, 2>"),
+                   ("prefill GEMM, 256-row tiles (down shape)", "gemm_kernel<0, false, 4>"),
                    ("small-batch gate/up", "mgemv_kernel<0, 2, 5>"))
 
 

@@ -36,7 +36,6 @@ namespace {
 
 using namespace tqdev;
 
-constexpr int kGemmBM = 128;    // token rows per workgroup: 4 waves x 32
 constexpr int kBtStride = 144;  // 128 trits + 16 bytes of padding per row
 
 // An 8-copy digit table (16 KB; the decode is a small share of the work,
@@ -66,7 +65,8 @@ __device__ __forceinline__ uint2 lut8_byte(const uint2 *lut, const uint32_t (&w)
 // (16 lanes on 16 rows, one chunk each) touch all 64 banks once.
 __device__ __forceinline__ int as_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-template <int FMT, bool SUMS>
+// TM: 16-row token sub-tiles per wave (2 or 4); a workgroup covers 64 * TM token rows.
+template <int FMT, bool SUMS, int TM>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W,
                                                    const int8_t *__restrict__ q,
                                                    const float *__restrict__ a_scale,
@@ -77,14 +77,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
   constexpr int WPG = FMT == 0 ? 7 : 9;
   __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLut8Copies : 1];
   __shared__ __attribute__((aligned(16))) int8_t Bt[64 * kBtStride];
-  __shared__ __attribute__((aligned(16))) int8_t As[kGemmBM * 128];
+  constexpr int BM = 64 * TM;   // token rows per workgroup
+  constexpr int NA = 2 * TM;    // activation chunks per thread per group
+  __shared__ __attribute__((aligned(16))) int8_t As[BM * 128];
   __shared__ float bscale[64];
 
   const Layout L(FMT, N, K);
   const int G = (int)L.G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.x, m0 = blockIdx.y * kGemmBM, c = blockIdx.z;
+  const int b = blockIdx.x, m0 = blockIdx.y * BM, c = blockIdx.z;
   // K chunk c of C: groups gbeg .. gend - 1 (unsigned 32-bit: C G < 2^22)
   const int gbeg = (int)((uint32_t)(c * G) / (uint32_t)C);
   const int gend = (int)((uint32_t)((c + 1) * G) / (uint32_t)C);
@@ -106,10 +108,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
   // 8 lanes of a row read its 128 bytes together.  Rows past M read row
   // M - 1: MFMA output row i depends on activation row i alone, and those
   // rows are never stored.
-  const int8_t *arow[4];
-  int aoff[4];
+  const int8_t *arow[NA];
+  int aoff[NA];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < NA; i++) {
     const int idx = i * 256 + tid, r = idx >> 3, cs = idx & 7, ac = cs ^ ((r >> 1) & 7);
     arow[i] = q + (size_t)min(m0 + r, M - 1) * K + ac * 16;
     aoff[i] = r * 128 + cs * 16;
@@ -128,22 +130,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
       w[8] = *reinterpret_cast<const uint16_t *>(gb + Wb * 32 + lr * 2);
     }
   };
-  auto load_a = [&](int g, v2l (&st)[4]) {
+  auto load_a = [&](int g, v2l (&st)[NA]) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) st[i] = *reinterpret_cast<const v2l *>(arow[i] + (size_t)g * 128);
+    for (int i = 0; i < NA; i++) st[i] = *reinterpret_cast<const v2l *>(arow[i] + (size_t)g * 128);
   };
 
-  v4i acc32[2][4];
-  float accf[2][4][4];
+  v4i acc32[TM][4];
+  float accf[TM][4][4];
 #pragma unroll
-  for (int ms = 0; ms < 2; ms++)
+  for (int ms = 0; ms < TM; ms++)
 #pragma unroll
     for (int ns = 0; ns < 4; ns++)
 #pragma unroll
       for (int v = 0; v < 4; v++) accf[ms][ns][v] = 0.0f;
 
   uint32_t wcur[WPG], wnext[WPG];
-  v2l ast[4];  // the activation tile's chunks of this thread, one group ahead of As
+  v2l ast[NA];  // the activation tile's chunks of this thread, one group ahead of As
   load_w(gbeg, wcur);
   load_a(gbeg, ast);
 
@@ -194,19 +196,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
       if (dp == 0) bscale[dr] = row_live ? half_bits(wcur[8]) : 0.0f;
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++) *reinterpret_cast<v2l *>(As + aoff[i]) = ast[i];
+    for (int i = 0; i < NA; i++) *reinterpret_cast<v2l *>(As + aoff[i]) = ast[i];
     load_a(gn, ast);
     __syncthreads();
 
     // ---- MFMA: wave rows m0 + 32*wave + 16*ms + i, all 64 columns --------
-    v2l acur[2][2];
+    v2l acur[TM][2];
 #pragma unroll
-    for (int ms = 0; ms < 2; ms++)
+    for (int ms = 0; ms < TM; ms++)
 #pragma unroll
       for (int ks = 0; ks < 2; ks++)
-        acur[ms][ks] = *reinterpret_cast<const v2l *>(As + as_off(32 * wave + 16 * ms + li, 4 * ks + slot));
+        acur[ms][ks] = *reinterpret_cast<const v2l *>(As + as_off(16 * TM * wave + 16 * ms + li, 4 * ks + slot));
 #pragma unroll
-    for (int ms = 0; ms < 2; ms++)
+    for (int ms = 0; ms < TM; ms++)
 #pragma unroll
       for (int ns = 0; ns < 4; ns++) acc32[ms][ns] = v4i{0, 0, 0, 0};
 #pragma unroll
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
       for (int ns = 0; ns < 4; ns++)
         bf[ns] = *reinterpret_cast<const v2l *>(Bt + (16 * ns + li) * kBtStride + 64 * ks + 16 * slot);
 #pragma unroll
-      for (int ms = 0; ms < 2; ms++)
+      for (int ms = 0; ms < TM; ms++)
 #pragma unroll
         for (int ns = 0; ns < 4; ns++)
           acc32[ms][ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(acur[ms][ks], bf[ns], acc32[ms][ns], 0, 0, 0);
@@ -227,11 +229,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
       const int col = 16 * ns + li;
       const float sc = bscale[col];
 #pragma unroll
-      for (int ms = 0; ms < 2; ms++) {
+      for (int ms = 0; ms < TM; ms++) {
 #pragma unroll
         for (int v = 0; v < 4; v++) {
           if (SUMS) {
-            const int row = m0 + 32 * wave + 16 * ms + 4 * slot + v;
+            const int row = m0 + 16 * TM * wave + 16 * ms + 4 * slot + v;
             if (row < M && col < rows)
               sums[((size_t)row * N + (size_t)b * tq::kBlockRows + col) * G + g] = acc32[ms][ns][v];
           } else {
@@ -251,9 +253,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
   __shared__ int last_flag;
   if (C > 1) {
     const size_t tile = (size_t)blockIdx.y * gridDim.x + b, ntiles = (size_t)gridDim.x * gridDim.y;
-    float *mine = partials + ((size_t)c * ntiles + tile) * 256 * 32 + tid;
+    float *mine = partials + ((size_t)c * ntiles + tile) * 256 * (16 * TM) + tid;
 #pragma unroll
-    for (int ms = 0; ms < 2; ms++)
+    for (int ms = 0; ms < TM; ms++)
 #pragma unroll
       for (int ns = 0; ns < 4; ns++)
 #pragma unroll
@@ -268,15 +270,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
     __syncthreads();
     if (!last_flag) return;  // another chunk finishes this tile
 #pragma unroll
-    for (int ms = 0; ms < 2; ms++)
+    for (int ms = 0; ms < TM; ms++)
 #pragma unroll
       for (int ns = 0; ns < 4; ns++)
 #pragma unroll
         for (int v = 0; v < 4; v++) accf[ms][ns][v] = 0.0f;
     for (int cc = 0; cc < C; cc++) {
-      const float *src = partials + ((size_t)cc * ntiles + tile) * 256 * 32 + tid;
+      const float *src = partials + ((size_t)cc * ntiles + tile) * 256 * (16 * TM) + tid;
 #pragma unroll
-      for (int ms = 0; ms < 2; ms++)
+      for (int ms = 0; ms < TM; ms++)
 #pragma unroll
         for (int ns = 0; ns < 4; ns++)
 #pragma unroll
@@ -286,18 +288,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
     }
     // consumed: leave the workspace zero for the next call, whatever its shape
     for (int cc = 0; cc < C; cc++) {
-      float *dst = partials + ((size_t)cc * ntiles + tile) * 256 * 32 + tid;
+      float *dst = partials + ((size_t)cc * ntiles + tile) * 256 * (16 * TM) + tid;
 #pragma unroll
-      for (int k = 0; k < 32; k++)
+      for (int k = 0; k < 16 * TM; k++)
         __hip_atomic_store(dst + k * 256, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (tid == 0) __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 #pragma unroll
-  for (int ms = 0; ms < 2; ms++)
+  for (int ms = 0; ms < TM; ms++)
 #pragma unroll
     for (int v = 0; v < 4; v++) {
-      const int row = m0 + 32 * wave + 16 * ms + 4 * slot + v;
+      const int row = m0 + 16 * TM * wave + 16 * ms + 4 * slot + v;
       if (row >= M) continue;
       const float a = a_scale[row];
 #pragma unroll
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
 }
 
 struct GemmPlan {
-  int C;
+  int TM, C, tiles_y;
   size_t counters_bytes, partials_bytes;
 };
 
@@ -318,20 +320,43 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 #ifndef TQ_GEMM_TARGET
 #define TQ_GEMM_TARGET 768
 #endif
+#ifndef TQ_GEMM_TARGET4
+#define TQ_GEMM_TARGET4 512
+#endif
 
-// K chunks per tile: enough workgroups for about three per CU
-// (TQ_GEMM_TARGET), at least 8 groups per chunk; the debug group sums take
-// one chunk.
+// K chunks of `tiles` tiles for `target` concurrent workgroups: as many as
+// fit, at least 8 groups per chunk.
+int64_t gemm_chunks(int64_t tiles, int64_t G, int64_t target) {
+  int64_t C = target / tiles;
+  if (C > G / 8) C = G / 8;
+  return C < 1 ? 1 : C;
+}
+
+// Tile and K split.  TM = 2: 128 token rows per workgroup, three
+// workgroups per CU (TQ_GEMM_TARGET slots).  TM = 4: 256 rows, two per CU
+// (TQ_GEMM_TARGET4); it reads the decoded weights from LDS half as often per
+// MFMA, which about pays for the lost third workgroup, so it is taken where
+// it fills its slots at least as well: the share of slots busy over the
+// launch's rounds.  The debug group sums take TM = 2 and one chunk.
 GemmPlan gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, bool sums) {
   const Layout L(fmt, N, K);
-  const int64_t tiles = L.NB * ((M + kGemmBM - 1) / kGemmBM);
-  int64_t C = sums ? 1 : TQ_GEMM_TARGET / tiles;
-  if (C > L.G / 8) C = L.G / 8;
-  if (C < 1) C = 1;
   GemmPlan p;
+  p.TM = 2;
+  int64_t tiles = L.NB * ((M + 127) / 128), C = sums ? 1 : gemm_chunks(tiles, L.G, TQ_GEMM_TARGET);
+  if (!sums && M > 128) {
+    const int64_t t4 = L.NB * ((M + 255) / 256), c4 = gemm_chunks(t4, L.G, TQ_GEMM_TARGET4);
+    const int64_t wg2 = tiles * C, r2 = (wg2 + TQ_GEMM_TARGET - 1) / TQ_GEMM_TARGET;
+    const int64_t wg4 = t4 * c4, r4 = (wg4 + TQ_GEMM_TARGET4 - 1) / TQ_GEMM_TARGET4;
+    if (wg4 * r2 * TQ_GEMM_TARGET >= wg2 * r4 * TQ_GEMM_TARGET4) {
+      p.TM = 4;
+      tiles = t4;
+      C = c4;
+    }
+  }
   p.C = (int)C;
+  p.tiles_y = (int)((M + 64 * p.TM - 1) / (64 * p.TM));
   p.counters_bytes = C > 1 ? round256((size_t)tiles * 4) : 0;
-  p.partials_bytes = C > 1 ? round256((size_t)C * tiles * 256 * 32 * 4) : 0;
+  p.partials_bytes = C > 1 ? round256((size_t)C * tiles * 256 * 16 * p.TM * 4) : 0;
   return p;
 }
 
@@ -355,17 +380,19 @@ int tq_internal_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, co
   }
   uint32_t *counters = p.C > 1 ? (uint32_t *)ws : nullptr;
   float *partials = p.C > 1 ? (float *)((char *)ws + p.counters_bytes) : nullptr;
-  const dim3 grid((unsigned)L.NB, (unsigned)((M + kGemmBM - 1) / kGemmBM), (unsigned)p.C), block(256);
+  const dim3 grid((unsigned)L.NB, (unsigned)p.tiles_y, (unsigned)p.C), block(256);
   const uint8_t *Wb = (const uint8_t *)W;
-#define TQ_GEMM(F_, S_)                                                                               \
-  hipLaunchKernelGGL((gemm_kernel<F_, S_>), grid, block, 0, st, Wb, q, a, y, sums, partials, counters, \
+#define TQ_GEMM(F_, S_, TM_)                                                                               \
+  hipLaunchKernelGGL((gemm_kernel<F_, S_, TM_>), grid, block, 0, st, Wb, q, a, y, sums, partials, counters, \
                      (int)M, (int)N, (int)K, p.C)
   if (fmt == TQ_FMT_B3) {
-    if (sums) TQ_GEMM(0, true);
-    else TQ_GEMM(0, false);
+    if (sums) TQ_GEMM(0, true, 2);
+    else if (p.TM == 4) TQ_GEMM(0, false, 4);
+    else TQ_GEMM(0, false, 2);
   } else {
-    if (sums) TQ_GEMM(1, true);
-    else TQ_GEMM(1, false);
+    if (sums) TQ_GEMM(1, true, 2);
+    else if (p.TM == 4) TQ_GEMM(1, false, 4);
+    else TQ_GEMM(1, false, 2);
   }
 #undef TQ_GEMM
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;

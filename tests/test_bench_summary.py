@@ -72,13 +72,13 @@ def test_counter_summary_averages_per_dispatch(tmp_path, capsys):
     _db(os.path.join(d, "p.db"),
         counters=[(DOM, "SQ_INSTS_VALU", 1, 100), (DOM, "SQ_INSTS_VALU", 1, 50),
                   (DOM, "SQ_INSTS_VALU", 2, 250),
-                  ("void (anonymous namespace)::gemm_kernel<0, false>(...)", "SQ_INSTS_MFMA", 7, 64),
+                  ("void (anonymous namespace)::gemm_kernel<0, false, 4>(...)", "SQ_INSTS_MFMA", 7, 64),
                   ("unrelated", "SQ_INSTS_VALU", 9, 1)])
     bench.counter_summary([d])
     text = capsys.readouterr().out.splitlines()
     assert text[0] == "gate/up"
     assert text[1].split() == ["SQ_INSTS_VALU", "200.0"]   # (150 + 250) / 2 dispatches
-    assert text[2] == "prefill GEMM"
+    assert text[2] == "prefill GEMM, 256-row tiles (down shape)"
     assert text[3].split() == ["SQ_INSTS_MFMA", "64.0"]
     assert len(text) == 4
 

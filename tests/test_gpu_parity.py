@@ -262,6 +262,28 @@ def test_gemm_vs_oracle(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", [B3, TB])
+@pytest.mark.parametrize("M,N,K", [(300, 5120, 17408), (512, 14336, 1024)])
+def test_gemm_wide_tile_sampled(fmt, M, N, K):
+    """Shapes on which the GEMM takes 256-token tiles: a ragged last token
+    tile with a 3-way K split, and 448 tiles with no split; every token row
+    of 40 sampled output columns."""
+    say(f"gemm wide {FMTS[fmt]} M={M} N={N} K={K}")
+    tq = _tq()
+    t, s = weights(N, K, 6700 + M)
+    q, a = _quant_gpu(acts_f16(M, K, 6800 + M))
+    W = upload_blob(fmt, t, s)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = tq.workspace(fmt, M, N, K)
+    tq.tq_gemm(fmt, M, N, K, W, q, a, y, ws)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 63, 64, N - 1], np.random.default_rng(2).integers(0, N, 36)]))
+    ref = oracle.gemv_rows(t, s, q.cpu().numpy(), a.cpu().numpy(), rows)
+    assert_close(y.cpu().numpy()[:, rows], ref, "gemm wide")
+    if ws is not None:
+        assert not ws.any().item()
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
 @pytest.mark.parametrize("N,K", [(17408, 5120), (5120, 17408)])
 def test_gemm_prefill_full_size_sampled(fmt, N, K):
     """The prefill shapes at full size (M = 512), checked on 48 sampled
