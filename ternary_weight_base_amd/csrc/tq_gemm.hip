@@ -7,13 +7,13 @@
 // as the one a GPU runs well when a prompt forms large matrices ("Ternary
 // Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section "后面还有没有优化空间").
 //
-// grid (NB, ceil(M / 128)), 256 threads (4 waves).  Per group the block's
-// 64 weight rows x 128 trits are decoded to int8 in LDS (canonical k order;
-// lane = row, wave = a quarter of the row's bytes, uniform branches, 16-byte
-// stores), and the tile's 128 token rows x 128 activation bytes are staged
-// in LDS too; each wave multiplies its 32 token rows by the weights with
-// 2 x 4 x 2 v_mfma_i32_16x16x64_i8 and rescales the int32 group sums by
-// s[n][g] into fp32 accumulators.  The activations go through LDS because
+// grid (NB, ceil(M / (64 TM)), C), 256 threads (4 waves), TM = 2 or 4.
+// Per group the block's 64 weight rows x 128 trits are decoded to int8 in
+// LDS (canonical k order; lane = row, wave = a quarter of the row's bytes,
+// uniform branches, 16-byte stores), and the tile's 64 TM token rows x 128
+// activation bytes are staged in LDS too; each wave multiplies its 16 TM
+// token rows by the weights with TM x 4 x 2 v_mfma_i32_16x16x64_i8 and
+// rescales the int32 group sums by s[n][g] into fp32 accumulators.  The activations go through LDS because
 // the MFMA operand layout (lane l on token row l % 16) read straight from
 // memory puts every lane of a load on a different row: 64 vector-L1
 // accesses per instruction, and the L1 then bounds the loop.  Loaded 8
@@ -40,7 +40,7 @@ constexpr int kBtStride = 144;  // 128 trits + 16 bytes of padding per row
 
 // An 8-copy digit table (16 KB; the decode is a small share of the work,
 // so its bank conflicts cost little): with the B tile and the activation
-// tile, 41 KB per workgroup, three workgroups per CU.  Entry v of copy c at
+// tile, 41 KB per workgroup at TM = 2, three workgroups per CU.  Entry v of copy c at
 // byte v * 64 + c * 8; lane l reads copy l % 8.
 constexpr int kLut8Copies = 8;
 
@@ -59,7 +59,7 @@ __device__ __forceinline__ uint2 lut8_byte(const uint2 *lut, const uint32_t (&w)
   return *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(lut) + ((byte << 6) | laneoff));
 }
 
-// The activation tile of one group, 128 token rows x 128 bytes, in LDS.
+// The activation tile of one group, 64 TM token rows x 128 bytes, in LDS.
 // 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7) of the row, so
 // that both the coalesced fill (8 lanes per row) and the MFMA operand reads
 // (16 lanes on 16 rows, one chunk each) touch all 64 banks once.
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
     load_a(gn, ast);
     __syncthreads();
 
-    // ---- MFMA: wave rows m0 + 32*wave + 16*ms + i, all 64 columns --------
+    // ---- MFMA: wave rows m0 + 16*TM*wave + 16*ms + i, all 64 columns -----
     v2l acur[TM][2];
 #pragma unroll
     for (int ms = 0; ms < TM; ms++)
