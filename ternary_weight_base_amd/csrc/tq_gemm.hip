@@ -336,8 +336,8 @@ int64_t gemm_chunks(int64_t tiles, int64_t G, int64_t target) {
 // workgroups per CU (TQ_GEMM_TARGET slots).  TM = 4: 256 rows, two per CU
 // (TQ_GEMM_TARGET4); it reads the decoded weights from LDS half as often per
 // MFMA, which about pays for the lost third workgroup, so it is taken where
-// it fills its slots at least as well: the share of slots busy over the
-// launch's rounds.  The debug group sums take TM = 2 and one chunk.
+// it fills its slots better: the share of slots busy over the launch's
+// rounds (on a tie the 128-row tile measured faster).  The debug group sums take TM = 2 and one chunk.
 GemmPlan gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, bool sums) {
   const Layout L(fmt, N, K);
   GemmPlan p;
@@ -347,7 +347,7 @@ GemmPlan gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, bool sums) {
     const int64_t t4 = L.NB * ((M + 255) / 256), c4 = gemm_chunks(t4, L.G, TQ_GEMM_TARGET4);
     const int64_t wg2 = tiles * C, r2 = (wg2 + TQ_GEMM_TARGET - 1) / TQ_GEMM_TARGET;
     const int64_t wg4 = t4 * c4, r4 = (wg4 + TQ_GEMM_TARGET4 - 1) / TQ_GEMM_TARGET4;
-    if (wg4 * r2 * TQ_GEMM_TARGET >= wg2 * r4 * TQ_GEMM_TARGET4) {
+    if (wg4 * r2 * TQ_GEMM_TARGET > wg2 * r4 * TQ_GEMM_TARGET4) {
       p.TM = 4;
       tiles = t4;
       C = c4;
