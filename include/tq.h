@@ -264,7 +264,7 @@ size_t tq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 /* y[M][N] as tq_gemv, for any M >= 1.  M <= 16 runs the decode GEMV; larger
  * M unpacks trits to int8 in LDS and runs int8 MFMA with int32
  * accumulation per group, then scales per group in fp32, on output tiles of
- * 128 or 256 tokens x 64 rows (chosen per shape).  When the output has few
+ * 64, 128 or 256 tokens x 64 rows (chosen per shape).  When the output has few
  * tiles, K is also split into chunks whose fp32 sums meet through the
  * workspace in a fixed order (tq_gemm_workspace_bytes > 0: pass a
  * zero-filled workspace of that size, 16-byte aligned; every call leaves it

@@ -7,7 +7,7 @@
 // as the one a GPU runs well when a prompt forms large matrices ("Ternary
 // Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section "后面还有没有优化空间").
 //
-// grid (NB, ceil(M / (64 TM)), C), 256 threads (4 waves), TM = 2 or 4.
+// grid (NB, ceil(M / (64 TM)), C), 256 threads (4 waves), TM = 1, 2 or 4.
 // Per group the block's 64 weight rows x 128 trits are decoded to int8 in
 // LDS (canonical k order; lane = row, wave = a quarter of the row's bytes,
 // uniform branches, 16-byte stores), and the tile's 64 TM token rows x 128
@@ -65,7 +65,7 @@ __device__ __forceinline__ uint2 lut8_byte(const uint2 *lut, const uint32_t (&w)
 // (16 lanes on 16 rows, one chunk each) touch all 64 banks once.
 __device__ __forceinline__ int as_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-// TM: 16-row token sub-tiles per wave (2 or 4); a workgroup covers 64 * TM token rows.
+// TM: 16-row token sub-tiles per wave (1, 2 or 4); a workgroup covers 64 * TM token rows.
 template <int FMT, bool SUMS, int TM>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W,
                                                    const int8_t *__restrict__ q,
@@ -323,6 +323,9 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 #ifndef TQ_GEMM_TARGET4
 #define TQ_GEMM_TARGET4 512
 #endif
+#ifndef TQ_GEMM_TARGET1
+#define TQ_GEMM_TARGET1 1024
+#endif
 
 // K chunks of `tiles` tiles for `target` concurrent workgroups: as many as
 // fit, at least 8 groups per chunk.
@@ -343,7 +346,12 @@ GemmPlan gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, bool sums) {
   GemmPlan p;
   p.TM = 2;
   int64_t tiles = L.NB * ((M + 127) / 128), C = sums ? 1 : gemm_chunks(tiles, L.G, TQ_GEMM_TARGET);
-  if (!sums && M > 128) {
+  if (!sums && M <= 64) {
+    // one 64-row tile row: TM = 1, four workgroups per CU (TQ_GEMM_TARGET1)
+    p.TM = 1;
+    tiles = L.NB;
+    C = gemm_chunks(tiles, L.G, TQ_GEMM_TARGET1);
+  } else if (!sums && M > 128) {
     const int64_t t4 = L.NB * ((M + 255) / 256), c4 = gemm_chunks(t4, L.G, TQ_GEMM_TARGET4);
     const int64_t wg2 = tiles * C, r2 = (wg2 + TQ_GEMM_TARGET - 1) / TQ_GEMM_TARGET;
     const int64_t wg4 = t4 * c4, r4 = (wg4 + TQ_GEMM_TARGET4 - 1) / TQ_GEMM_TARGET4;
@@ -388,10 +396,12 @@ int tq_internal_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, co
   if (fmt == TQ_FMT_B3) {
     if (sums) TQ_GEMM(0, true, 2);
     else if (p.TM == 4) TQ_GEMM(0, false, 4);
+    else if (p.TM == 1) TQ_GEMM(0, false, 1);
     else TQ_GEMM(0, false, 2);
   } else {
     if (sums) TQ_GEMM(1, true, 2);
     else if (p.TM == 4) TQ_GEMM(1, false, 4);
+    else if (p.TM == 1) TQ_GEMM(1, false, 1);
     else TQ_GEMM(1, false, 2);
   }
 #undef TQ_GEMM

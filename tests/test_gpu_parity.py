@@ -248,7 +248,7 @@ def test_gate_up_swiglu_vs_oracle(fmt, M, N, K):
 # ------------------------------------------------------------------ GEMM ---
 
 @pytest.mark.parametrize("fmt", [B3, TB])
-@pytest.mark.parametrize("M,N,K", [(17, 130, 640), (200, 64, 1024), (512, 1000, 5120)])
+@pytest.mark.parametrize("M,N,K", [(17, 130, 640), (40, 1000, 5120), (200, 64, 1024), (512, 1000, 5120)])
 def test_gemm_vs_oracle(fmt, M, N, K):
     say(f"gemm {FMTS[fmt]} M={M} N={N} K={K}")
     tq = _tq()
