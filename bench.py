@@ -549,7 +549,7 @@ def profile_summary(trace_dir, fetch_dir, write_dir):
     calib = 64 << 20
     dom = [n for n in durs if "proj_kernel<0, 2, 2," in n]
     print("kernel                                                        calls   avg_us   total_ms")
-    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:20]:
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:24]:
         print(f"{name[:60]:60s} {len(v):7d} {sum(v) / len(v) / 1e3:8.3f} {sum(v) / 1e6:10.3f}")
 
     def per_dispatch(ctrs, cname, pick):
