@@ -275,14 +275,40 @@ int tq_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_
 
 /* ---- device: parity hooks (same decode / integer core as above) ------- */
 
-/* trits[N][K] (int8, device) decoded on the GPU by the GEMV kernels' decoder. */
+/* trits[N][K] (int8, device) decoded on the GPU with the decode kernels'
+ * per-format decoder (B3 digit table, 2B code masks, BP plane masks). */
 int tq_debug_unpack(int fmt, int64_t N, int64_t K, const void *W, int8_t *trits, void *stream);
 
-/* S[M][N][K/128] int32 (device): the per-group integer sums exactly as the
- * GEMV (use_gemm_path = 0, M <= 16) or the MFMA GEMM (use_gemm_path = 1)
- * computes them before scaling. */
+/* The integer core of the method, S[m][n][g] = sum_{i<128} t[n][128g+i] *
+ * q[m][128g+i] (the signed sum taken before the group's FP16 scale, "三值
+ * 权重 27B 压到 5.9GB｜本地部署成本账单重算", section 三), written as int32
+ * S[M][N][K/128] (device) by the very kernel, launch plan (work split, tile
+ * height, K chunks) and decode path that the matching product call runs,
+ * with the scaling and the reductions replaced by a store of each sum:
+ *   use_gemm_path = 0: tq_gemv's kernel (M = 1: the one-token projection
+ *     kernel, either activation form as its grid picks; M = 2..16: the
+ *     MFMA GEMV), all three formats (BP: M = 1 only);
+ *   use_gemm_path = 1: tq_gemm's MFMA GEMM kernel and plan for this M (any
+ *     M >= 1, also M <= 16, which tq_gemm itself sends to the GEMV), B3/2B.
+ * No workspace is used. */
 int tq_debug_group_sums(int fmt, int64_t M, int64_t N, int64_t K, const void *W,
                         const int8_t *q, int32_t *S, int use_gemm_path, void *stream);
+
+/* As tq_debug_group_sums for the two matrices of tq_gemv_gate_up_swiglu,
+ * through that call's kernel and plan: S is int32 [2][M][N][K/128] (gate,
+ * then up).  1 <= M <= 16; BP: M = 1. */
+int tq_debug_gate_up_sums(int fmt, int64_t M, int64_t N, int64_t K, const void *Wg,
+                          const void *Wu, const int8_t *q, int32_t *S, void *stream);
+
+/* As tq_debug_group_sums for tq_gemv_quant (the decode stack's projection
+ * launches): the same kernel and plan, with its fused quantiser turning x
+ * (fp16, or fp32 with its block maxima) into int8 inside the launch, writes
+ * S int32 [nmat][N][K/128] (nmat 2 with Wu) from those int8 values and, if
+ * a_scale is not NULL, the activation scale it derived (fp32 [1]).
+ * Arguments as tq_gemv_quant; no workspace. */
+int tq_debug_gemv_quant_sums(int fmt, int64_t N, int64_t K, const void *W, const void *Wu,
+                             int x_dtype, const void *x, const float *x_bmax, int64_t x_nb,
+                             int32_t *S, float *a_scale, void *stream);
 
 /* ---- device: measurement hook ----------------------------------------- */
 

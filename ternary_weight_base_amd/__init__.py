@@ -35,7 +35,8 @@ EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant
            "tq_gemm_workspace_bytes", "tq_gemm", "tq_debug_unpack", "tq_debug_group_sums",
            "tq_gemv_quant_workspace_bytes", "tq_gemv_quant",
            "tq_decode_stack_workspace_bytes", "tq_decode_stack", "tq_hadamard_quant_act",
-           "tq_ternarize", "tq_debug_stream_read")
+           "tq_ternarize", "tq_debug_stream_read", "tq_debug_gate_up_sums",
+           "tq_debug_gemv_quant_sums")
 
 
 class TqLayer(ctypes.Structure):
@@ -75,6 +76,8 @@ def _load():
         "tq_hadamard_quant_act": ([I, I64, I64, P, P, P, P, P], I),
         "tq_ternarize": ([I64, I64, P, P, P], I),
         "tq_debug_stream_read": ([P, SZ, P, I64, P], I),
+        "tq_debug_gate_up_sums": ([I, I64, I64, I64, P, P, P, P, P], I),
+        "tq_debug_gemv_quant_sums": ([I, I64, I64, P, P, I, P, P, I64, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -208,6 +211,23 @@ def tq_debug_unpack(fmt, N, K, W, trits, stream=None) -> None:
 def tq_debug_group_sums(fmt, M, N, K, W, q, S, use_gemm_path=False, stream=None) -> None:
     _check(lib.tq_debug_group_sums(fmt, M, N, K, _ptr(W), _ptr(q), _ptr(S), int(use_gemm_path),
                                    _stream(stream)), "tq_debug_group_sums")
+
+
+def tq_debug_gate_up_sums(fmt, M, N, K, Wg, Wu, q, S, stream=None) -> None:
+    """S int32 [2][M][N][K/128]: the gate and up group sums of tq_gemv_gate_up_swiglu's kernel."""
+    _check(lib.tq_debug_gate_up_sums(fmt, M, N, K, _ptr(Wg), _ptr(Wu), _ptr(q), _ptr(S),
+                                     _stream(stream)), "tq_debug_gate_up_sums")
+
+
+def tq_debug_gemv_quant_sums(fmt, N, K, W, Wu, x, S, x_bmax=None, a_scale=None, stream=None) -> None:
+    """S int32 [nmat][N][K/128] (and a_scale fp32 [1]) from tq_gemv_quant's kernel,
+    which quantises x (fp16 [K], or fp32 [K] with x_bmax) inside the launch."""
+    import torch
+    dtype = {torch.float16: TQ_F16, torch.float32: TQ_F32}.get(x.dtype, -1)
+    nb = 0 if x_bmax is None else x_bmax.numel()
+    _check(lib.tq_debug_gemv_quant_sums(fmt, N, K, _ptr(W), _ptr(Wu), dtype, _ptr(x), _ptr(x_bmax), nb,
+                                        _ptr(S), _ptr(a_scale), _stream(stream)),
+           "tq_debug_gemv_quant_sums")
 
 
 def tq_debug_stream_read(src, sink, stream=None) -> None:

@@ -35,10 +35,17 @@ def _run(cmd):
     _report(cmd, r.returncode, r.stdout + r.stderr)
 
 
-def _run_parallel(cmds):
-    procs = [(c, subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
-             for c in cmds]
-    for c, p in procs:
+def _run_parallel(cmds, jobs=None):
+    """Run the compile commands, at most `jobs` at once (default: the CPUs this
+    process may use, capped at 16)."""
+    jobs = jobs or max(1, min(16, len(os.sched_getaffinity(0))))
+    pending, running = list(cmds), []
+    while pending or running:
+        while pending and len(running) < jobs:
+            c = pending.pop(0)
+            running.append((c, subprocess.Popen(c, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                                text=True)))
+        c, p = running.pop(0)
         out, _ = p.communicate()
         _report(c, p.returncode, out)
 
@@ -53,11 +60,19 @@ def build() -> str:
               "-c", os.path.join(CSRC, src), "-o", o])
         host_objs.append(o)
     objs, cmds = [], []
-    for src in ("tq_kernels.hip", "tq_proj.hip", "tq_proj_b3.hip", "tq_proj_b3_sg.hip", "tq_proj_2b.hip",
-                "tq_proj_2b_sg.hip", "tq_proj_bp.hip", "tq_proj_bp_sg.hip", "tq_gemv_mfma.hip",
-                "tq_hadamard.hip", "tq_gemm.hip", "tq_stream.hip"):
-        o = os.path.join(bdir, src.replace(".hip", ".o"))
-        cmds.append(["hipcc", *HIP_FLAGS, "-I", INC, "-I", CSRC, "-c", os.path.join(CSRC, src),
+    units = [(src, src.replace(".hip", ".o"), []) for src in
+             ("tq_kernels.hip", "tq_proj.hip", "tq_gemv_mfma.hip", "tq_hadamard.hip", "tq_gemm.hip",
+              "tq_stream.hip")]
+    # the projection kernel: one object per (packed format, activation form, output kind)
+    for fmt, fname in ((0, "b3"), (1, "2b"), (2, "bp")):
+        for lx in (1, 0):
+            for sums in (0, 1):
+                obj = f"tq_proj_{fname}{'' if lx else '_sg'}{'_sums' if sums else ''}.o"
+                units.append(("tq_proj_inst.hip", obj,
+                              [f"-DTQ_INST_FMT={fmt}", f"-DTQ_INST_LX={lx}", f"-DTQ_INST_SUMS={sums}"]))
+    for src, obj, defs in units:
+        o = os.path.join(bdir, obj)
+        cmds.append(["hipcc", *HIP_FLAGS, *defs, "-I", INC, "-I", CSRC, "-c", os.path.join(CSRC, src),
                      "-o", o])
         objs.append(o)
     _run_parallel(cmds)

@@ -13,8 +13,6 @@ namespace tqdev {
 
 constexpr int kLutCopies = 32;   // one table copy per lane of a half wave
 constexpr int kLutEntries = 256; // byte values; 243..255 map to zero trits
-constexpr int kWavesMax = 8;     // waves per GEMV workgroup
-constexpr int kGsMax = 8;        // groups per wave slice (all prefetched)
 
 typedef long v2l __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -120,17 +118,12 @@ __device__ __forceinline__ uint2 b3_byte(const uint2 *lut, const uint32_t (&w)[7
   return lut_lookup<j & 3>(lut, w[j >> 2], laneoff);
 }
 
-// Activations of one group for MT rows, as 32 words per row: either held in
-// (scalar) registers, or read through wave-uniform pointers on use.
+// Activations of one group for MT rows, as 32 words per row, held in
+// (scalar or vector) registers.
 template <int MT>
 struct XRegs {
   uint32_t v[MT][32];
   __device__ __forceinline__ uint32_t get(int m, int i) const { return v[m][i]; }
-};
-template <int MT>
-struct XPtrs {
-  const uint32_t *__restrict__ p[MT];
-  __device__ __forceinline__ uint32_t get(int m, int i) const { return p[m][i]; }
 };
 
 // Integer core of one B3 group for MT activation rows.

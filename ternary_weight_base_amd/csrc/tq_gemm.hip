@@ -340,18 +340,19 @@ int64_t gemm_chunks(int64_t tiles, int64_t G, int64_t target) {
 // (TQ_GEMM_TARGET4); it reads the decoded weights from LDS half as often per
 // MFMA, which about pays for the lost third workgroup, so it is taken where
 // it fills its slots better: the share of slots busy over the launch's
-// rounds (on a tie the 128-row tile measured faster).  The debug group sums take TM = 2 and one chunk.
-GemmPlan gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, bool sums) {
+// rounds (on a tie the 128-row tile measured faster).  The group-sum hook
+// takes the same plan.
+GemmPlan gemm_plan(int fmt, int64_t M, int64_t N, int64_t K) {
   const Layout L(fmt, N, K);
   GemmPlan p;
   p.TM = 2;
-  int64_t tiles = L.NB * ((M + 127) / 128), C = sums ? 1 : gemm_chunks(tiles, L.G, TQ_GEMM_TARGET);
-  if (!sums && M <= 64) {
+  int64_t tiles = L.NB * ((M + 127) / 128), C = gemm_chunks(tiles, L.G, TQ_GEMM_TARGET);
+  if (M <= 64) {
     // one 64-row tile row: TM = 1, four workgroups per CU (TQ_GEMM_TARGET1)
     p.TM = 1;
     tiles = L.NB;
     C = gemm_chunks(tiles, L.G, TQ_GEMM_TARGET1);
-  } else if (!sums && M > 128) {
+  } else if (M > 128) {
     const int64_t t4 = L.NB * ((M + 255) / 256), c4 = gemm_chunks(t4, L.G, TQ_GEMM_TARGET4);
     const int64_t wg2 = tiles * C, r2 = (wg2 + TQ_GEMM_TARGET - 1) / TQ_GEMM_TARGET;
     const int64_t wg4 = t4 * c4, r4 = (wg4 + TQ_GEMM_TARGET4 - 1) / TQ_GEMM_TARGET4;
@@ -371,39 +372,40 @@ GemmPlan gemm_plan(int fmt, int64_t M, int64_t N, int64_t K, bool sums) {
 }  // namespace
 
 size_t tq_internal_gemm_ws_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
-  const GemmPlan p = gemm_plan(fmt, M, N, K, false);
+  const GemmPlan p = gemm_plan(fmt, M, N, K);
   return p.counters_bytes + p.partials_bytes;
 }
 
 // Arguments already checked by the caller (shape, alignment); the workspace
-// (zero-filled before its first use, left zero) is checked here.
+// (zero-filled before its first use, left zero) is checked here.  With
+// `sums` (the parity hook) the same plan runs the group-sum instantiation:
+// every K chunk stores its own groups' sums, no workspace is used.
 int tq_internal_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
                      const float *a, float *y, int32_t *sums, void *ws, size_t ws_bytes, hipStream_t st) {
   const Layout L(fmt, N, K);
-  const GemmPlan p = gemm_plan(fmt, M, N, K, sums != nullptr);
-  if (p.C > 1) {
+  const GemmPlan p = gemm_plan(fmt, M, N, K);
+  if (p.C > 1 && !sums) {
     if (!ws) return TQ_ERR_NULL;
     if (((uintptr_t)ws & 15u) != 0) return TQ_ERR_ALIGN;
     if (ws_bytes < p.counters_bytes + p.partials_bytes) return TQ_ERR_SIZE;
   }
-  uint32_t *counters = p.C > 1 ? (uint32_t *)ws : nullptr;
-  float *partials = p.C > 1 ? (float *)((char *)ws + p.counters_bytes) : nullptr;
+  uint32_t *counters = p.C > 1 && !sums ? (uint32_t *)ws : nullptr;
+  float *partials = p.C > 1 && !sums ? (float *)((char *)ws + p.counters_bytes) : nullptr;
   const dim3 grid((unsigned)L.NB, (unsigned)p.tiles_y, (unsigned)p.C), block(256);
   const uint8_t *Wb = (const uint8_t *)W;
 #define TQ_GEMM(F_, S_, TM_)                                                                               \
   hipLaunchKernelGGL((gemm_kernel<F_, S_, TM_>), grid, block, 0, st, Wb, q, a, y, sums, partials, counters, \
                      (int)M, (int)N, (int)K, p.C)
+#define TQ_GEMM_TM(F_, S_)            \
+  if (p.TM == 4) TQ_GEMM(F_, S_, 4);  \
+  else if (p.TM == 1) TQ_GEMM(F_, S_, 1); \
+  else TQ_GEMM(F_, S_, 2);
   if (fmt == TQ_FMT_B3) {
-    if (sums) TQ_GEMM(0, true, 2);
-    else if (p.TM == 4) TQ_GEMM(0, false, 4);
-    else if (p.TM == 1) TQ_GEMM(0, false, 1);
-    else TQ_GEMM(0, false, 2);
+    if (sums) { TQ_GEMM_TM(0, true) } else { TQ_GEMM_TM(0, false) }
   } else {
-    if (sums) TQ_GEMM(1, true, 2);
-    else if (p.TM == 4) TQ_GEMM(1, false, 4);
-    else if (p.TM == 1) TQ_GEMM(1, false, 1);
-    else TQ_GEMM(1, false, 2);
+    if (sums) { TQ_GEMM_TM(1, true) } else { TQ_GEMM_TM(1, false) }
   }
+#undef TQ_GEMM_TM
 #undef TQ_GEMM
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }

@@ -19,7 +19,9 @@
 // MFMAs per tile cover the group; the int32 result is scaled by the group's
 // scale (moved through the same transpose) into fp32 accumulators.  Waves
 // meet in LDS (the digit table's space, reused), K chunks of a block through
-// the workspace, finished by the last chunk in chunk order.
+// the workspace, finished by the last chunk in chunk order.  The SUMS
+// instantiation (parity hook) runs the same plan, decode, transpose and
+// MFMAs and stores the int32 group sums instead of scaling them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,6 +45,7 @@ struct MArgs {
   const int8_t *q;        // [M][K]
   const float *a_scale;   // [M]
   float *out;             // [M][N]
+  int32_t *sums;          // SUMS kernels only: [nmat][M][N][K/128]
   float *partials;        // counter meet: [C][nmat][NB][64 * kOut]
   uint32_t *counters;     // counter meet: [NB], zero on entry and on exit
   void *slots;            // exchange meet: [NB][C - 1][64 * kOut] words (32-bit one
@@ -126,7 +129,7 @@ __device__ __forceinline__ void decode_half(const uint2 *lut, uint32_t laneoff, 
   }
 }
 
-template <int FMT, int NMAT, int GS>
+template <int FMT, int NMAT, int GS, bool SUMS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void mgemv_kernel(MArgs A) {
   constexpr int WPG = FMT == 0 ? 7 : 9;
   constexpr int D0 = GS < 2 ? GS : 2;
@@ -242,6 +245,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
         for (int n = 0; n < 4; n++) asm volatile("" : "+v"(acc[n]));  // ... and end here
       }
+      if constexpr (SUMS) {
+        // element v of tile n: token 4 (lane / 16) + v, row 16 n + lane % 16
+        const int rows = (int)L.valid_rows(b);
+#pragma unroll
+        for (int n = 0; n < 4; n++)
+#pragma unroll
+          for (int v = 0; v < 4; v++) {
+            const int m = 4 * ls + v, r = 16 * n + li;
+            if (live && m < M && r < rows)
+              A.sums[(((size_t)mat * M + m) * N + (size_t)b * tq::kBlockRows + r) * G + g0 + i] = acc[n][v];
+          }
+        continue;
+      }
 #pragma unroll
       for (int n = 0; n < 4; n++)
 #pragma unroll
@@ -251,6 +267,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     if (i + D0 < GS) issue(i + D0);  // after this group's registers are free
   }
+  if constexpr (SUMS) return;
 
   // ---- waves meet in LDS (the table is no longer read) ---------------------
   __syncthreads();
@@ -381,12 +398,12 @@ MPlan plan(int fmt, int64_t N, int64_t K, int nmat) {
   return p;
 }
 
-template <int FMT, int NMAT>
+template <int FMT, int NMAT, bool SUMS>
 int launch(const MPlan &p, const MArgs &A, hipStream_t st) {
   const dim3 grid((unsigned)(p.NB * p.C)), block(kThreads);
 #define TQ_CASE(G_)                                                                   \
   case G_:                                                                            \
-    hipLaunchKernelGGL((mgemv_kernel<FMT, NMAT, G_>), grid, block, 0, st, A);         \
+    hipLaunchKernelGGL((mgemv_kernel<FMT, NMAT, G_, SUMS>), grid, block, 0, st, A);   \
     break;
   switch (p.gs) {
     TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5) TQ_CASE(6)
@@ -420,6 +437,7 @@ int tq_internal_mgemv(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, 
   A.q = q;
   A.a_scale = a_scale;
   A.out = y;
+  A.sums = nullptr;
   A.meet = p.meet ? 1 : 0;
   A.counters = p.counters_bytes ? reinterpret_cast<uint32_t *>(ws) : nullptr;
   A.partials = p.partials_bytes ? reinterpret_cast<float *>((char *)ws + p.counters_bytes) : nullptr;
@@ -428,6 +446,31 @@ int tq_internal_mgemv(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, 
   A.N = (int)N;
   A.K = (int)K;
   A.C = p.C;
-  if (fmt == TQ_FMT_B3) return nmat == 2 ? launch<0, 2>(p, A, st) : launch<0, 1>(p, A, st);
-  return nmat == 2 ? launch<1, 2>(p, A, st) : launch<1, 1>(p, A, st);
+  if (fmt == TQ_FMT_B3) return nmat == 2 ? launch<0, 2, false>(p, A, st) : launch<0, 1, false>(p, A, st);
+  return nmat == 2 ? launch<1, 2, false>(p, A, st) : launch<1, 1, false>(p, A, st);
+}
+
+// The group-sum hook of the same call: the same plan and kernel, int32 sums
+// out (S: [nmat][M][N][K/128]); no workspace, no output.
+int tq_internal_mgemv_sums(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const void *W1,
+                           const int8_t *q, int32_t *S, hipStream_t st) {
+  const int nmat = W1 ? 2 : 1;
+  const MPlan p = plan(fmt, N, K, nmat);
+  MArgs A;
+  A.W0 = (const uint8_t *)W0;
+  A.W1 = (const uint8_t *)(W1 ? W1 : W0);
+  A.q = q;
+  A.a_scale = nullptr;
+  A.out = nullptr;
+  A.sums = S;
+  A.meet = p.meet ? 1 : 0;
+  A.counters = nullptr;
+  A.partials = nullptr;
+  A.slots = nullptr;
+  A.M = (int)M;
+  A.N = (int)N;
+  A.K = (int)K;
+  A.C = p.C;
+  if (fmt == TQ_FMT_B3) return nmat == 2 ? launch<0, 2, true>(p, A, st) : launch<0, 1, true>(p, A, st);
+  return nmat == 2 ? launch<1, 2, true>(p, A, st) : launch<1, 1, true>(p, A, st);
 }

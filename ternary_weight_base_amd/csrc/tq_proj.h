@@ -1,7 +1,7 @@
 // tq_proj.h -- shared declarations of the one-token projection kernel
-// (device side in tq_proj_kernel.h, instantiated per packed format in
-// tq_proj_b3.hip and tq_proj_2b.hip) and its host driver (tq_proj.hip).
-// Internal to the library.
+// (device side in tq_proj_kernel.h, instantiated per packed format,
+// activation form and output kind by tq_proj_inst.hip) and its host driver
+// (tq_proj.hip).  Internal to the library.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -78,6 +78,8 @@ struct ProjArgs {
   int split, C, W, I;    // split mode, chunks per block, workgroups and items (mode 1)
   int meet;              // 1: exchange meet, 0: counter meet
   int slot_stride;       // exchange meet: tree nodes per block (pieces - 1)
+  int32_t *sums;         // group-sum kernels only: [nmat][N][K/128], the int32 sums
+  float *sums_scale;     // group-sum kernels only (optional): the activation scale
 };
 
 struct Plan {
@@ -98,10 +100,12 @@ struct WsLayout {
 // Launch the kernel of packed format FMT (0 B3, 1 2B, 2 BP) for this plan
 // (nmat 1 or 2, in_kind one of InKind), with the activations in VGPRs
 // through LDS (LX, grids of at most kLxMaxGrid workgroups) or in SGPRs.
-// Returns a tq_status.  Instantiated one (FMT, LX) pair per source file
-// (tq_proj_b3.hip, tq_proj_b3_sg.hip, ...), so that they compile in
-// parallel.
-template <int FMT, bool LX>
+// SUMS: the same kernel with the same work split, quantiser and integer
+// core, storing each (row, group)'s int32 sum into A.sums instead of
+// scaling and reducing them (the parity hooks).  Returns a tq_status.
+// tq_proj_inst.hip instantiates one (FMT, LX, SUMS) triple per object, so
+// that they compile in parallel.
+template <int FMT, bool LX, bool SUMS>
 int launch_lx(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st);
 
 }  // namespace tqproj

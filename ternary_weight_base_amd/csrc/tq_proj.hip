@@ -88,10 +88,12 @@ WsLayout ws_layout(const Plan *ps, int n) {
 }
 
 // One projection, its cut blocks meeting through the workspace at `ws`
-// laid out as `w` (zero on entry, left zero).
+// laid out as `w` (zero on entry, left zero).  With `sums` the same plan
+// runs the group-sum instantiation instead (no workspace, no output).
 int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, int in_kind,
                 const void *in, const float *in_aux, int in_nb, float *out, float *out_bmax,
-                char *ws, const WsLayout &w, hipStream_t st, const int8_t *out_signs = nullptr) {
+                char *ws, const WsLayout &w, hipStream_t st, const int8_t *out_signs = nullptr,
+                int32_t *sums = nullptr, float *sums_scale = nullptr) {
   const int nmat = W1 ? 2 : 1;
   const Plan p = plan_proj(fmt, N, K, nmat);
   ProjArgs A;
@@ -107,10 +109,13 @@ int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, i
   if (p.split && (!p.meet_ok || out_signs)) return TQ_ERR_SHAPE;
   A.meet = p.meet_ok && !out_signs;
   A.slot_stride = p.slot_stride;
-  A.counters = p.cut ? reinterpret_cast<uint32_t *>(ws + w.counters) : nullptr;
-  A.partials = p.cut ? reinterpret_cast<float *>(ws + w.partials) : nullptr;
-  A.meet_max = A.meet ? reinterpret_cast<uint32_t *>(ws + w.meet) : nullptr;
-  A.slots = A.meet ? (void *)(ws + w.slots) : nullptr;
+  const bool has_ws = ws != nullptr;
+  A.counters = p.cut && has_ws ? reinterpret_cast<uint32_t *>(ws + w.counters) : nullptr;
+  A.partials = p.cut && has_ws ? reinterpret_cast<float *>(ws + w.partials) : nullptr;
+  A.meet_max = A.meet && has_ws ? reinterpret_cast<uint32_t *>(ws + w.meet) : nullptr;
+  A.slots = A.meet && has_ws ? (void *)(ws + w.slots) : nullptr;
+  A.sums = sums;
+  A.sums_scale = sums_scale;
   A.N = (int)N;
   A.K = (int)K;
   A.in_nb = in_nb;
@@ -119,11 +124,16 @@ int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, i
   A.W = p.W;
   A.I = p.I;
   const bool lx = p.grid <= kLxMaxGrid;
-  if (fmt == TQ_FMT_B3)
-    return lx ? launch_lx<0, true>(p, A, nmat, in_kind, st) : launch_lx<0, false>(p, A, nmat, in_kind, st);
-  if (fmt == TQ_FMT_2B)
-    return lx ? launch_lx<1, true>(p, A, nmat, in_kind, st) : launch_lx<1, false>(p, A, nmat, in_kind, st);
-  return lx ? launch_lx<2, true>(p, A, nmat, in_kind, st) : launch_lx<2, false>(p, A, nmat, in_kind, st);
+#define TQ_LAUNCH(F_)                                                                         \
+  if (sums)                                                                                   \
+    return lx ? launch_lx<F_, true, true>(p, A, nmat, in_kind, st)                            \
+              : launch_lx<F_, false, true>(p, A, nmat, in_kind, st);                          \
+  return lx ? launch_lx<F_, true, false>(p, A, nmat, in_kind, st)                             \
+            : launch_lx<F_, false, false>(p, A, nmat, in_kind, st);
+  if (fmt == TQ_FMT_B3) { TQ_LAUNCH(0) }
+  if (fmt == TQ_FMT_2B) { TQ_LAUNCH(1) }
+  TQ_LAUNCH(2)
+#undef TQ_LAUNCH
 }
 
 WsLayout proj_ws(int fmt, int64_t N, int64_t K, int nmat) {
@@ -166,7 +176,6 @@ StackWs stack_ws(int fmt, int64_t hidden, int64_t inter, int64_t qkv_out, int64_
 // ---------------------------------------------------------------------
 // One-token GEMV entry points (called by tq_gemv / tq_gemv_gate_up_swiglu)
 // ---------------------------------------------------------------------
-bool tq_internal_proj_fits(int64_t N, int64_t K) { return shape_ok(N, K); }
 
 size_t tq_internal_proj_ws_bytes(int fmt, int64_t N, int64_t K, int nmat) {
   return proj_ws_bytes(fmt, N, K, nmat);
@@ -182,6 +191,15 @@ int tq_internal_proj_int8(int fmt, int64_t N, int64_t K, const void *W0, const v
     if (ws_bytes < w.total) return TQ_ERR_SIZE;
   }
   return launch_proj(fmt, N, K, W0, W1, kInInt8, q, a_scale, 0, y, nullptr, (char *)ws, w, st);
+}
+
+// The group-sum hook of tq_gemv / tq_gemv_gate_up_swiglu at M = 1: the
+// same plan and kernel with int32 sums out (S: [nmat][N][K/128]).
+int tq_internal_proj_sums_int8(int fmt, int64_t N, int64_t K, const void *W0, const void *W1,
+                               const int8_t *q, int32_t *S, hipStream_t st) {
+  const WsLayout w = proj_ws(fmt, N, K, W1 ? 2 : 1);
+  return launch_proj(fmt, N, K, W0, W1, kInInt8, q, nullptr, 0, nullptr, nullptr, nullptr, w, st,
+                     nullptr, S, nullptr);
 }
 
 // ---------------------------------------------------------------------
@@ -212,6 +230,21 @@ extern "C" int tq_gemv_quant(int fmt, int64_t N, int64_t K, const void *W, const
   }
   return launch_proj(fmt, N, K, W, Wu, x_dtype == TQ_F16 ? kInF16 : kInF32, x, x_bmax, (int)x_nb,
                      y, y_bmax, (char *)ws, w, (hipStream_t)stream, y_signs);
+}
+
+extern "C" int tq_debug_gemv_quant_sums(int fmt, int64_t N, int64_t K, const void *W, const void *Wu,
+                                        int x_dtype, const void *x, const float *x_bmax, int64_t x_nb,
+                                        int32_t *S, float *a_scale, void *stream) {
+  if (!W || !x || !S || (x_dtype == TQ_F32 && !x_bmax)) return TQ_ERR_NULL;
+  if (!fmt_ok(fmt)) return TQ_ERR_FORMAT;
+  if (x_dtype != TQ_F16 && x_dtype != TQ_F32) return TQ_ERR_DTYPE;
+  if (!shape_ok(N, K) || (x_dtype == TQ_F32 && x_nb != K / 64)) return TQ_ERR_SHAPE;
+  if (!aligned16(W) || (Wu && !aligned16(Wu)) || !aligned16(x) || !aligned4(S) ||
+      (x_bmax && !aligned4(x_bmax)) || (a_scale && !aligned4(a_scale)))
+    return TQ_ERR_ALIGN;
+  const WsLayout w = proj_ws(fmt, N, K, Wu ? 2 : 1);
+  return launch_proj(fmt, N, K, W, Wu, x_dtype == TQ_F16 ? kInF16 : kInF32, x, x_bmax, (int)x_nb,
+                     nullptr, nullptr, nullptr, w, (hipStream_t)stream, nullptr, S, a_scale);
 }
 
 // ---------------------------------------------------------------------

@@ -1,6 +1,7 @@
 // tq_proj_kernel.h -- the one-token projection kernel: activation quantiser
-// fused in, weight stream software-pipelined.  Included by the per-format
-// instantiation units tq_proj_{b3,2b,bp}.hip and tq_proj_{b3,2b,bp}_sg.hip.
+// fused in, weight stream software-pipelined.  Included by the instantiation
+// unit tq_proj_inst.hip (compiled once per packed format, activation form
+// and output kind).
 //
 // What is computed is the decode GEMV of include/tq.h: per group of 128
 // weights an integer dot of decoded trits with int8 activations, scaled by
@@ -33,7 +34,9 @@
 // The waves' partial sums meet in LDS; the pieces of a block cut between
 // workgroups then meet through the workspace (by exchange along a fixed
 // tree, or through a counter: tq_proj.h), so results do not depend on
-// timing.
+// timing.  The SUMS instantiation (parity hooks) runs every step above
+// unchanged but stores each (row, group)'s int32 sum and skips the scaling
+// and the reductions.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -110,7 +113,7 @@ __device__ __forceinline__ void *meet_slot0(const ProjArgs &A, int b, int lane) 
 // 140 VGPRs, so it is launched only for grids of at most one workgroup per
 // CU (two waves per SIMD, 256 VGPRs); bigger grids keep the SGPR form
 // within 128 VGPRs (two workgroups per CU).
-template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX>
+template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX, bool SUMS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LX ? 2 : 4)))
 void proj_kernel(ProjArgs A) {
   constexpr int WPG = FMT == 0 ? 7 : 9;   // words per (row, group) in registers
@@ -254,7 +257,7 @@ void proj_kernel(ProjArgs A) {
   // ---- 3. absmax, quantise the slice ----------------------------------------
   float a_scale;
   if constexpr (IN == kInInt8) {
-    a_scale = A.in_aux[0];
+    a_scale = SUMS ? 0.0f : A.in_aux[0];
   } else {
     float amax = 0.0f;
     if constexpr (IN == kInF16) {
@@ -359,6 +362,11 @@ void proj_kernel(ProjArgs A) {
         }
         sc = half_bits(wd[mat][i][8]);
       }
+      if constexpr (SUMS) {
+        if (live && lane < (int)L.valid_rows(sb[i]))
+          A.sums[((size_t)mat * N + (size_t)sb[i] * tq::kBlockRows + lane) * G + sg[i]] = S[0];
+        continue;
+      }
       const float s = live ? sc : 0.0f;
 #pragma unroll
       for (int p = 0; p < NPART; p++) {
@@ -366,6 +374,11 @@ void proj_kernel(ProjArgs A) {
         asm volatile("" : "+v"(acc[p][mat]));  // ... and ends here: one matrix at a time
       }
     }
+  }
+
+  if constexpr (SUMS) {
+    if (wg == 0 && tid == 0 && A.sums_scale) *A.sums_scale = a_scale;
+    return;
   }
 
   // ---- 5. reduce: waves in LDS, cut blocks through the workspace ----------
@@ -473,13 +486,13 @@ void proj_kernel(ProjArgs A) {
   }
 }
 
-template <int FMT, int NMAT, int IN, bool LX>
+template <int FMT, int NMAT, int IN, bool LX, bool SUMS>
 int launch_in(const Plan &p, const ProjArgs &A, hipStream_t st) {
   constexpr int D = NMAT == 2 ? TQ_PROJ_D2 : TQ_PROJ_D1;
   const dim3 grid((unsigned)p.grid), block(kThreads);
-#define TQ_CASE(G_, S_)                                                                      \
-  case G_:                                                                                   \
-    hipLaunchKernelGGL((proj_kernel<FMT, NMAT, IN, G_, D, S_, LX>), grid, block, 0, st, A);  \
+#define TQ_CASE(G_, S_)                                                                            \
+  case G_:                                                                                         \
+    hipLaunchKernelGGL((proj_kernel<FMT, NMAT, IN, G_, D, S_, LX, SUMS>), grid, block, 0, st, A);  \
     break;
   if constexpr (NMAT == 1) {
     switch (p.gs) {
@@ -502,16 +515,16 @@ int launch_in(const Plan &p, const ProjArgs &A, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
-template <int FMT, bool LX>
+template <int FMT, bool LX, bool SUMS>
 int launch_lx(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st) {
   if (nmat == 2) {
-    if (in_kind == kInInt8) return launch_in<FMT, 2, kInInt8, LX>(p, A, st);
-    if (in_kind == kInF16) return launch_in<FMT, 2, kInF16, LX>(p, A, st);
-    return launch_in<FMT, 2, kInF32, LX>(p, A, st);
+    if (in_kind == kInInt8) return launch_in<FMT, 2, kInInt8, LX, SUMS>(p, A, st);
+    if (in_kind == kInF16) return launch_in<FMT, 2, kInF16, LX, SUMS>(p, A, st);
+    return launch_in<FMT, 2, kInF32, LX, SUMS>(p, A, st);
   }
-  if (in_kind == kInInt8) return launch_in<FMT, 1, kInInt8, LX>(p, A, st);
-  if (in_kind == kInF16) return launch_in<FMT, 1, kInF16, LX>(p, A, st);
-  return launch_in<FMT, 1, kInF32, LX>(p, A, st);
+  if (in_kind == kInInt8) return launch_in<FMT, 1, kInInt8, LX, SUMS>(p, A, st);
+  if (in_kind == kInF16) return launch_in<FMT, 1, kInF16, LX, SUMS>(p, A, st);
+  return launch_in<FMT, 1, kInF32, LX, SUMS>(p, A, st);
 }
 
 

@@ -80,7 +80,7 @@ def test_decode_stack_small(fmt, L, hidden, inter, qkv_out, o_in):
     _check_layers(host, x, a, outs, FMTS[fmt])
 
 
-@pytest.mark.parametrize("fmt", [B3, BP])
+@pytest.mark.parametrize("fmt", [B3, TB, BP])
 def test_decode_stack_full_shapes_two_layers(fmt):
     """The 27B-shaped layer (hidden 5120, intermediate 17408, QKV 10240, O 8192),
     two layers."""

@@ -249,7 +249,10 @@ def test_device_entry_points_validate_on_host():
     # BP runs on the one-token kernel only
     assert L.tq_gemv(BP, 2, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
     assert L.tq_gemm(BP, 512, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
-    assert L.tq_debug_unpack(BP, 64, 128, FAKE, FAKE, None) == -5
+    assert L.tq_debug_group_sums(BP, 2, 64, 128, FAKE, FAKE, FAKE, 0, None) == -5
+    assert L.tq_debug_group_sums(BP, 1, 64, 128, FAKE, FAKE, FAKE, 1, None) == -5
+    assert L.tq_debug_gate_up_sums(BP, 2, 64, 128, FAKE, FAKE, FAKE, FAKE, None) == -5
+    assert L.tq_debug_unpack(3, 64, 128, FAKE, FAKE, None) == -5
     assert tq.tq_gemv_workspace_bytes(BP, 2, 5120, 8192) == 0
     assert tq.tq_gemv_workspace_bytes(BP, 1, 5120, 8192) > 0
     # gemm
@@ -268,6 +271,18 @@ def test_device_entry_points_validate_on_host():
     assert L.tq_debug_group_sums(B3, 17, 64, 128, FAKE, FAKE, FAKE, 0, None) == -2
     assert L.tq_debug_group_sums(B3, 1, 64, 128, FAKE, FAKE, ODD, 1, None) == -3
     assert L.tq_debug_group_sums(B3, 1, 64, 128, FAKE, MIS, FAKE, 1, None) == -3
+    assert L.tq_debug_gate_up_sums(B3, 1, 64, 128, FAKE, None, FAKE, FAKE, None) == -1
+    assert L.tq_debug_gate_up_sums(B3, 17, 64, 128, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert L.tq_debug_gate_up_sums(B3, 1, 64, 128, FAKE, MIS, FAKE, FAKE, None) == -3
+    # fused-quantiser sums: (fmt, N, K, W, Wu, x_dtype, x, x_bmax, x_nb, S, a_scale, stream)
+    Q = L.tq_debug_gemv_quant_sums
+    assert Q(B3, 64, 256, FAKE, None, 0, FAKE, None, 0, None, None, None) == -1
+    assert Q(B3, 64, 256, FAKE, None, 1, FAKE, None, 4, FAKE, None, None) == -1
+    assert Q(B3, 64, 256, FAKE, None, 2, FAKE, None, 0, FAKE, None, None) == -6
+    assert Q(B3, 64, 256, FAKE, None, 1, FAKE, FAKE, 3, FAKE, None, None) == -2
+    assert Q(7, 64, 256, FAKE, None, 0, FAKE, None, 0, FAKE, None, None) == -5
+    assert Q(B3, 64, 256, FAKE, None, 0, MIS, None, 0, FAKE, None, None) == -3
+    assert Q(B3, 64, 256, FAKE, None, 0, FAKE, None, 0, FAKE, ODD, None) == -3
 
 
 def test_decode_stack_validates_on_host():
