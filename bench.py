@@ -62,7 +62,7 @@ def parse():
 
 
 # The sources the dominant kernel (the projection kernel) is built from.
-DOMINANT_SOURCES = ("tq_proj.h", "tq_proj_kernel.h", "tq_proj.hip", "tq_proj_b3.hip", "tq_device.h",
+DOMINANT_SOURCES = ("tq_proj.h", "tq_proj_kernel.h", "tq_proj.hip", "tq_proj_inst.hip", "tq_device.h",
                     "tq_layout.h", "../../include/tq.h")
 
 
@@ -141,6 +141,11 @@ def main():
     def token():
         tq.tq_decode_stack(fmt, L, HIDDEN, INTER, QKV_OUT, O_IN, layers, x_in, a_in,
                            y_qkv, y_o, h, y_dn, st_ws)
+
+    # the same token through the persistent kernel (one launch per 32 layers)
+    def token_persistent():
+        tq.tq_decode_stack(fmt, L, HIDDEN, INTER, QKV_OUT, O_IN, layers, x_in, a_in,
+                           y_qkv, y_o, h, y_dn, st_ws, persistent=True)
 
     # the same token with the FFN input rotated online (block-64 Hadamard and
     # signs, folded into the O projection's epilogue)
@@ -227,6 +232,8 @@ def main():
     assert torch.isfinite(y_dn).all().item() and torch.isfinite(h).all().item(), "non-finite"
     tok_s = 1000.0 / ms_per_step
     stream_gbps = stack.step_weight_bytes / (ms_per_step * 1e-3) / 1e9
+    persistent_ms = time_graph(capture(token_persistent), max(3, args.steps // 4), 1)
+    assert tq.stack_timeouts(st_ws) == 0, "a wait of the persistent stack kernel gave up"
     sep_ms = time_graph(capture(token_separate), max(3, args.steps // 4), 1)
     rot_ms = time_graph(capture(token_rot), max(3, args.steps // 4), 1)
 
@@ -311,6 +318,7 @@ def main():
         "weight_stream_frac_of_8TBps": round(stream_gbps / PEAK_HBM_GBPS, 4),
         "weight_stream_frac_of_measured_read_ceiling": round(stream_gbps / read_gbps, 4),
         "hbm_read_ceiling": read_ceiling,
+        "stack_persistent_tok_s": round(1000.0 / persistent_ms, 2),
         "separate_launch_tok_s": round(1000.0 / sep_ms, 2),
         "ffn_hadamard_tok_s": round(1000.0 / rot_ms, 2),
         "roofline": roofline,

@@ -106,8 +106,16 @@ size_t tq_packed_bytes(int fmt, int64_t N, int64_t K);
 
 /* Pack trits[N][K] (int8 in {-1,0,1}, row-major) and scales[N][K/128]
  * (IEEE fp16 bit patterns, finite) into dst (host memory, >= dst_bytes).
- * Host only; the caller uploads the blob.  TQ_ERR_VALUE on a bad trit or a
- * non-finite scale, TQ_ERR_SIZE if dst_bytes is too small. */
+ * The formats are the pages' packed ternary codes with one FP16 scale per
+ * group: B3, base-3 digits that the decode kernel unpacks back to -1/0/+1
+ * before the integer dot ("Ternary Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…",
+ * section "Decode 为什么只能算一般"); 2B, trits stored on a 2-bit grid
+ * (pwwt.cn/news/4940051, section 1.2); BP, nonzero and sign bit-planes
+ * (the Bonsai page, section "后面还有没有优化空间", first item); each
+ * re-tiled at load time into the order the kernels consume it (same
+ * section, second item).  Host only; the caller uploads the blob.
+ * TQ_ERR_VALUE on a bad trit or a non-finite scale, TQ_ERR_SIZE if
+ * dst_bytes is too small. */
 int tq_pack(int fmt, int64_t N, int64_t K, const int8_t *trits, const uint16_t *scales,
             void *dst, size_t dst_bytes);
 
@@ -134,7 +142,11 @@ int tq_unpack(int fmt, int64_t N, int64_t K, const void *src, size_t src_bytes,
 
 /* ---- device: activation quantiser ------------------------------------- */
 
-/* Per row m of x[M][K] (dtype TQ_F16 or TQ_F32, device):
+/* The per-token Q8 activation quantiser that feeds the integer dots
+ * ("Ternary Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section
+ * "后面还有没有优化空间", first item: the dot sums Q8 activations; the same
+ * page's section "Decode 为什么只能算一般" times this step at about 1.1 us
+ * per call).  Per row m of x[M][K] (dtype TQ_F16 or TQ_F32, device):
  *   a = max_k |x|; a == 0 -> a_scale[m] = 0, q = 0;
  *   else a_scale[m] = a/127, q[m][k] = clamp(rint(x * (127/a)), -127, 127),
  *   all in IEEE fp32 with round-to-nearest-even (bit-exact with the CPU
@@ -175,13 +187,23 @@ int tq_hadamard_quant_act(int dtype, int64_t M, int64_t K, const void *x, const 
  * different streams is not allowed. */
 size_t tq_gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
-/* y[M][N] (fp32, device) from the packed blob W (device, tq_packed_bytes
+/* The decode matrix-vector product: every token streams the whole packed
+ * matrix once, decodes it in registers and runs the integer dot per group
+ * ("Ternary Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section
+ * "Decode 为什么只能算一般"); 2..16 tokens share one read of the weights
+ * (same page, section "后面还有没有优化空间", third item).
+ * y[M][N] (fp32, device) from the packed blob W (device, tq_packed_bytes
  * bytes), q[M][K] int8 and a_scale[M] fp32 as produced by tq_quant_act.
- * 1 <= M <= 16. */
+ * 1 <= M <= 16.  ws: a workspace of tq_gemv_workspace_bytes (may be NULL
+ * when that is 0). */
 int tq_gemv(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
             const float *a_scale, float *y, void *ws, size_t ws_bytes, void *stream);
 
-/* h[M][N] = silu(y_gate) * y_up, silu(z) = z / (1 + exp(-z)), where y_gate
+/* The fused FFN front: gate, up and SwiGLU in one kernel that shares its
+ * quantised input between the two matrices, while each matrix keeps its
+ * own weight stream ("Ternary Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…",
+ * section "Decode 为什么只能算一般").
+ * h[M][N] = silu(y_gate) * y_up, silu(z) = z / (1 + exp(-z)), where y_gate
  * and y_up are tq_gemv of Wg and Wu (same shape and format) on the same
  * shared q.  The two weight streams are read in one pass. */
 int tq_gemv_gate_up_swiglu(int fmt, int64_t M, int64_t N, int64_t K, const void *Wg,
@@ -242,26 +264,53 @@ size_t tq_decode_stack_workspace_bytes(int fmt, int64_t layers, int64_t hidden, 
  * every product is tq_gemv's.  x_in and a_in are the layer inputs that the
  * attention and normalisation steps (not part of this library) would
  * produce.  Outputs are fp32, [layers][N]; y_o, h and the workspace must be
- * 16-byte aligned, hidden and inter multiples of 128.  The call enqueues
- * 4*layers kernel launches on `stream` (graph-capturable), one per
- * projection, in the order QKV, O, gate/up, down of layer 0, then layer 1,
- * ...: each starts after the previous one ends, as the projections of a
- * decoder must.
+ * 16-byte aligned, hidden and inter multiples of 128.  The projections run
+ * one after another, QKV, O, gate/up, down of layer 0, then layer 1, ...:
+ * each starts on its input only once the one before it is complete, as the
+ * projections of a decoder must.
  * ffn_signs (optional, device int8 [layers][hidden]): the FFN input is
  * rotated online before gate/up, as tq_gemv_quant's y_signs: y_o[l] holds
- * the rotated O output, which gate/up quantise and share. */
+ * the rotated O output, which gate/up quantise and share.
+ *
+ * tq_decode_stack enqueues 4 * layers kernel launches on `stream`
+ * (graph-capturable), one per projection, each starting after the one
+ * before it ends.  tq_decode_stack_persistent computes the same outputs,
+ * bit for bit, in one persistent launch per 32 layers: one workgroup per CU
+ * (all resident together; it assumes the GPU is not shared with other work
+ * while it runs) runs every projection in turn, each workgroup issuing the
+ * weight loads of its share before it waits, at a grid barrier built from
+ * device-memory flags, for the previous projection to be complete.  Each
+ * wait is bounded by a time limit: a wait that gives up adds 1 to the
+ * workspace's first 32-bit word and lets the launch finish (outputs are then
+ * undefined, and the workspace must be zero-filled again before the next
+ * call); the word is never cleared by the library, so it reads 0 after
+ * correct calls.  The 64-bit word at byte offset 8 of the workspace sets the
+ * time limit in ticks of the GPU's 100 MHz real-time counter (0: 100 ms).
+ * On MI355X it measures slower than the separate launches (the barrier,
+ * the device-scope loads of each projection's input and the device-scope
+ * stores cost about as much as the launch gaps they replace), so it is not
+ * the default.  Both leave the workspace as they found it apart from those
+ * two header words and the block maxima at its end. */
 int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t inter, int64_t qkv_out,
                     int64_t o_in, const tq_layer *weights /* host array [layers] */,
                     const void *x_in, const void *a_in, float *y_qkv, float *y_o, float *h,
                     float *y_out, const int8_t *ffn_signs, void *ws, size_t ws_bytes,
                     void *stream);
+int tq_decode_stack_persistent(int fmt, int64_t layers, int64_t hidden, int64_t inter,
+                               int64_t qkv_out, int64_t o_in, const tq_layer *weights,
+                               const void *x_in, const void *a_in, float *y_qkv, float *y_o,
+                               float *h, float *y_out, const int8_t *ffn_signs, void *ws,
+                               size_t ws_bytes, void *stream);
 
 /* ---- device: prefill GEMM --------------------------------------------- */
 
 /* Workspace bytes tq_gemm needs (same zero-fill rule as above). */
 size_t tq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
-/* y[M][N] as tq_gemv, for any M >= 1.  M <= 16 runs the decode GEMV; larger
+/* Prefill: many tokens at once form a large matrix product that the GPU's
+ * matrix units run well, unlike batch-1 decode ("Ternary Bonsai 2 27B：8GB
+ * 显卡硬塞 27B 三元模型…", section "Decode 为什么只能算一般").
+ * y[M][N] as tq_gemv, for any M >= 1.  M <= 16 runs the decode GEMV; larger
  * M unpacks trits to int8 in LDS and runs int8 MFMA with int32
  * accumulation per group, then scales per group in fp32, on output tiles of
  * 64, 128 or 256 tokens x 64 rows (chosen per shape).  When the output has few

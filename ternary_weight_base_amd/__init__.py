@@ -36,7 +36,7 @@ EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant
            "tq_gemv_quant_workspace_bytes", "tq_gemv_quant",
            "tq_decode_stack_workspace_bytes", "tq_decode_stack", "tq_hadamard_quant_act",
            "tq_ternarize", "tq_debug_stream_read", "tq_debug_gate_up_sums",
-           "tq_debug_gemv_quant_sums")
+           "tq_debug_gemv_quant_sums", "tq_decode_stack_persistent")
 
 
 class TqLayer(ctypes.Structure):
@@ -73,6 +73,7 @@ def _load():
         "tq_gemv_quant": ([I, I64, I64, P, P, I, P, P, I64, P, P, P, P, SZ, P], I),
         "tq_decode_stack_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "tq_decode_stack": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
+        "tq_decode_stack_persistent": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
         "tq_hadamard_quant_act": ([I, I64, I64, P, P, P, P, P], I),
         "tq_ternarize": ([I64, I64, P, P, P], I),
         "tq_debug_stream_read": ([P, SZ, P, I64, P], I),
@@ -261,16 +262,24 @@ def tq_decode_stack_workspace_bytes(fmt, layers, hidden, inter, qkv_out, o_in) -
 
 
 def tq_decode_stack(fmt, layers, hidden, inter, qkv_out, o_in, weights, x_in, a_in,
-                    y_qkv, y_o, h, y_out, ws, stream=None, ffn_signs=None) -> None:
+                    y_qkv, y_o, h, y_out, ws, stream=None, ffn_signs=None, persistent=False) -> None:
     """weights: list of (qkv, o, gate, up, down) device tensors per layer (or a
     ctypes array of TqLayer built once with stack_layers()).  ffn_signs (int8
-    [layers][hidden]) rotates the FFN input online."""
+    [layers][hidden]) rotates the FFN input online.  persistent=True calls
+    tq_decode_stack_persistent (one launch per 32 layers) instead of one
+    launch per projection."""
     arr = weights if isinstance(weights, ctypes.Array) else stack_layers(weights)
     wp, wb = _ws(ws)
-    _check(lib.tq_decode_stack(fmt, layers, hidden, inter, qkv_out, o_in,
-                               ctypes.cast(arr, ctypes.c_void_p), _ptr(x_in), _ptr(a_in),
-                               _ptr(y_qkv), _ptr(y_o), _ptr(h), _ptr(y_out), _ptr(ffn_signs),
-                               wp, wb, _stream(stream)), "tq_decode_stack")
+    fn = lib.tq_decode_stack_persistent if persistent else lib.tq_decode_stack
+    _check(fn(fmt, layers, hidden, inter, qkv_out, o_in, ctypes.cast(arr, ctypes.c_void_p),
+              _ptr(x_in), _ptr(a_in), _ptr(y_qkv), _ptr(y_o), _ptr(h), _ptr(y_out), _ptr(ffn_signs),
+              wp, wb, _stream(stream)), "tq_decode_stack_persistent" if persistent else "tq_decode_stack")
+
+
+def stack_timeouts(ws) -> int:
+    """Waits of the persistent decode stack that gave up (the workspace's first
+    32-bit word; 0 after correct calls).  Synchronises with the device."""
+    return int(ws.view(-1)[0:1].view(-1).cpu().numpy().view("uint32")[0]) if ws is not None else 0
 
 
 def stack_layers(weights):

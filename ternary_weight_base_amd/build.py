@@ -70,6 +70,9 @@ def build() -> str:
                 obj = f"tq_proj_{fname}{'' if lx else '_sg'}{'_sums' if sums else ''}.o"
                 units.append(("tq_proj_inst.hip", obj,
                               [f"-DTQ_INST_FMT={fmt}", f"-DTQ_INST_LX={lx}", f"-DTQ_INST_SUMS={sums}"]))
+    # the persistent decode-token kernel: one object per packed format
+    for fmt, fname in ((0, "b3"), (1, "2b"), (2, "bp")):
+        units.append(("tq_stack.hip", f"tq_stack_{fname}.o", [f"-DTQ_STACK_FMT={fmt}"]))
     for src, obj, defs in units:
         o = os.path.join(bdir, obj)
         cmds.append(["hipcc", *HIP_FLAGS, *defs, "-I", INC, "-I", CSRC, "-c", os.path.join(CSRC, src),

@@ -5,7 +5,7 @@
 // group's fp16 scale ("三值权重 27B 压到 5.9GB｜本地部署成本账单重算", section 三),
 // here as a dense contraction on the matrix cores, the path the pages name
 // as the one a GPU runs well when a prompt forms large matrices ("Ternary
-// Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section "后面还有没有优化空间").
+// Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section "Decode 为什么只能算一般").
 //
 // grid (NB, ceil(M / (64 TM)), C), 256 threads (4 waves), TM = 1, 2 or 4.
 // Per group the block's 64 weight rows x 128 trits are decoded to int8 in

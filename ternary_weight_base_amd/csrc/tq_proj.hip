@@ -7,6 +7,7 @@
 #include "tq.h"
 #include "tq_layout.h"
 #include "tq_proj.h"
+#include "tq_stack.h"
 
 using tq::Layout;
 using namespace tqproj;
@@ -87,16 +88,13 @@ WsLayout ws_layout(const Plan *ps, int n) {
   return w;
 }
 
-// One projection, its cut blocks meeting through the workspace at `ws`
-// laid out as `w` (zero on entry, left zero).  With `sums` the same plan
-// runs the group-sum instantiation instead (no workspace, no output).
-int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, int in_kind,
-                const void *in, const float *in_aux, int in_nb, float *out, float *out_bmax,
-                char *ws, const WsLayout &w, hipStream_t st, const int8_t *out_signs = nullptr,
-                int32_t *sums = nullptr, float *sums_scale = nullptr) {
-  const int nmat = W1 ? 2 : 1;
-  const Plan p = plan_proj(fmt, N, K, nmat);
-  ProjArgs A;
+// The kernel arguments of one projection for plan p, its cut blocks meeting
+// through the workspace at `ws` laid out as `w` (zero on entry, left zero).
+// TQ_ERR_SHAPE if the plan cannot rotate the output.
+int proj_args(const Plan &p, int64_t N, int64_t K, const void *W0, const void *W1, const void *in,
+              const float *in_aux, int in_nb, float *out, float *out_bmax, char *ws,
+              const WsLayout &w, const int8_t *out_signs, int32_t *sums, float *sums_scale,
+              ProjArgs &A) {
   A.W0 = (const uint8_t *)W0;
   A.W1 = (const uint8_t *)(W1 ? W1 : W0);
   A.in = in;
@@ -123,6 +121,21 @@ int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, i
   A.C = p.C;
   A.W = p.W;
   A.I = p.I;
+  return TQ_OK;
+}
+
+// One projection as its own launch.  With `sums` the same plan runs the
+// group-sum instantiation instead (no workspace, no output).
+int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, int in_kind,
+                const void *in, const float *in_aux, int in_nb, float *out, float *out_bmax,
+                char *ws, const WsLayout &w, hipStream_t st, const int8_t *out_signs = nullptr,
+                int32_t *sums = nullptr, float *sums_scale = nullptr) {
+  const int nmat = W1 ? 2 : 1;
+  const Plan p = plan_proj(fmt, N, K, nmat);
+  ProjArgs A;
+  int rc = proj_args(p, N, K, W0, W1, in, in_aux, in_nb, out, out_bmax, ws, w, out_signs, sums,
+                     sums_scale, A);
+  if (rc != TQ_OK) return rc;
   const bool lx = p.grid <= kLxMaxGrid;
 #define TQ_LAUNCH(F_)                                                                         \
   if (sums)                                                                                   \
@@ -152,10 +165,11 @@ bool shape_ok(int64_t N, int64_t K) {
          K <= ((int64_t)1 << 20);
 }
 
-// Decode-stack workspace: the meet sections shared by the four launches of
-// every layer (each launch leaves them zero), then the block maxima of y_o
-// and of h.
+// Decode-stack workspace: the persistent kernel's synchronisation words,
+// then the meet sections shared by the projections of every layer (each
+// projection leaves them zero), then the block maxima of y_o and of h.
 struct StackWs {
+  size_t meet_base;  // offset of the meet sections (laid out as `meet` from there)
   WsLayout meet;
   size_t bmax_o, bmax_h, total;
 };
@@ -164,11 +178,22 @@ StackWs stack_ws(int fmt, int64_t hidden, int64_t inter, int64_t qkv_out, int64_
   const Plan ps[4] = {plan_proj(fmt, qkv_out, hidden, 1), plan_proj(fmt, hidden, o_in, 1),
                       plan_proj(fmt, inter, hidden, 2), plan_proj(fmt, hidden, inter, 1)};
   StackWs w;
+  w.meet_base = round256(tqstack::kSyncBytes);
   w.meet = ws_layout(ps, 4);
-  w.bmax_o = w.meet.total;
+  w.bmax_o = w.meet_base + w.meet.total;
   w.bmax_h = w.bmax_o + round256((size_t)Layout(fmt, hidden, o_in).NB * 4);
   w.total = w.bmax_h + round256((size_t)Layout(fmt, inter, hidden).NB * 4);
   return w;
+}
+
+// Persistent workgroups: one per CU of the current device (at most
+// tqstack::kMaxWg), 0 if the kernel cannot keep one resident per CU.
+int stack_grid(int fmt) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  (void)fmt;
+  return cus < tqstack::kMaxWg ? cus : tqstack::kMaxWg;
 }
 
 }  // namespace
@@ -258,11 +283,12 @@ extern "C" size_t tq_decode_stack_workspace_bytes(int fmt, int64_t layers, int64
   return stack_ws(fmt, hidden, inter, qkv_out, o_in).total;
 }
 
-extern "C" int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t inter,
-                               int64_t qkv_out, int64_t o_in, const tq_layer *weights,
-                               const void *x_in, const void *a_in, float *y_qkv, float *y_o,
-                               float *h, float *y_out, const int8_t *ffn_signs, void *ws,
-                               size_t ws_bytes, void *stream) {
+namespace {
+
+// Checks shared by both forms of the decode stack.
+int stack_check(int fmt, int64_t layers, int64_t hidden, int64_t inter, int64_t qkv_out, int64_t o_in,
+                const tq_layer *weights, const void *x_in, const void *a_in, float *y_qkv, float *y_o,
+                float *h, float *y_out, void *ws, size_t ws_bytes) {
   if (!weights || !x_in || !a_in || !y_qkv || !y_o || !h || !y_out || !ws) return TQ_ERR_NULL;
   if (!fmt_ok(fmt)) return TQ_ERR_FORMAT;
   const size_t need = tq_decode_stack_workspace_bytes(fmt, layers, hidden, inter, qkv_out, o_in);
@@ -278,30 +304,113 @@ extern "C" int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t 
   if (!aligned16(x_in) || !aligned16(a_in) || !aligned16(ws) || !aligned16(y_o) ||
       !aligned16(h) || !aligned4(y_qkv) || !aligned4(y_out))
     return TQ_ERR_ALIGN;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" int tq_decode_stack(int fmt, int64_t layers, int64_t hidden, int64_t inter,
+                                        int64_t qkv_out, int64_t o_in, const tq_layer *weights,
+                                        const void *x_in, const void *a_in, float *y_qkv, float *y_o,
+                                        float *h, float *y_out, const int8_t *ffn_signs, void *ws,
+                                        size_t ws_bytes, void *stream) {
+  int rc = stack_check(fmt, layers, hidden, inter, qkv_out, o_in, weights, x_in, a_in, y_qkv, y_o, h,
+                       y_out, ws, ws_bytes);
+  if (rc != TQ_OK) return rc;
   const StackWs w = stack_ws(fmt, hidden, inter, qkv_out, o_in);
   char *base = (char *)ws;
+  char *meet = base + w.meet_base;
   float *bmax_o = reinterpret_cast<float *>(base + w.bmax_o);
   float *bmax_h = reinterpret_cast<float *>(base + w.bmax_h);
   const int nb_o = (int)Layout(fmt, hidden, o_in).NB, nb_h = (int)Layout(fmt, inter, hidden).NB;
   const uint16_t *x16 = (const uint16_t *)x_in, *a16 = (const uint16_t *)a_in;
   hipStream_t st = (hipStream_t)stream;
-  int rc;
   for (int64_t l = 0; l < layers; l++) {
     const tq_layer &Lw = weights[l];
     float *yo = y_o + l * hidden, *hl = h + l * inter;
     if ((rc = launch_proj(fmt, qkv_out, hidden, Lw.qkv, nullptr, kInF16, x16 + l * hidden, nullptr,
-                          0, y_qkv + l * qkv_out, nullptr, base, w.meet, st)) != TQ_OK)
+                          0, y_qkv + l * qkv_out, nullptr, meet, w.meet, st)) != TQ_OK)
       return rc;
     if ((rc = launch_proj(fmt, hidden, o_in, Lw.o, nullptr, kInF16, a16 + l * o_in, nullptr, 0, yo,
-                          bmax_o, base, w.meet, st, ffn_signs ? ffn_signs + l * hidden : nullptr)) !=
+                          bmax_o, meet, w.meet, st, ffn_signs ? ffn_signs + l * hidden : nullptr)) !=
         TQ_OK)
       return rc;
     if ((rc = launch_proj(fmt, inter, hidden, Lw.gate, Lw.up, kInF32, yo, bmax_o, nb_o, hl, bmax_h,
-                          base, w.meet, st)) != TQ_OK)
+                          meet, w.meet, st)) != TQ_OK)
       return rc;
     if ((rc = launch_proj(fmt, hidden, inter, Lw.down, nullptr, kInF32, hl, bmax_h, nb_h,
-                          y_out + l * hidden, nullptr, base, w.meet, st)) != TQ_OK)
+                          y_out + l * hidden, nullptr, meet, w.meet, st)) != TQ_OK)
       return rc;
+  }
+  return TQ_OK;
+}
+
+extern "C" int tq_decode_stack_persistent(int fmt, int64_t layers, int64_t hidden, int64_t inter,
+                               int64_t qkv_out, int64_t o_in, const tq_layer *weights,
+                               const void *x_in, const void *a_in, float *y_qkv, float *y_o,
+                               float *h, float *y_out, const int8_t *ffn_signs, void *ws,
+                               size_t ws_bytes, void *stream) {
+  int rc = stack_check(fmt, layers, hidden, inter, qkv_out, o_in, weights, x_in, a_in, y_qkv, y_o, h,
+                       y_out, ws, ws_bytes);
+  if (rc != TQ_OK) return rc;
+  if (ffn_signs && hidden % 64 != 0) return TQ_ERR_SHAPE;
+  const int nwg = stack_grid(fmt);
+  if (nwg < 1) return TQ_ERR_HIP;
+  const StackWs w = stack_ws(fmt, hidden, inter, qkv_out, o_in);
+  char *base = (char *)ws;
+  char *meet = base + w.meet_base;
+  tqstack::StackArgs S;
+  const int64_t NK[4][2] = {{qkv_out, hidden}, {hidden, o_in}, {inter, hidden}, {hidden, inter}};
+  for (int j = 0; j < 4; j++) {
+    const int nmat = j == 2 ? 2 : 1;
+    const Plan p = plan_proj(fmt, NK[j][0], NK[j][1], nmat);
+    // per-layer pointers are set by the kernel; W1 marks the two-matrix kind
+    const int in_nb = j >= 2 ? (int)(NK[j][1] / 64) : 0;
+    const int8_t *signs = j == 1 && ffn_signs ? ffn_signs : nullptr;
+    rc = proj_args(p, NK[j][0], NK[j][1], nullptr, nullptr, nullptr, nullptr, in_nb, nullptr, nullptr,
+                   meet, w.meet, signs, nullptr, nullptr, S.kind[j].P);
+    if (rc != TQ_OK) return rc;
+    S.kind[j].gs = p.gs;
+    S.kind[j].grid = p.grid;
+    // the persistent kernel gives each workgroup at most one share of a
+    // projection; plans with more shares than CUs run as separate launches
+    if (p.grid > nwg)
+      return tq_decode_stack(fmt, layers, hidden, inter, qkv_out, o_in, weights, x_in, a_in,
+                                      y_qkv, y_o, h, y_out, ffn_signs, ws, ws_bytes, stream);
+  }
+  S.x_in = (const uint16_t *)x_in;
+  S.a_in = (const uint16_t *)a_in;
+  S.ffn_signs = ffn_signs;
+  S.bmax_o = reinterpret_cast<float *>(base + w.bmax_o);
+  S.bmax_h = reinterpret_cast<float *>(base + w.bmax_h);
+  S.sync = reinterpret_cast<uint32_t *>(base);
+  S.hidden = (int)hidden;
+  S.inter = (int)inter;
+  S.qkv_out = (int)qkv_out;
+  S.o_in = (int)o_in;
+  hipStream_t st = (hipStream_t)stream;
+  for (int64_t l0 = 0; l0 < layers; l0 += tqstack::kStackMaxLayers) {
+    const int nl = (int)(layers - l0 < tqstack::kStackMaxLayers ? layers - l0 : tqstack::kStackMaxLayers);
+    for (int i = 0; i < nl; i++) {
+      const tq_layer &Lw = weights[l0 + i];
+      S.w[i][0] = Lw.qkv;
+      S.w[i][1] = Lw.o;
+      S.w[i][2] = Lw.gate;
+      S.w[i][3] = Lw.up;
+      S.w[i][4] = Lw.down;
+    }
+    S.layers = nl;
+    S.x_in = (const uint16_t *)x_in + l0 * hidden;
+    S.a_in = (const uint16_t *)a_in + l0 * o_in;
+    S.y_qkv = y_qkv + l0 * qkv_out;
+    S.y_o = y_o + l0 * hidden;
+    S.h = h + l0 * inter;
+    S.y_out = y_out + l0 * hidden;
+    S.ffn_signs = ffn_signs ? ffn_signs + l0 * hidden : nullptr;
+    if (fmt == TQ_FMT_B3) rc = tqstack::launch_stack<0>(S, nwg, st);
+    else if (fmt == TQ_FMT_2B) rc = tqstack::launch_stack<1>(S, nwg, st);
+    else rc = tqstack::launch_stack<2>(S, nwg, st);
+    if (rc != TQ_OK) return rc;
   }
   return TQ_OK;
 }

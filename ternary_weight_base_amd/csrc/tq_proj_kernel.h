@@ -108,113 +108,119 @@ __device__ __forceinline__ void *meet_slot0(const ProjArgs &A, int b, int lane) 
   return reinterpret_cast<S *>(A.slots) + (size_t)b * A.slot_stride * 64 + lane;
 }
 
-// LX: the quantised activations go through LDS into VGPRs instead of
-// v_readlane into SGPRs: fewer VALU operations per group but up to about
-// 140 VGPRs, so it is launched only for grids of at most one workgroup per
-// CU (two waves per SIMD, 256 VGPRs); bigger grids keep the SGPR form
-// within 128 VGPRs (two workgroups per CU).
-template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX, bool SUMS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LX ? 2 : 4)))
-void proj_kernel(ProjArgs A) {
-  constexpr int WPG = FMT == 0 ? 7 : 9;   // words per (row, group) in registers
-  constexpr int NP = (GS + 1) / 2;        // group pairs: one activation word per lane each
-  constexpr int D0 = D < GS ? D : GS;
-  constexpr int NPART = SPLIT ? kMaxParts : 1;  // blocks a range can touch
-  __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
-  __shared__ float red[NPART * NMAT * kNW * 64];
-  __shared__ float wmax[kNW];
-  __shared__ __attribute__((aligned(16))) uint32_t qs[LX ? kNW : 1][LX ? GS : 1][32];
-  // The digit table depends on nothing: its LDS stores overlap the kernel
-  // argument loads and the address arithmetic below.
-  if constexpr (FMT == 0) fill_b3_lut<kThreads>(lut);
+// LDS the projection body works in, allocated by the kernel that calls it
+// (a persistent kernel runs several bodies on one allocation).
+//   lut:  B3 digit table (kLutEntries * kLutCopies entries), filled by the kernel
+//   red:  [kMaxParts][2][kNW][64] partial sums of the waves
+//   wmax: [kNW] per-wave maxima of an fp16 input
+//   qs:   [kNW][gs_cap][32] quantised activation words (LX form)
+struct ProjLds {
+  uint2 *lut;
+  float *red;
+  float *wmax;
+  uint32_t *qs;
+};
 
-  const Layout L(FMT, A.N, A.K);
-  const int G = (int)L.G, N = A.N, K = A.K;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wg = blockIdx.x;
+// Device-scope loads and stores, for data that another workgroup of the same
+// persistent launch writes or reads (the caches of one XCD do not see the
+// writes of another before the launch ends).
+__device__ __forceinline__ float ld_dev_f32(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev_u64(const void *p) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_f32(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One projection's share of work for workgroup `wg` of the plan in A
+// (steps 1-5 above), as phases that the caller runs in order:
+//   setup; issue_first; load_inputs; compute; finish
+// (a standalone launch puts a workgroup barrier between load_inputs and
+// issue_first, so that activations are issued before weights).  GS is the
+// compile-time slot count.  Standalone (PERSIST false): gs_rt == GS, the
+// D-deep pipeline, plain loads and stores.  PERSIST (the persistent decode
+// kernel): GS is an upper bound and gs_rt the plan's slot count; the
+// caller issues the first D slots early (before the input is ready); the
+// input, produced by another workgroup of the same launch, is read with
+// device-scope loads; outputs are stored with device-scope stores (not
+// waited for: the finishing waves, wave < NPART, wait for them), and block
+// maxima go through an atomic maximum on a zeroed array.
+template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX, bool SUMS, bool PERSIST>
+struct ProjRun {
+  static constexpr int WPG = FMT == 0 ? 7 : 9;   // words per (row, group) in registers
+  static constexpr int NP = (GS + 1) / 2;        // group pairs: one activation word per lane each
+  static constexpr int D0 = D < GS ? D : GS;
+  static constexpr int NPART = SPLIT ? kMaxParts : 1;  // blocks a range can touch
+
+  ProjArgs A;
+  int wg, gsv, G, N, K;
   // Slot j of this wave -> (block sb[j], group sg[j]); slots past the
   // wave's ns live items reload its last live item (a cache hit: no second
   // trip to HBM), an idle wave's slots the range's last item.
   int bw0, ilast_b, ns, gb, jmax, sb[GS], sg[GS];
-  if constexpr (SPLIT) {
-    const int i0 = wg_first(wg, A, G), i1 = wg_first(wg + 1, A, G);
-    const int ilast = i1 - 1;
-    const int T = i1 - i0;                       // items of the range, <= kNW * GS
-    const int s0 = i0 + (int)((uint32_t)(wave * T) / kNW);  // the waves split the range evenly
-    ns = i0 + (int)((uint32_t)((wave + 1) * T) / kNW) - s0;
-    bw0 = (int)((uint32_t)i0 / (uint32_t)G);     // first block of the range
-    ilast_b = (int)((uint32_t)ilast / (uint32_t)G);
-    // GS <= G, so a wave's slots cross at most one block boundary
-    const int base = min(s0, ilast);
-    const int bb = (int)((uint32_t)base / (uint32_t)G);
-    gb = base - bb * G;
-    jmax = ns > 0 ? ns - 1 : ilast - base;
-#pragma unroll
-    for (int j = 0; j < GS; j++) {
-      const int g = gb + min(j, jmax);
-      sb[j] = g >= G ? bb + 1 : bb;
-      sg[j] = g >= G ? g - G : g;
-    }
-  } else {
-    const int b = wg / A.C, c = wg - b * A.C;
-    const int gbeg = (int)((uint32_t)(c * G) / (uint32_t)A.C);
-    const int gend = (int)((uint32_t)((c + 1) * G) / (uint32_t)A.C);
-    gb = gbeg + wave * GS;                       // first group of this wave
-    ns = max(0, min(gend - gb, GS));
-    jmax = ns > 0 ? ns - 1 : gend - 1 - gb;      // negative for an idle wave
-    bw0 = ilast_b = b;
-#pragma unroll
-    for (int j = 0; j < GS; j++) {
-      sb[j] = b;
-      sg[j] = gb + min(j, jmax);
-    }
-  }
-  const uint8_t *Wm[2] = {A.W0, A.W1};
-
-  // ---- 1a. activation slice: lane l holds word l % 32 of group 2p + l / 32
-  // (int8 input: the words themselves; fp16 / fp32: four values to quantise)
-  const int hsel = lane >> 5, word = lane & 31;
+  uint32_t wd[NMAT][GS][WPG];
   float4 xf[IN == kInF32 ? NP : 1];
   uint2 xh[IN == kInF16 ? NP : 1];
   uint32_t qv[NP];
-#pragma unroll
-  for (int p = 0; p < NP; p++) {
-    // this lane's slot, as arithmetic (an indexed sg[] would be moved to LDS)
-    const int jl = min(2 * p + hsel, GS - 1);
-    const int gl = gb + min(jl, jmax);
-    const int gp = SPLIT && gl >= G ? gl - G : gl;
-    const size_t off = (size_t)gp * tq::kGroup + 4 * (size_t)word;
-    if constexpr (IN == kInF32) xf[p] = *reinterpret_cast<const float4 *>((const float *)A.in + off);
-    else if constexpr (IN == kInF16) xh[p] = *reinterpret_cast<const uint2 *>((const uint16_t *)A.in + off);
-    else qv[p] = *reinterpret_cast<const uint32_t *>((const int8_t *)A.in + off);
-  }
-  // ---- 1b. what the absmax needs
   float bm[IN == kInF32 ? kBmaxPerLane : 1];
   uint4 xm[IN == kInF16 ? kXmaxLoads : 1];
-  if constexpr (IN == kInF32) {
+  float acc[NPART][NMAT];  // [block of the range][matrix]
+  float a_scale;
+
+  __device__ __forceinline__ void setup(const ProjArgs &args, int wg_, int gs_rt) {
+    A = args;
+    wg = wg_;
+    gsv = PERSIST ? gs_rt : GS;
+    const Layout L(FMT, A.N, A.K);
+    G = (int)L.G;
+    N = A.N;
+    K = A.K;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if constexpr (SPLIT) {
+      const int i0 = wg_first(wg, A, G), i1 = wg_first(wg + 1, A, G);
+      const int ilast = i1 - 1;
+      const int T = i1 - i0;                       // items of the range, <= kNW * gsv
+      const int s0 = i0 + (int)((uint32_t)(wave * T) / kNW);  // the waves split the range evenly
+      ns = i0 + (int)((uint32_t)((wave + 1) * T) / kNW) - s0;
+      bw0 = (int)((uint32_t)i0 / (uint32_t)G);     // first block of the range
+      ilast_b = (int)((uint32_t)ilast / (uint32_t)G);
+      // gsv <= G, so a wave's slots cross at most one block boundary
+      const int base = min(s0, ilast);
+      const int bb = (int)((uint32_t)base / (uint32_t)G);
+      gb = base - bb * G;
+      jmax = ns > 0 ? ns - 1 : ilast - base;
 #pragma unroll
-    for (int i = 0; i < kBmaxPerLane; i++) bm[i] = A.in_aux[min(lane + 64 * i, A.in_nb - 1)];
-  }
-  if constexpr (IN == kInF16) {
+      for (int j = 0; j < GS; j++) {
+        const int g = gb + min(j, jmax);
+        sb[j] = g >= G ? bb + 1 : bb;
+        sg[j] = g >= G ? g - G : g;
+      }
+    } else {
+      const int b = wg / A.C, c = wg - b * A.C;
+      const int gbeg = (int)((uint32_t)(c * G) / (uint32_t)A.C);
+      const int gend = (int)((uint32_t)((c + 1) * G) / (uint32_t)A.C);
+      gb = gbeg + wave * gsv;                      // first group of this wave
+      ns = max(0, min(gend - gb, gsv));
+      jmax = ns > 0 ? ns - 1 : gend - 1 - gb;      // negative for an idle wave
+      bw0 = ilast_b = b;
 #pragma unroll
-    for (int i = 0; i < kXmaxLoads; i++)
-      xm[i] = reinterpret_cast<const uint4 *>(A.in)[min(tid + kThreads * i, K / 8 - 1)];
+      for (int j = 0; j < GS; j++) {
+        sb[j] = b;
+        sg[j] = gb + min(j, jmax);
+      }
+    }
   }
 
-  // The CU returns vector loads in issue order, so activation loads issued
-  // behind other waves' weight loads would wait for those weights: every
-  // wave issues its activation loads before any wave of the workgroup
-  // issues weights.
-  __syncthreads();
-
-  // ---- 1c. weight loads of the first D groups (dead slots: a live group)
-  uint32_t wd[NMAT][GS][WPG];
-  auto issue = [&](int i) {
+  __device__ __forceinline__ void issue(int i) {
+    const Layout L(FMT, A.N, A.K);
+    const int lane = threadIdx.x & 63;
     int bi = sb[i], gi = sg[i];
     asm volatile("" : "+v"(gi));  // keeps the loads at this point of the program
     if constexpr (SPLIT) asm volatile("" : "+v"(bi));
     const int Wb = (int)L.block_rows(bi), lr = min(lane, Wb - 1);
+    const uint8_t *Wm[2] = {A.W0, A.W1};
 #pragma unroll
     for (int mat = 0; mat < NMAT; mat++) {
       const uint8_t *gp = Wm[mat] + L.group_base(bi, gi);
@@ -237,253 +243,363 @@ void proj_kernel(ProjArgs A) {
         wd[mat][i][8] = ld_stream2(gp + Wb * 32 + lr * 2);
       }
     }
-  };
-#pragma unroll
-  for (int i = 0; i < D0; i++) issue(i);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- 2. fp16 input: per-wave maxima of the whole x ------------------------
-  if constexpr (IN == kInF16) {
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kXmaxLoads; i++) m = habs_max8(xm[i], m);
-    for (int j = tid + kThreads * kXmaxLoads; j < K / 8; j += kThreads)
-      m = habs_max8(reinterpret_cast<const uint4 *>(A.in)[j], m);
-    m = wave_max(m);
-    if (lane == 0) wmax[wave] = m;
-    __syncthreads();
   }
 
-  // ---- 3. absmax, quantise the slice ----------------------------------------
-  float a_scale;
-  if constexpr (IN == kInInt8) {
-    a_scale = SUMS ? 0.0f : A.in_aux[0];
-  } else {
-    float amax = 0.0f;
+  // The weight loads of the first D slots (PERSIST: of at most the plan's
+  // slot count).
+  __device__ __forceinline__ void issue_first() {
+#pragma unroll
+    for (int i = 0; i < D0; i++)
+      if (!PERSIST || i < gsv) issue(i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- 1a/1b. the activation slice (lane l holds word l % 32 of group
+  // 2p + l / 32; int8 input: the words themselves; fp16 / fp32: four values
+  // to quantise) and what the absmax needs
+  __device__ __forceinline__ void load_inputs() {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int hsel = lane >> 5, word = lane & 31;
+#pragma unroll
+    for (int p = 0; p < NP; p++) {
+      if (PERSIST && 2 * p >= gsv) break;
+      // this lane's slot, as arithmetic (an indexed sg[] would be moved to LDS)
+      const int jl = min(2 * p + hsel, gsv - 1);
+      const int gl = gb + min(jl, jmax);
+      const int gp = SPLIT && gl >= G ? gl - G : gl;
+      const size_t off = (size_t)gp * tq::kGroup + 4 * (size_t)word;
+      if constexpr (IN == kInF32) {
+        const float *src = (const float *)A.in + off;
+        if constexpr (PERSIST) {
+          const uint64_t lo = ld_dev_u64(src), hi = ld_dev_u64(src + 2);
+          xf[p] = make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                              __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+        } else {
+          xf[p] = *reinterpret_cast<const float4 *>(src);
+        }
+      } else if constexpr (IN == kInF16) {
+        xh[p] = *reinterpret_cast<const uint2 *>((const uint16_t *)A.in + off);
+      } else {
+        qv[p] = *reinterpret_cast<const uint32_t *>((const int8_t *)A.in + off);
+      }
+    }
+    if constexpr (IN == kInF32) {
+#pragma unroll
+      for (int i = 0; i < kBmaxPerLane; i++) {
+        const float *src = A.in_aux + min(lane + 64 * i, A.in_nb - 1);
+        bm[i] = PERSIST ? ld_dev_f32(src) : *src;
+      }
+    }
     if constexpr (IN == kInF16) {
 #pragma unroll
-      for (int w = 0; w < kNW; w++) amax = fmaxf(amax, wmax[w]);
-    } else {
+      for (int i = 0; i < kXmaxLoads; i++)
+        xm[i] = reinterpret_cast<const uint4 *>(A.in)[min(tid + kThreads * i, K / 8 - 1)];
+    }
+  }
+
+  // ---- 2-4. absmax, quantisation, the pipelined decode + dot + scale
+  __device__ __forceinline__ void compute(const ProjLds &sm) {
+    const Layout L(FMT, A.N, A.K);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hsel = lane >> 5, word = lane & 31;
+    const uint2 *lut = sm.lut;
+    uint32_t *qs = sm.qs + (size_t)wave * GS * 32;  // this wave's [GS][32] words
+
+    // ---- 2. fp16 input: per-wave maxima of the whole x ----------------------
+    if constexpr (IN == kInF16) {
       float m = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kBmaxPerLane; i++) m = fmaxf(m, bm[i]);
-      for (int j = lane + 64 * kBmaxPerLane; j < A.in_nb; j += 64) m = fmaxf(m, A.in_aux[j]);
-      amax = wave_max(m);
+      for (int i = 0; i < kXmaxLoads; i++) m = habs_max8(xm[i], m);
+      for (int j = tid + kThreads * kXmaxLoads; j < K / 8; j += kThreads)
+        m = habs_max8(reinterpret_cast<const uint4 *>(A.in)[j], m);
+      m = wave_max(m);
+      if (lane == 0) sm.wmax[wave] = m;
+      __syncthreads();
     }
-    const bool zero = amax == 0.0f;
-    const float inv = zero ? 0.0f : 127.0f / amax;  // IEEE division, as the quantiser
-    a_scale = zero ? 0.0f : amax / 127.0f;
-#pragma unroll
-    for (int p = 0; p < NP; p++) {
-      if constexpr (IN == kInF32) {
-        qv[p] = quant4(xf[p].x, xf[p].y, xf[p].z, xf[p].w, inv, zero);
-      } else {
-        qv[p] = quant4(half_bits(xh[p].x & 0xffffu), half_bits(xh[p].x >> 16),
-                       half_bits(xh[p].y & 0xffffu), half_bits(xh[p].y >> 16), inv, zero);
-      }
-    }
-  }
-  if constexpr (LX) {  // the wave's own slice: no barrier needed
-#pragma unroll
-    for (int p = 0; p < NP; p++) {
-      const int jl = 2 * p + hsel;
-      if (jl < GS) qs[wave][jl][word] = qv[p];
-    }
-  }
-  // 2B: activation sum of every group of the slice (a 32-lane reduction)
-  int xsum[GS];
-  if constexpr (FMT == 1) {
-#pragma unroll
-    for (int p = 0; p < NP; p++) {
-      int s = sdot4(qv[p], 0x01010101u, 0);
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off, 32);
-      xsum[2 * p] = __builtin_amdgcn_readlane(s, 0);
-      if (2 * p + 1 < GS) xsum[2 * p + 1] = __builtin_amdgcn_readlane(s, 32);
-    }
-  }
 
-  // ---- 4. pipelined decode + integer dot + scale ---------------------------
-  const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
-  float acc[NPART][NMAT];  // [block of the range][matrix]
-#pragma unroll
-  for (int p = 0; p < NPART; p++)
-#pragma unroll
-    for (int mat = 0; mat < NMAT; mat++) acc[p][mat] = 0.0f;
-  // Empty asm statements (kept in program order) pin the schedule through
-  // data dependences: a group's activation words enter its iteration
-  // through one; each matrix's weight words enter through one (so the wait
-  // for its loads lands there) and its accumulator leaves through another,
-  // so one matrix's lookups and dots are in flight at a time; the loads of
-  // issue() take their group index from one.  Without them the compiler
-  // interleaves iterations and holds several groups' lookups at once.
-#pragma unroll
-  for (int i = 0; i < GS; i++) {
-    if (i + D0 < GS) issue(i + D0);
-    asm volatile("" : "+v"(qv[i >> 1]));
-    XRegs<1> xa;  // SGPRs (v_readlane) or, with LX, VGPRs (LDS)
-    if constexpr (LX) {
-      const uint4 *xq = reinterpret_cast<const uint4 *>(&qs[wave][i][0]);
-#pragma unroll
-      for (int k = 0; k < 8; k++) {
-        const uint4 t = xq[k];
-        xa.v[0][4 * k] = t.x;
-        xa.v[0][4 * k + 1] = t.y;
-        xa.v[0][4 * k + 2] = t.z;
-        xa.v[0][4 * k + 3] = t.w;
-      }
+    // ---- 3. absmax, quantise the slice --------------------------------------
+    if constexpr (IN == kInInt8) {
+      a_scale = SUMS ? 0.0f : A.in_aux[0];
     } else {
+      float amax = 0.0f;
+      if constexpr (IN == kInF16) {
 #pragma unroll
-      for (int k = 0; k < 32; k++) xa.v[0][k] = __builtin_amdgcn_readlane(qv[i >> 1], 32 * (i & 1) + k);
-    }
-    const bool live = i < ns;
-    const int part = SPLIT ? sb[i] - bw0 : 0;
-#pragma unroll
-    for (int mat = 0; mat < NMAT; mat++) {
-#pragma unroll
-      for (int k = 0; k < WPG; k++) asm volatile("" : "+v"(wd[mat][i][k]));  // this matrix starts here
-      int S[1] = {0};
-      float sc;
-      if constexpr (FMT == 0) {
-        const uint32_t w[7] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2], wd[mat][i][3],
-                               wd[mat][i][4], wd[mat][i][5], wd[mat][i][6]};
-        if constexpr (LX) S[0] = b3_group_v(lut, laneoff, w, xa.v[0]);
-        else b3_group<1>(lut, laneoff, w, xa, S);
-        sc = half_bits(wd[mat][i][6] >> 16);
+        for (int w = 0; w < kNW; w++) amax = fmaxf(amax, sm.wmax[w]);
       } else {
-        const uint32_t w[9] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2],
-                               wd[mat][i][3], wd[mat][i][4], wd[mat][i][5],
-                               wd[mat][i][6], wd[mat][i][7], wd[mat][i][8]};
-        if constexpr (FMT == 1) {
-          const int xs[1] = {xsum[i]};
-          tb_group<1>(w, xa, xs, S);
-        } else {
-          S[0] = bp_group(w, xa);
-        }
-        sc = half_bits(wd[mat][i][8]);
-      }
-      if constexpr (SUMS) {
-        if (live && lane < (int)L.valid_rows(sb[i]))
-          A.sums[((size_t)mat * N + (size_t)sb[i] * tq::kBlockRows + lane) * G + sg[i]] = S[0];
-        continue;
-      }
-      const float s = live ? sc : 0.0f;
+        float m = 0.0f;
 #pragma unroll
-      for (int p = 0; p < NPART; p++) {
-        acc[p][mat] = fmaf(p == part ? s : 0.0f, (float)S[0], acc[p][mat]);
-        asm volatile("" : "+v"(acc[p][mat]));  // ... and ends here: one matrix at a time
+        for (int i = 0; i < kBmaxPerLane; i++) m = fmaxf(m, bm[i]);
+        for (int j = lane + 64 * kBmaxPerLane; j < A.in_nb; j += 64)
+          m = fmaxf(m, PERSIST ? ld_dev_f32(A.in_aux + j) : A.in_aux[j]);
+        amax = wave_max(m);
       }
+      const bool zero = amax == 0.0f;
+      const float inv = zero ? 0.0f : 127.0f / amax;  // IEEE division, as the quantiser
+      a_scale = zero ? 0.0f : amax / 127.0f;
+#pragma unroll
+      for (int p = 0; p < NP; p++) {
+        if (PERSIST && 2 * p >= gsv) break;
+        if constexpr (IN == kInF32) {
+          qv[p] = quant4(xf[p].x, xf[p].y, xf[p].z, xf[p].w, inv, zero);
+        } else {
+          qv[p] = quant4(half_bits(xh[p].x & 0xffffu), half_bits(xh[p].x >> 16),
+                         half_bits(xh[p].y & 0xffffu), half_bits(xh[p].y >> 16), inv, zero);
+        }
+      }
+    }
+    if constexpr (LX) {  // the wave's own slice: no barrier needed
+#pragma unroll
+      for (int p = 0; p < NP; p++) {
+        const int jl = 2 * p + hsel;
+        if (jl < gsv) qs[jl * 32 + word] = qv[p];
+      }
+    }
+    // 2B: activation sum of every group of the slice (a 32-lane reduction)
+    int xsum[GS];
+    if constexpr (FMT == 1) {
+#pragma unroll
+      for (int p = 0; p < NP; p++) {
+        if (PERSIST && 2 * p >= gsv) break;
+        int s = sdot4(qv[p], 0x01010101u, 0);
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off, 32);
+        xsum[2 * p] = __builtin_amdgcn_readlane(s, 0);
+        if (2 * p + 1 < GS) xsum[2 * p + 1] = __builtin_amdgcn_readlane(s, 32);
+      }
+    }
+
+    // ---- 4. pipelined decode + integer dot + scale -------------------------
+    const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
+#pragma unroll
+    for (int p = 0; p < NPART; p++)
+#pragma unroll
+      for (int mat = 0; mat < NMAT; mat++) acc[p][mat] = 0.0f;
+    // Empty asm statements (kept in program order) pin the schedule through
+    // data dependences: a group's activation words enter its iteration
+    // through one; each matrix's weight words enter through one (so the wait
+    // for its loads lands there) and its accumulator leaves through another,
+    // so one matrix's lookups and dots are in flight at a time; the loads of
+    // issue() take their group index from one.  Without them the compiler
+    // interleaves iterations and holds several groups' lookups at once.
+#pragma unroll
+    for (int i = 0; i < GS; i++) {
+      if (PERSIST && i >= gsv) break;
+      if (i + D0 < GS && (!PERSIST || i + D0 < gsv)) issue(i + D0);
+      asm volatile("" : "+v"(qv[i >> 1]));
+      XRegs<1> xa;  // SGPRs (v_readlane) or, with LX, VGPRs (LDS)
+      if constexpr (LX) {
+        const uint4 *xq = reinterpret_cast<const uint4 *>(qs + i * 32);
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          const uint4 t = xq[k];
+          xa.v[0][4 * k] = t.x;
+          xa.v[0][4 * k + 1] = t.y;
+          xa.v[0][4 * k + 2] = t.z;
+          xa.v[0][4 * k + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 32; k++) xa.v[0][k] = __builtin_amdgcn_readlane(qv[i >> 1], 32 * (i & 1) + k);
+      }
+      const bool live = i < ns;
+      const int part = SPLIT ? sb[i] - bw0 : 0;
+#pragma unroll
+      for (int mat = 0; mat < NMAT; mat++) {
+#pragma unroll
+        for (int k = 0; k < WPG; k++) asm volatile("" : "+v"(wd[mat][i][k]));  // this matrix starts here
+        int S[1] = {0};
+        float sc;
+        if constexpr (FMT == 0) {
+          const uint32_t w[7] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2], wd[mat][i][3],
+                                 wd[mat][i][4], wd[mat][i][5], wd[mat][i][6]};
+          if constexpr (LX) S[0] = b3_group_v(lut, laneoff, w, xa.v[0]);
+          else b3_group<1>(lut, laneoff, w, xa, S);
+          sc = half_bits(wd[mat][i][6] >> 16);
+        } else {
+          const uint32_t w[9] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2],
+                                 wd[mat][i][3], wd[mat][i][4], wd[mat][i][5],
+                                 wd[mat][i][6], wd[mat][i][7], wd[mat][i][8]};
+          if constexpr (FMT == 1) {
+            const int xs[1] = {xsum[i]};
+            tb_group<1>(w, xa, xs, S);
+          } else {
+            S[0] = bp_group(w, xa);
+          }
+          sc = half_bits(wd[mat][i][8]);
+        }
+        if constexpr (SUMS) {
+          if (live && lane < (int)L.valid_rows(sb[i]))
+            A.sums[((size_t)mat * N + (size_t)sb[i] * tq::kBlockRows + lane) * G + sg[i]] = S[0];
+          continue;
+        }
+        const float s = live ? sc : 0.0f;
+#pragma unroll
+        for (int p = 0; p < NPART; p++) {
+          acc[p][mat] = fmaf(p == part ? s : 0.0f, (float)S[0], acc[p][mat]);
+          asm volatile("" : "+v"(acc[p][mat]));  // ... and ends here: one matrix at a time
+        }
+      }
+    }
+    if constexpr (SUMS) {
+      if (wg == 0 && tid == 0 && A.sums_scale) *A.sums_scale = a_scale;
     }
   }
 
-  if constexpr (SUMS) {
-    if (wg == 0 && tid == 0 && A.sums_scale) *A.sums_scale = a_scale;
-    return;
-  }
-
-  // ---- 5. reduce: waves in LDS, cut blocks through the workspace ----------
+  // ---- 5. reduce: waves in LDS, cut blocks through the workspace, store --
+  // (PERSIST: the stores are issued but not waited for)
+  __device__ __forceinline__ void finish(const ProjLds &sm) {
+    if constexpr (SUMS) return;
+    const Layout L(FMT, A.N, A.K);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    float *red = sm.red;
 #pragma unroll
-  for (int p = 0; p < NPART; p++)
-#pragma unroll
-    for (int mat = 0; mat < NMAT; mat++)
-      red[((p * NMAT + mat) * kNW + wave) * 64 + lane] = acc[p][mat];
-  __syncthreads();
-  // wave p finishes block bw0 + p of the range (if the range reaches it)
-  const int part = wave, b = bw0 + part;
-  if (part >= NPART || b > ilast_b) return;
-  float tot[NMAT];
-#pragma unroll
-  for (int mat = 0; mat < NMAT; mat++) {
-    float s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kNW; w++) s += red[((part * NMAT + mat) * kNW + w) * 64 + lane];
-    tot[mat] = s;
-  }
-  const size_t n = (size_t)b * tq::kBlockRows + lane;
-  const bool row_ok = lane < (int)L.valid_rows(b);
-  // The pieces of a block cut over several workgroups meet (tq_proj.h).
-  bool fin = row_ok;  // this lane stores row n
-  if constexpr (SPLIT) {
-    // each range holds at least G items, so a cut block has two pieces
-    const int wf = item_wg(b * G, A, G), wl = item_wg(b * G + G - 1, A, G);
-    if (wf != wl) fin = meet_tree<NMAT>(tot, row_ok, wg - wf, 2, meet_slot0<NMAT>(A, b, lane), 64);
-  } else if (A.C > 1 && A.meet) {
-    fin = meet_tree<NMAT>(tot, row_ok, wg - b * A.C, A.C, meet_slot0<NMAT>(A, b, lane), 64);
-  } else if (A.C > 1) {
-    const int c = wg - b * A.C;
-    if (row_ok) {
+    for (int p = 0; p < NPART; p++)
 #pragma unroll
       for (int mat = 0; mat < NMAT; mat++)
-        __hip_atomic_store(&A.partials[((size_t)c * NMAT + mat) * N + n], tot[mat], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // the partial sums have reached device scope
-    uint32_t prev = 0;
-    if (lane == 0)
-      prev = __hip_atomic_fetch_add(&A.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __shfl(prev, 0, 64);
-    if (prev != (uint32_t)(A.C - 1)) return;  // another chunk finishes this block
+        red[((p * NMAT + mat) * kNW + wave) * 64 + lane] = acc[p][mat];
+    __syncthreads();
+    // wave p finishes block bw0 + p of the range (if the range reaches it)
+    const int part = wave, b = bw0 + part;
+    if (part >= NPART || b > ilast_b) return;
+    float tot[NMAT];
 #pragma unroll
     for (int mat = 0; mat < NMAT; mat++) {
       float s = 0.0f;
-      if (row_ok) {
-        for (int cc = 0; cc < A.C; cc++)
-          s += __hip_atomic_load(&A.partials[((size_t)cc * NMAT + mat) * N + n], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-        // consumed: leave the workspace zero for the next call, whatever its shape
-        for (int cc = 0; cc < A.C; cc++)
-          __hip_atomic_store(&A.partials[((size_t)cc * NMAT + mat) * N + n], 0.0f, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      }
+#pragma unroll
+      for (int w = 0; w < kNW; w++) s += red[((part * NMAT + mat) * kNW + w) * 64 + lane];
       tot[mat] = s;
     }
-    if (lane == 0) __hip_atomic_store(&A.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  float y;
-  if (NMAT == 1) {
-    y = a_scale * tot[0];
-  } else {
-    const float yg = a_scale * tot[0], yu = a_scale * tot[NMAT - 1];
-    y = yg / (1.0f + expf(-yg)) * yu;
-  }
-  if constexpr (NMAT == 1) {
-    if (A.out_signs) {
-      // Online Hadamard rotation of the block before the next projection
-      // consumes it ("Ternary Bonsai 2 27B…", section "后面还有没有优化空间"):
-      // Sylvester's H_64 over the 64 rows (lanes), butterflies in double,
-      // scaled by 1/8, then the row's sign.  Every row is valid (N % 64 == 0).
-      double v = (double)y;
+    const size_t n = (size_t)b * tq::kBlockRows + lane;
+    const bool row_ok = lane < (int)L.valid_rows(b);
+    // The pieces of a block cut over several workgroups meet (tq_proj.h).
+    bool fin = row_ok;  // this lane stores row n
+    if constexpr (SPLIT) {
+      // each range holds at least G items, so a cut block has two pieces
+      const int wf = item_wg(b * G, A, G), wl = item_wg(b * G + G - 1, A, G);
+      if (wf != wl) fin = meet_tree<NMAT>(tot, row_ok, wg - wf, 2, meet_slot0<NMAT>(A, b, lane), 64);
+    } else if (A.C > 1 && A.meet) {
+      fin = meet_tree<NMAT>(tot, row_ok, wg - b * A.C, A.C, meet_slot0<NMAT>(A, b, lane), 64);
+    } else if (A.C > 1) {
+      const int c = wg - b * A.C;
+      if (row_ok) {
 #pragma unroll
-      for (int h = 1; h < 64; h <<= 1) {
-        const double o = __shfl_xor(v, h, 64);
-        v = (lane & h) ? o - v : v + o;
+        for (int mat = 0; mat < NMAT; mat++)
+          __hip_atomic_store(&A.partials[((size_t)c * NMAT + mat) * N + n], tot[mat], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       }
-      const float r = (float)(v * 0.125);
-      y = A.out_signs[n] < 0 ? -r : r;
+      __builtin_amdgcn_s_waitcnt(0);  // the partial sums have reached device scope
+      uint32_t prev = 0;
+      if (lane == 0)
+        prev = __hip_atomic_fetch_add(&A.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      prev = __shfl(prev, 0, 64);
+      if (prev != (uint32_t)(A.C - 1)) return;  // another chunk finishes this block
+#pragma unroll
+      for (int mat = 0; mat < NMAT; mat++) {
+        float s = 0.0f;
+        if (row_ok) {
+          for (int cc = 0; cc < A.C; cc++)
+            s += __hip_atomic_load(&A.partials[((size_t)cc * NMAT + mat) * N + n], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+          // consumed: leave the workspace zero for the next call, whatever its shape
+          for (int cc = 0; cc < A.C; cc++)
+            __hip_atomic_store(&A.partials[((size_t)cc * NMAT + mat) * N + n], 0.0f, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        tot[mat] = s;
+      }
+      if (lane == 0) __hip_atomic_store(&A.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float y;
+    if (NMAT == 1) {
+      y = a_scale * tot[0];
+    } else {
+      const float yg = a_scale * tot[0], yu = a_scale * tot[NMAT - 1];
+      y = yg / (1.0f + expf(-yg)) * yu;
+    }
+    if constexpr (NMAT == 1) {
+      if (A.out_signs) {
+        // Online Hadamard rotation of the block before the next projection
+        // consumes it ("Ternary Bonsai 2 27B…", section "Decode 为什么只能算一般":
+        // a Hadamard transform shared by gate and up, the sign multiply merged
+        // into the path): Sylvester's H_64 over the 64 rows (lanes),
+        // butterflies in double, scaled by 1/8, then the row's sign.  Every
+        // row is valid (N % 64 == 0).
+        double v = (double)y;
+#pragma unroll
+        for (int h = 1; h < 64; h <<= 1) {
+          const double o = __shfl_xor(v, h, 64);
+          v = (lane & h) ? o - v : v + o;
+        }
+        const float r = (float)(v * 0.125);
+        y = A.out_signs[n] < 0 ? -r : r;
+      }
+    }
+    if (fin) {
+      if constexpr (PERSIST) st_dev_f32(A.out + n, y);
+      else A.out[n] = y;
+    }
+    if (A.out_bmax) {
+      const float m = wave_max(fin ? fabsf(y) : 0.0f);
+      if constexpr (PERSIST) {
+        // the array was zeroed before this projection; |y| >= 0, so the
+        // bits order as the values
+        if (lane == 0 && __ballot(fin) != 0)
+          __hip_atomic_fetch_max(reinterpret_cast<uint32_t *>(A.out_bmax) + b, __float_as_uint(m),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+      }
+      const uint64_t fm = __ballot(fin), vm = __ballot(row_ok);
+      if (fm == vm) {
+        if (lane == 0) A.out_bmax[b] = m;  // this wave stored every row of the block
+      } else if (fm != 0 && lane == 0) {
+        // exchange meet, rows finished by several workgroups: each adds its
+        // maximum (|y| >= 0, so the bits order as the values) and then, once
+        // that is done, its row count; the one completing the count stores
+        uint32_t *mm = A.meet_max + 2 * (size_t)b;
+        __hip_atomic_fetch_max(&mm[0], __float_as_uint(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        const uint32_t k = (uint32_t)__popcll(fm), rows = (uint32_t)__popcll(vm);
+        const uint32_t prev = __hip_atomic_fetch_add(&mm[1], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev + k == rows) {
+          A.out_bmax[b] = __uint_as_float(__hip_atomic_load(&mm[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          __hip_atomic_store(&mm[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&mm[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
     }
   }
-  if (fin) A.out[n] = y;
-  if (A.out_bmax) {
-    const float m = wave_max(fin ? fabsf(y) : 0.0f);
-    const uint64_t fm = __ballot(fin), vm = __ballot(row_ok);
-    if (fm == vm) {
-      if (lane == 0) A.out_bmax[b] = m;  // this wave stored every row of the block
-    } else if (fm != 0 && lane == 0) {
-      // exchange meet, rows finished by several workgroups: each adds its
-      // maximum (|y| >= 0, so the bits order as the values) and then, once
-      // that is done, its row count; the one completing the count stores
-      uint32_t *mm = A.meet_max + 2 * (size_t)b;
-      __hip_atomic_fetch_max(&mm[0], __float_as_uint(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);
-      const uint32_t k = (uint32_t)__popcll(fm), rows = (uint32_t)__popcll(vm);
-      const uint32_t prev = __hip_atomic_fetch_add(&mm[1], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev + k == rows) {
-        A.out_bmax[b] = __uint_as_float(__hip_atomic_load(&mm[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        __hip_atomic_store(&mm[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&mm[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
+};
+
+// LX: the quantised activations go through LDS into VGPRs instead of
+// v_readlane into SGPRs: fewer VALU operations per group but up to about
+// 140 VGPRs, so it is launched only for grids of at most one workgroup per
+// CU (two waves per SIMD, 256 VGPRs); bigger grids keep the SGPR form
+// within 128 VGPRs (two workgroups per CU).
+template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX, bool SUMS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LX ? 2 : 4)))
+void proj_kernel(ProjArgs A) {
+  constexpr int NPART = SPLIT ? kMaxParts : 1;
+  __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
+  __shared__ float red[NPART * NMAT * kNW * 64];
+  __shared__ float wmax[kNW];
+  __shared__ __attribute__((aligned(16))) uint32_t qs[LX ? kNW * GS * 32 : 1];
+  // The digit table depends on nothing: its LDS stores overlap the kernel
+  // argument loads and the address arithmetic of the body.
+  if constexpr (FMT == 0) fill_b3_lut<kThreads>(lut);
+  const ProjLds sm{lut, red, wmax, qs};
+  ProjRun<FMT, NMAT, IN, GS, D, SPLIT, LX, SUMS, false> r;
+  r.setup(A, (int)blockIdx.x, GS);
+  r.load_inputs();
+  // The CU returns vector loads in issue order, so activation loads issued
+  // behind other waves' weight loads would wait for those weights: every
+  // wave issues its activation loads before any wave of the workgroup
+  // issues weights.
+  __syncthreads();
+  r.issue_first();
+  r.compute(sm);
+  r.finish(sm);
 }
 
 template <int FMT, int NMAT, int IN, bool LX, bool SUMS>

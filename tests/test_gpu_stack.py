@@ -1,8 +1,10 @@
-"""GPU parity of tq_decode_stack (one fused quantise+project launch per projection) against the
-oracle, layer by layer.  Each stage is checked on the GPU's own input of that
-stage (stage-isolated), because chained fp32 stages cannot be bit-exact
-end-to-end (an ulp of difference can move an int8 across a rounding tie);
-the chain as a whole is checked within the same tolerance."""
+"""GPU parity of the decode stack against the oracle, layer by layer:
+tq_decode_stack (one fused quantise+project launch per projection) and
+tq_decode_stack_persistent (one launch per 32 layers), which must agree bit
+for bit.  Each stage is checked on the GPU's own input
+of that stage (stage-isolated), because chained fp32 stages cannot be
+bit-exact end-to-end (an ulp of difference can move an int8 across a
+rounding tie); the chain as a whole is checked within the same tolerance."""
 import numpy as np
 import pytest
 
@@ -21,7 +23,8 @@ def _gpu():
     oracle.set_threads(8)
 
 
-def _run_stack(fmt, L, hidden, inter, qkv_out, o_in, seed, zero_layers=()):
+def _run_stack(fmt, L, hidden, inter, qkv_out, o_in, seed, zero_layers=(), persistent=False,
+               ffn_signs=None):
     import ternary_weight_base_amd as tq
     shapes = {"qkv": (qkv_out, hidden), "o": (hidden, o_in), "gate": (inter, hidden),
               "up": (inter, hidden), "down": (hidden, inter)}
@@ -47,11 +50,17 @@ def _run_stack(fmt, L, hidden, inter, qkv_out, o_in, seed, zero_layers=()):
     nbytes = tq.tq_decode_stack_workspace_bytes(fmt, L, hidden, inter, qkv_out, o_in)
     ws = torch.zeros((nbytes + 15) // 16 * 4, dtype=torch.int32, device="cuda")
     outs = []
+    sg = None if ffn_signs is None else dev(ffn_signs)
     for rep in range(2):  # twice: the workspace must come back ready for reuse
         tq.tq_decode_stack(fmt, L, hidden, inter, qkv_out, o_in, devw, dev(x), dev(a),
-                           y_qkv, y_o, h, y_out, ws)
+                           y_qkv, y_o, h, y_out, ws, persistent=persistent, ffn_signs=sg)
         torch.cuda.synchronize()
         outs.append([t.cpu().numpy().copy() for t in (y_qkv, y_o, h, y_out)])
+        assert tq.stack_timeouts(ws) == 0, "a wait of the persistent kernel gave up"
+        # all but the block maxima of y_o and h (the last two sections) left zero
+        r256 = lambda n: (n + 255) // 256 * 256
+        keep = r256((hidden + 63) // 64 * 4) + r256((inter + 63) // 64 * 4)
+        assert not ws[:(nbytes - keep) // 4].any().item(), "workspace not left zero"
     for r0, r1 in zip(*outs):
         assert np.array_equal(r0.view(np.uint32), r1.view(np.uint32)), "not deterministic"
     return host, x, a, outs[0]
@@ -138,3 +147,66 @@ def test_decode_stack_split_k_everywhere(fmt):
     say(f"stack split-K {FMTS[fmt]}")
     host, x, a, outs = _run_stack(fmt, 2, 2048, 5120, 1024, 2048, 51)
     _check_layers(host, x, a, outs, "splitk")
+
+
+@pytest.mark.parametrize("fmt", [B3, TB, BP])
+@pytest.mark.parametrize("L,hidden,inter,qkv_out,o_in", [(3, 640, 1152, 1280, 1024),
+                                                          (2, 2048, 5120, 1024, 2048),
+                                                          (1, 256, 20608, 384, 9216),
+                                                          (2, 5120, 17408, 10240, 8192),
+                                                          (33, 256, 512, 384, 256)])
+def test_persistent_matches_launches(fmt, L, hidden, inter, qkv_out, o_in):
+    """The persistent kernel and the per-projection launches run the same
+    plans, quantiser, integer cores and meets: every output equal bit for
+    bit (27B shapes; split K everywhere; long rows; 33 layers = two
+    persistent launches)."""
+    say(f"persistent vs launches {FMTS[fmt]} L={L} {hidden}/{inter}/{qkv_out}/{o_in}")
+    _, _, _, p = _run_stack(fmt, L, hidden, inter, qkv_out, o_in, 61 + L)
+    _, _, _, q = _run_stack(fmt, L, hidden, inter, qkv_out, o_in, 61 + L, persistent=True)
+    for name, u, v in zip(("y_qkv", "y_o", "h", "y_out"), p, q):
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), name
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
+def test_persistent_ffn_rotation_matches_launches(fmt):
+    """With the FFN input rotated in O's epilogue (counter meet), full shapes."""
+    say(f"persistent rotation {FMTS[fmt]}")
+    signs = synth.signs(synth.seed(71, 1), 2 * 5120).reshape(2, 5120)
+    _, _, _, p = _run_stack(fmt, 2, 5120, 17408, 10240, 8192, 71, ffn_signs=signs)
+    _, _, _, q = _run_stack(fmt, 2, 5120, 17408, 10240, 8192, 71, ffn_signs=signs, persistent=True)
+    for name, u, v in zip(("y_qkv", "y_o", "h", "y_out"), p, q):
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), name
+
+
+def test_persistent_wait_limit_gives_up_and_exits():
+    """Failure handling of the bounded waits, forced from the host: a wait
+    limit of one real-time tick (set in the workspace header) makes the
+    persistent kernel's waits give up; the launch still ends normally and
+    reports them in the workspace's first word.  A fresh workspace then
+    gives correct results again."""
+    import ternary_weight_base_amd as tq
+    say("persistent wait limit")
+    L, hidden, inter, qkv_out, o_in = 2, 640, 1152, 1280, 1024
+    shapes = {"qkv": (qkv_out, hidden), "o": (hidden, o_in), "gate": (inter, hidden),
+              "up": (inter, hidden), "down": (hidden, inter)}
+    devw = [[dev(tq.tq_pack(B3, synth.trits(synth.seed(81, l, i, 1), N, K),
+                            synth.scales(synth.seed(81, l, i, 2), N, K)))
+             for i, (N, K) in enumerate(shapes.values())] for l in range(L)]
+    x = dev(synth.normal_f16(synth.seed(81, 9, 1), L, hidden))
+    a = dev(synth.normal_f16(synth.seed(81, 9, 2), L, o_in))
+    outs = [torch.empty((L, n), device="cuda") for n in (qkv_out, hidden, inter, hidden)]
+    nbytes = tq.tq_decode_stack_workspace_bytes(B3, L, hidden, inter, qkv_out, o_in)
+    ws = torch.zeros((nbytes + 15) // 16 * 4, dtype=torch.int32, device="cuda")
+    ws[2] = 1  # wait limit: one tick (words 2..3, little endian)
+    tq.tq_decode_stack(B3, L, hidden, inter, qkv_out, o_in, devw, x, a, *outs, ws, persistent=True)
+    torch.cuda.synchronize()
+    assert tq.stack_timeouts(ws) > 0
+    ws.zero_()
+    tq.tq_decode_stack(B3, L, hidden, inter, qkv_out, o_in, devw, x, a, *outs, ws, persistent=True)
+    torch.cuda.synchronize()
+    assert tq.stack_timeouts(ws) == 0
+    ref = [t.clone() for t in outs]
+    tq.tq_decode_stack(B3, L, hidden, inter, qkv_out, o_in, devw, x, a, *outs, ws)
+    torch.cuda.synchronize()
+    for u, v in zip(ref, outs):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))

@@ -285,8 +285,11 @@ def test_device_entry_points_validate_on_host():
     assert Q(B3, 64, 256, FAKE, None, 0, FAKE, None, 0, FAKE, ODD, None) == -3
 
 
-def test_decode_stack_validates_on_host():
-    L = tq.lib
+@pytest.mark.parametrize("name", ["tq_decode_stack", "tq_decode_stack_persistent"])
+def test_decode_stack_validates_on_host(name):
+    class _L:  # the function under test in place of tq_decode_stack
+        tq_decode_stack = getattr(tq.lib, name)
+    L = _L
     args = (B3, 2, 640, 1152, 1280, 1024)
     need = tq.tq_decode_stack_workspace_bytes(*args)
     assert need > 0
