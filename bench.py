@@ -63,7 +63,7 @@ def parse():
 
 # The sources the dominant kernel (the projection kernel) is built from.
 DOMINANT_SOURCES = ("tq_proj.h", "tq_proj_kernel.h", "tq_proj.hip", "tq_proj_inst.hip", "tq_device.h",
-                    "tq_layout.h", "../../include/tq.h")
+                    "tq_layout.h")
 
 
 def kernel_source_sha() -> str:
@@ -243,12 +243,18 @@ def main():
     gu_bytes = 2 * stack.bytes["gate"] + HIDDEN * 4 + (HIDDEN // 64) * 4 + INTER * 4
     gu_us = time_graph(capture(gate_up_all), 5, 1) * 1000.0 / L
     gu_gbps = gu_bytes / (gu_us * 1e-6) / 1e9
-    traffic = None
+    traffic, trace = None, None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha") == kernel_source_sha() and tr.get("fmt") == args.fmt:
             traffic = tr.get("hbm_bytes_per_launch")
+            if tr.get("trace_avg_launch_us"):
+                t_us = tr["trace_avg_launch_us"]
+                trace = {"avg_launch_us": t_us, "achieved": round(gu_bytes / (t_us * 1e-6) / 1e9, 1),
+                         "frac": round(gu_bytes / (t_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                         "source": os.path.relpath(TRAFFIC_FILE, ROOT) + " (rocprofv3 kernel trace "
+                                   "of this script, same kernel sources)"}
     # ---- measured HBM read ceiling: a plain streaming read of 2 GiB (beyond
     # the 256 MB MALL), beside which the byte rates above are also reported
     rd = torch.ones(1 << 29, dtype=torch.int32, device=dev)
@@ -266,6 +272,7 @@ def main():
                 "kernel": "proj_kernel<fmt,2,fp32 input> (fused quantise + gate/up/SwiGLU, "
                           "2 x 17408x5120), as launched by the stack",
                 "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 3),
+                "trace": trace,
                 "frac_of_measured_read_ceiling": round(gu_gbps / read_gbps, 4)}
 
     # ---- the other rows of the hot path, measured on the same weights -------
@@ -294,8 +301,15 @@ def main():
             torch.cuda.empty_cache()
         extras["layout_ab"] = ab
 
-    # ---- CPU baseline: the oracle on a bounded sample of the same workload
-    cpu = cpu_baseline(synth, args.cpu_seconds, args.fmt) if args.cpu_seconds > 0 else None
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload,
+    # and the oracle's check of the timed run's own outputs (layers 0 and L-1)
+    cpu, parity = None, None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(synth, args.cpu_seconds, args.fmt)
+        graph.replay()  # the timed token once more, then its outputs
+        torch.cuda.synchronize()
+        outs = [t.cpu().numpy() for t in (y_qkv, y_o, h, y_dn)]
+        parity = stack_parity(synth, outs, x_in.cpu().numpy(), a_in.cpu().numpy(), sorted({0, L - 1}))
 
     out = {
         "metric": METRIC,
@@ -323,6 +337,7 @@ def main():
         "ffn_hadamard_tok_s": round(1000.0 / rot_ms, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
         "other_rows": extras,
     }
     print(json.dumps(out))
@@ -334,7 +349,8 @@ def cpu_baseline(synth, budget_s: float, fmt_name: str):
     Layers are run until the time budget is spent; tok/s = layers/s / 64."""
     import oracle
 
-    cores = min(16, len(os.sched_getaffinity(0)))
+    avail = len(os.sched_getaffinity(0))
+    cores = min(16, avail)
     oracle.set_threads(cores)
     fmt = oracle.FMT_B3 if fmt_name == "b3" else oracle.FMT_2B
     done, elapsed, l = 0, 0.0, 0
@@ -361,10 +377,47 @@ def cpu_baseline(synth, budget_s: float, fmt_name: str):
         l += 1
     layers_per_s = done / elapsed
     return {"value": round(layers_per_s / LAYERS, 4), "unit": "tok/s", "cores": cores,
-            "kind": "oracle",
+            "host_cpus_available": avail, "kind": "oracle",
             "sample": f"{done} of {LAYERS} layers of the same stack (unpack+quant+project+SwiGLU "
                       f"from canonical packed blobs, {fmt_name}), {elapsed:.1f} s; tok/s = "
                       f"layers/s / {LAYERS}"}
+
+
+def stack_parity(synth, outs, x_in, a_in, layers):
+    """The timed stack's own outputs against the oracle, stage-isolated (each
+    stage fed the GPU's input of that stage, so the int8 codes are bit-exact
+    and the fp32 outputs compare within the tolerance), on the given layers.
+    Runs with the CPU baseline (it is the oracle's part of this run)."""
+    import oracle
+
+    y_qkv, y_o, h, y_dn = outs
+    worst_abs, worst_l2 = 0.0, 0.0
+
+    def cmp(y, ref):
+        nonlocal worst_abs, worst_l2
+        y, ref = np.asarray(y, np.float64).ravel(), np.asarray(ref, np.float64).ravel()
+        peak = np.abs(ref).max()
+        worst_abs = max(worst_abs, float(np.abs(y - ref).max() / peak))
+        worst_l2 = max(worst_l2, float(np.linalg.norm(y - ref) / np.linalg.norm(ref)))
+
+    for l in layers:
+        hw = {}
+        for name, (N, K) in Stack.SHAPES.items():
+            seed = synth.seed(3, 1000 + l, Stack.MATRIX_ID[name])
+            hw[name] = (synth.trits(synth.seed(seed, 1), N, K), synth.scales(synth.seed(seed, 2), N, K))
+        q, sc = oracle.quant(x_in[l:l + 1])
+        cmp(y_qkv[l], oracle.gemv(*hw["qkv"], q, sc))
+        q, sc = oracle.quant(a_in[l:l + 1])
+        cmp(y_o[l], oracle.gemv(*hw["o"], q, sc))
+        q, sc = oracle.quant(y_o[l:l + 1])
+        cmp(h[l], oracle.swiglu(oracle.gemv(*hw["gate"], q, sc), oracle.gemv(*hw["up"], q, sc)))
+        q, sc = oracle.quant(h[l:l + 1])
+        cmp(y_dn[l], oracle.gemv(*hw["down"], q, sc))
+        del hw
+    return {"layers": list(layers), "max_abs_err_rel_to_peak": worst_abs, "max_rel_l2": worst_l2,
+            "tolerance": {"max_abs_err_rel_to_peak": 1e-3, "rel_l2": 1e-5},
+            "ok": worst_abs <= 1e-3 and worst_l2 <= 1e-5,
+            "how": "stage-isolated against the oracle, every output of the four projections"}
 
 
 def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time_graph):
@@ -548,48 +601,55 @@ def counter_summary(dirs):
 
 def profile_summary(trace_dir, fetch_dir, write_dir):
     """Text summary of a profiled bench run (printed) and the dominant kernel's
-    HBM traffic per launch (written to TRAFFIC_FILE).  The traffic counters are
-    scaled by what they read for the 64 MiB device copy the bench makes: its
-    true bytes are 64 MiB read and 64 MiB written."""
+    trace duration and HBM traffic per launch (written to TRAFFIC_FILE).
+    FETCH_SIZE is scaled by what it reads for the 2 GiB streaming read of the
+    same run (tq_debug_stream_read: every byte read exactly once, with the
+    same nontemporal 16-byte loads as the weights), WRITE_SIZE by what it
+    reads for the bench's 64 MiB device copy (64 MiB written)."""
     durs, _ = _rocpd(trace_dir)
     _, fetch = _rocpd(fetch_dir)
     _, write = _rocpd(write_dir)
-    calib = 64 << 20
-    dom = [n for n in durs if "proj_kernel<0, 2, 2," in n]
+    read_bytes, copy_bytes = 1 << 31, 64 << 20
+    dom = [n for n in durs if "proj_kernel<0, 2, 2," in n and "true, true, false>" in n]
     print("kernel                                                        calls   avg_us   total_ms")
-    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:24]:
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:28]:
         print(f"{name[:60]:60s} {len(v):7d} {sum(v) / len(v) / 1e3:8.3f} {sum(v) / 1e6:10.3f}")
 
     def per_dispatch(ctrs, cname, pick):
-        vals = [x for (k, cn), v in ctrs.items() if cn == cname and pick(k) for x in v]
-        return vals
+        return [x for (k, cn), v in ctrs.items() if cn == cname and pick(k) for x in v]
 
-    # the calibration copy: the runtime's buffer-copy dispatch whose counters
-    # sit nearest to 64 MiB (the other device copies are weight uploads of
-    # <= 20 MB); 1024 B per KiB
-    fcal = per_dispatch(fetch, "FETCH_SIZE", lambda k: "copyBuffer" in k)
+    fcal = per_dispatch(fetch, "FETCH_SIZE", lambda k: "stream_read_kernel" in k)
+    # the copy: the runtime's buffer-copy dispatch whose count sits nearest to 64 MiB
+    # (the other device copies are weight uploads of <= 20 MB); 1024 B per KiB
     wcal = per_dispatch(write, "WRITE_SIZE", lambda k: "copyBuffer" in k)
     if not dom or not fcal or not wcal:
-        raise SystemExit("dominant kernel or calibration copy not found in the profiles")
-    fcal = [max(fcal)]  # FETCH_SIZE reads about half the true bytes: the largest copy
-    wcal = [min(wcal, key=lambda v: abs(v - calib / 1024))]
-    fscale = calib / (fcal[0] * 1024)
-    wscale = calib / (wcal[0] * 1024)
+        raise SystemExit("dominant kernel or calibration dispatches not found in the profiles")
+    fscale = read_bytes / (sum(fcal) / len(fcal) * 1024)
+    wbest = min(wcal, key=lambda v: abs(v - copy_bytes / 1024))
+    wscale = copy_bytes / (wbest * 1024)
     f = per_dispatch(fetch, "FETCH_SIZE", lambda k: k in dom)
     w = per_dispatch(write, "WRITE_SIZE", lambda k: k in dom)
     fb = sum(f) / len(f) * 1024 * fscale
     wb = sum(w) / len(w) * 1024 * wscale
     dur = [x for n in dom for x in durs[n]]
+    avg_us = sum(dur) / len(dur) / 1e3
+    alg = 2 * 19496960 + 5120 * 4 + 80 * 4 + 17408 * 4  # weights, fp32 input, its maxima, output
     print(f"\ndominant kernel: {dom[0]}")
-    print(f"  launches traced {len(dur)}, avg duration {sum(dur) / len(dur) / 1e3:.3f} us")
-    print(f"  FETCH_SIZE per launch {sum(f) / len(f):.0f} KiB raw, x{fscale:.3f} (copy calibration) "
-          f"= {fb / 1e6:.3f} MB")
-    print(f"  WRITE_SIZE per launch {sum(w) / len(w):.0f} KiB raw, x{wscale:.3f} (copy calibration) "
-          f"= {wb / 1e6:.3f} MB")
-    print(f"  calibration copy of 64 MiB: FETCH_SIZE {max(fcal):.0f} KiB, WRITE_SIZE {max(wcal):.0f} KiB")
+    print(f"  launches traced {len(dur)}, avg duration {avg_us:.3f} us -> {alg / (avg_us * 1e3):.1f} GB/s "
+          f"algorithmic ({alg} B per launch), {alg / (avg_us * 1e3) / PEAK_HBM_GBPS:.4f} of 8 TB/s")
+    print(f"  FETCH_SIZE per launch {sum(f) / len(f):.0f} KiB raw, x{fscale:.4f} (2 GiB streaming-read "
+          f"calibration) = {fb / 1e6:.3f} MB")
+    print(f"  WRITE_SIZE per launch {sum(w) / len(w):.0f} KiB raw, x{wscale:.4f} (64 MiB copy "
+          f"calibration) = {wb / 1e6:.3f} MB")
+    print(f"  calibration: streaming read of {read_bytes} B: FETCH_SIZE {sum(fcal) / len(fcal):.0f} KiB per "
+          f"dispatch ({len(fcal)} dispatches); copy of {copy_bytes} B: WRITE_SIZE {wbest:.0f} KiB")
     out = {"kernel": dom[0], "fmt": "b3", "kernel_source_sha": kernel_source_sha(),
+           "trace_avg_launch_us": round(avg_us, 3), "trace_launches": len(dur),
+           "algorithmic_bytes_per_launch": alg,
            "hbm_bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
-           "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)}
+           "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+           "fetch_calibration": "stream_read_kernel, 2 GiB read once",
+           "write_calibration": "64 MiB device copy"}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(f"\nwrote {os.path.relpath(TRAFFIC_FILE, ROOT)}")

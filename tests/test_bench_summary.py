@@ -1,7 +1,8 @@
 """Host logic of bench.py's profile summaries (CPU): the dominant kernel's HBM
-traffic is its FETCH_SIZE / WRITE_SIZE per dispatch scaled by what the same
-counters read for the bench's 64 MiB device copy, and the counter summary
-averages each counter per dispatch.  Synthetic rocprofv3-style databases."""
+traffic is its FETCH_SIZE per dispatch scaled by what the same counter reads
+for the 2 GiB streaming read, and its WRITE_SIZE scaled by what that counter
+reads for the bench's 64 MiB device copy; the counter summary averages each
+counter per dispatch.  Synthetic rocprofv3-style databases."""
 import json
 import os
 import sqlite3
@@ -10,8 +11,10 @@ import pytest
 
 import bench
 
-DOM = "void tqproj::proj_kernel<0, 2, 2, 6, 2, true, true>(tqproj::ProjArgs)"
+DOM = "void tqproj::proj_kernel<0, 2, 2, 6, 2, true, true, false>(tqproj::ProjArgs)"
+SUMS = "void tqproj::proj_kernel<0, 2, 2, 6, 2, true, true, true>(tqproj::ProjArgs)"
 COPY = "__amd_rocclr_copyBuffer"
+READ = "void (anonymous namespace)::stream_read_kernel(uint4 const*, unsigned long, unsigned int*)"
 
 
 def _db(path, kernels=(), counters=()):
@@ -28,15 +31,16 @@ def _db(path, kernels=(), counters=()):
     c.close()
 
 
-def test_profile_summary_scales_traffic_by_the_copy(tmp_path, monkeypatch, capsys):
+def test_profile_summary_scales_traffic_by_the_calibrations(tmp_path, monkeypatch, capsys):
     kt, fe, wr = (str(tmp_path / d) for d in ("kt", "fetch", "write"))
     _db(os.path.join(kt, "a", "kt.db"),
-        kernels=[(DOM, 12000), (DOM, 13000), ("other_kernel", 5000)])
+        kernels=[(DOM, 12000), (DOM, 13000), ("other_kernel", 5000), (SUMS, 99000)])
     # per dispatch the counter arrives split over instances (summed per dispatch);
-    # the copy reads half its true bytes (scale 2) and writes them all (scale 1)
+    # the streaming read of 2 GiB reports half its true bytes (scale 2), the
+    # copy's writes are counted in full (scale 1)
     _db(os.path.join(fe, "f.db"),
-        counters=[(COPY, "FETCH_SIZE", 1, 16384), (COPY, "FETCH_SIZE", 1, 16384),
-                  (COPY, "FETCH_SIZE", 2, 1000),              # a small upload copy
+        counters=[(READ, "FETCH_SIZE", 1, 524288), (READ, "FETCH_SIZE", 1, 524288),
+                  (COPY, "FETCH_SIZE", 2, 1000),              # not a calibration
                   (DOM, "FETCH_SIZE", 3, 9000), (DOM, "FETCH_SIZE", 3, 10000),
                   (DOM, "FETCH_SIZE", 4, 21000)])
     _db(os.path.join(wr, "w.db"),
@@ -54,9 +58,10 @@ def test_profile_summary_scales_traffic_by_the_copy(tmp_path, monkeypatch, capsy
     assert rec["kernel_source_sha"] == bench.kernel_source_sha()
     text = capsys.readouterr().out
     assert "avg duration 12.500 us" in text
+    assert rec["trace_avg_launch_us"] == 12.5 and rec["trace_launches"] == 2
 
 
-def test_profile_summary_needs_the_calibration_copy(tmp_path, monkeypatch):
+def test_profile_summary_needs_the_calibrations(tmp_path, monkeypatch):
     kt, fe, wr = (str(tmp_path / d) for d in ("kt", "fetch", "write"))
     _db(os.path.join(kt, "kt.db"), kernels=[(DOM, 12000)])
     _db(os.path.join(fe, "f.db"), counters=[(DOM, "FETCH_SIZE", 1, 9000)])
