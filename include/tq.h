@@ -178,6 +178,22 @@ int tq_hadamard_quant_act(int dtype, int64_t M, int64_t K, const void *x, const 
 
 /* ---- device: decode GEMV (M <= 16 tokens) ----------------------------- */
 
+/* tq_gemv for callers that cannot allocate (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels
+ * and results (bit for bit) with the workspace taken from a fixed array of
+ * TQ_NOALLOC_SCRATCH_BYTES in device memory that the library owns, one per
+ * GPU, set up at the first call on each device and held until the process
+ * ends.  No allocation happens in the call.  Each call zero-fills the part
+ * it needs with a small kernel before the GEMV (both enqueued on `stream`).
+ * TQ_ERR_SIZE if this shape's workspace (tq_gemv_workspace_bytes) exceeds
+ * the array.  All calls on one GPU share its array: calls that may run
+ * concurrently on one GPU (different streams, graphs replayed concurrently)
+ * race on it and must not be made.  Other arguments and errors as tq_gemv. */
+#define TQ_NOALLOC_SCRATCH_BYTES (4u << 20)
+int tq_gemv_noalloc(int fmt, int64_t M, int64_t N, int64_t K, const void *W, const int8_t *q,
+                    const float *a_scale, float *y, void *stream);
+size_t tq_noalloc_scratch_bytes(void); /* TQ_NOALLOC_SCRATCH_BYTES, as built */
+
 /* Workspace bytes tq_gemv / tq_gemv_gate_up_swiglu need for this shape
  * (0 when the launch does not split K across workgroups).  The workspace
  * is device memory that must be zero-filled once before its first use;

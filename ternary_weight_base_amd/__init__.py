@@ -36,7 +36,8 @@ EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant
            "tq_gemv_quant_workspace_bytes", "tq_gemv_quant",
            "tq_decode_stack_workspace_bytes", "tq_decode_stack", "tq_hadamard_quant_act",
            "tq_ternarize", "tq_debug_stream_read", "tq_debug_gate_up_sums",
-           "tq_debug_gemv_quant_sums", "tq_decode_stack_persistent")
+           "tq_debug_gemv_quant_sums", "tq_decode_stack_persistent",
+           "tq_gemv_noalloc", "tq_noalloc_scratch_bytes")
 
 
 class TqLayer(ctypes.Structure):
@@ -74,6 +75,8 @@ def _load():
         "tq_decode_stack_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "tq_decode_stack": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
         "tq_decode_stack_persistent": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
+        "tq_gemv_noalloc": ([I, I64, I64, I64, P, P, P, P, P], I),
+        "tq_noalloc_scratch_bytes": ([], SZ),
         "tq_hadamard_quant_act": ([I, I64, I64, P, P, P, P, P], I),
         "tq_ternarize": ([I64, I64, P, P, P], I),
         "tq_debug_stream_read": ([P, SZ, P, I64, P], I),
@@ -190,6 +193,12 @@ def tq_gemv(fmt, M, N, K, W, q, a_scale, y, ws=None, stream=None) -> None:
     wp, wb = _ws(ws)
     _check(lib.tq_gemv(fmt, M, N, K, _ptr(W), _ptr(q), _ptr(a_scale), _ptr(y), wp, wb,
                        _stream(stream)), "tq_gemv")
+
+
+def tq_gemv_noalloc(fmt, M, N, K, W, q, a_scale, y, stream=None) -> None:
+    """tq_gemv with the library's own fixed device scratch array as workspace."""
+    _check(lib.tq_gemv_noalloc(fmt, M, N, K, _ptr(W), _ptr(q), _ptr(a_scale), _ptr(y), _stream(stream)),
+           "tq_gemv_noalloc")
 
 
 def tq_gemv_gate_up_swiglu(fmt, M, N, K, Wg, Wu, q, a_scale, h, ws=None, stream=None) -> None:

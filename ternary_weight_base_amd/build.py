@@ -62,7 +62,7 @@ def build() -> str:
     objs, cmds = [], []
     units = [(src, src.replace(".hip", ".o"), []) for src in
              ("tq_kernels.hip", "tq_proj.hip", "tq_gemv_mfma.hip", "tq_hadamard.hip", "tq_gemm.hip",
-              "tq_stream.hip")]
+              "tq_stream.hip", "tq_noalloc.hip")]
     # the projection kernel: one object per (packed format, activation form, output kind)
     for fmt, fname in ((0, "b3"), (1, "2b"), (2, "bp")):
         for lx in (1, 0):

@@ -274,6 +274,14 @@ def test_device_entry_points_validate_on_host():
     assert L.tq_debug_gate_up_sums(B3, 1, 64, 128, FAKE, None, FAKE, FAKE, None) == -1
     assert L.tq_debug_gate_up_sums(B3, 17, 64, 128, FAKE, FAKE, FAKE, FAKE, None) == -2
     assert L.tq_debug_gate_up_sums(B3, 1, 64, 128, FAKE, MIS, FAKE, FAKE, None) == -3
+    # the allocation-free GEMV: every rejection before any device work
+    NA = L.tq_gemv_noalloc
+    assert NA(B3, 1, 5120, 17408, None, FAKE, FAKE, FAKE, None) == -1
+    assert NA(B3, 8, 5120, 17408, FAKE, MIS, FAKE, FAKE, None) == -3
+    assert NA(B3, 8, 5120, 17408, FAKE, FAKE, FAKE, ODD, None) == -3
+    assert NA(B3, 17, 5120, 17408, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert NA(9, 1, 5120, 17408, FAKE, FAKE, FAKE, FAKE, None) == -5
+    assert L.tq_noalloc_scratch_bytes() == 4 << 20
     # fused-quantiser sums: (fmt, N, K, W, Wu, x_dtype, x, x_bmax, x_nb, S, a_scale, stream)
     Q = L.tq_debug_gemv_quant_sums
     assert Q(B3, 64, 256, FAKE, None, 0, FAKE, None, 0, None, None, None) == -1
