@@ -159,7 +159,7 @@ int tq_quant_act(int dtype, int64_t M, int64_t K, const void *x, int8_t *q, floa
  * quantisation of the rotated rows.  The pages place a Hadamard transform,
  * shared by gate and up, in front of the fused gate/up/SwiGLU kernel, with a
  * sign multiply merged into the path after it ("Ternary Bonsai 2 27B：8GB
- * 显卡硬塞 27B 三元模型…", section "后面还有没有优化空间").  Block size and
+ * 显卡硬塞 27B 三元模型…", section "Decode 为什么只能算一般").  Block size and
  * signs are not given there; this library rotates each block of 64
  * consecutive elements of a row:
  *   r_i = s_i * (1/8) * sum_{j<64} (-1)^popcount(i & j) x_j

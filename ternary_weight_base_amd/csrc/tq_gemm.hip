@@ -38,10 +38,12 @@ using namespace tqdev;
 
 constexpr int kBtStride = 144;  // 128 trits + 16 bytes of padding per row
 
-// An 8-copy digit table (16 KB; the decode is a small share of the work,
-// so its bank conflicts cost little): with the B tile and the activation
-// tile, 41 KB per workgroup at TM = 2, three workgroups per CU.  Entry v of copy c at
-// byte v * 64 + c * 8; lane l reads copy l % 8.
+// An 8-copy digit table (16 KB): with the B tile and the activation tile,
+// 41 KB per workgroup at TM = 2, three workgroups per CU.  Entry v of copy c
+// at byte v * 64 + c * 8; lane l reads copy l % 8.  Lanes decoding bytes
+// whose entries share a bank collide: the SQ counters of the 128-row tile
+// put LDS bank-conflict cycles at about 1.15x the LDS-active cycles, with
+// LDS issue waits near a fifth of the waves' lifetime.
 constexpr int kLut8Copies = 8;
 
 __device__ __forceinline__ void fill_lut8(uint2 *lut) {

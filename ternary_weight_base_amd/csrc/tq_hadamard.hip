@@ -4,7 +4,7 @@
 // The pages put a Hadamard transform in front of the fused gate/up/SwiGLU
 // kernel, shared by both projections, with a sign multiply merged into the
 // path after it ("Ternary Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section
-// "后面还有没有优化空间").  Readings (the pages give neither size nor signs):
+// "Decode 为什么只能算一般").  Readings (the pages give neither size nor signs):
 // blocks of 64 consecutive elements, Sylvester's Hadamard matrix H_64 scaled
 // by 1/8 (an orthogonal map), then one sign +-1 per element:
 //   r_i = s_i * (1/8) * sum_j (-1)^popcount(i & j) x_j.

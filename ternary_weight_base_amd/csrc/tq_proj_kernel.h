@@ -8,8 +8,9 @@
 // the group's fp16 scale ("三值权重 27B 压到 5.9GB｜本地部署成本账单重算",
 // section 三; "Ternary Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section
 // "Decode 为什么只能算一般"), the activations quantised per token to int8 by
-// absmax (same page, section "后面还有没有优化空间").  The Bonsai page runs
-// the activation quantiser as its own launch and measures it at about 1.1 us;
+// absmax (same page, section "后面还有没有优化空间", first item: Q8
+// activations).  The Bonsai page runs the activation quantiser as its own
+// launch and measures it at about 1.1 us (section "Decode 为什么只能算一般");
 // here it is folded into the projection that consumes it.
 //
 // A work item is one (64-row weight block, K group of 128) pair, items in
