@@ -143,8 +143,12 @@ def test_gemv_quant_group_sums(fmt, N, K, dtype, gate_up):
 
 
 def _tile_rows(M):
-    """Token rows that touch every 64-, 128- and 256-row token tile and its edges."""
+    """Token rows that touch every 16-row token tile (one row of each, at a
+    position that moves from tile to tile) and the edges of every 64-row
+    stretch."""
     rows = {0, 15, 16, 63, M - 1}
+    for t in range((M + 15) // 16):
+        rows.add(16 * t + (7 * t) % 16)
     for edge in range(64, M, 64):
         rows |= {edge - 1, edge}
     return np.array(sorted(r for r in rows if 0 <= r < M))
@@ -157,7 +161,8 @@ def test_gemm_group_sums(fmt, M, N, K):
     """The prefill GEMM's own plan: 64-row tiles with K chunks for M <= 64,
     128- or 256-row tiles (a ragged last tile at M = 400) above.  Every
     element is written (no sentinel left); the sums of token rows touching
-    every tile equal the oracle's over all N and all groups."""
+    every 16-row stretch and every tile edge equal the oracle's over all N
+    and all groups."""
     say(f"gemm sums {FMTS[fmt]} M={M} N={N} K={K}")
     tq = _tq()
     seed = 7500 + N

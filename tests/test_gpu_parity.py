@@ -264,8 +264,12 @@ def test_gemm_vs_oracle(fmt, M, N, K):
 
 
 def _tile_rows(M):
-    """Token rows that touch every 64-, 128- and 256-row token tile and its edges."""
+    """Token rows that touch every 16-row token tile (one row of each, at a
+    position that moves from tile to tile) and the edges of every 64-row
+    stretch."""
     rows = {0, 15, 16, 63, M - 1}
+    for t in range((M + 15) // 16):
+        rows.add(16 * t + (7 * t) % 16)
     for edge in range(64, M, 64):
         rows |= {edge - 1, edge}
     return np.array(sorted(r for r in rows if 0 <= r < M))
@@ -293,10 +297,11 @@ def _gemm_full_check(fmt, M, N, K, seed):
 
 
 @pytest.mark.parametrize("fmt", [B3, TB])
-@pytest.mark.parametrize("M,N,K", [(400, 5120, 17408), (512, 14336, 1024)])
+@pytest.mark.parametrize("M,N,K", [(330, 5120, 17408), (400, 5120, 17408), (512, 14336, 1024)])
 def test_gemm_wide_tile_full(fmt, M, N, K):
-    """Shapes on which the GEMM takes 256-token tiles: a ragged last token
-    tile with a 3-way K split, and 448 tiles with no split."""
+    """256-token tiles with a ragged last tile and a 3-way K split (M = 400),
+    128-token tiles with a 3-way split (M = 330), and 448 256-token tiles
+    with no split (short K)."""
     say(f"gemm wide {FMTS[fmt]} M={M} N={N} K={K}")
     _gemm_full_check(fmt, M, N, K, 6700 + M)
 

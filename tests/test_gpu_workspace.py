@@ -86,7 +86,7 @@ def test_one_workspace_for_every_call(fmt):
     rotated(5120, 8192, 7030)       # rotated output: counter
     gemv(4, 5120, 17408, 7040)      # MFMA GEMV, split-K
     gemm(128, 5120, 17408, 7050)    # GEMM, split-K
-    gemm(400, 5120, 17408, 7070)    # GEMM, 256-row tiles, 3-way split-K
+    gemm(330, 5120, 17408, 7070)    # GEMM, 128-row tiles, ragged last tile, 3-way split-K
     gemm(48, 5120, 17408, 7080)     # GEMM, 64-row tiles, 12-way split-K
     gemv(1, 4096, 8192, 7060)       # 4 K chunks: exchange, two tree levels
 
