@@ -68,8 +68,11 @@ def build() -> str:
         for lx in (1, 0):
             for sums in (0, 1):
                 obj = f"tq_proj_{fname}{'' if lx else '_sg'}{'_sums' if sums else ''}.o"
+                # kernel-argument preloading: the kernel's leading scalar
+                # arguments arrive in SGPRs (tq_proj_kernel.h)
                 units.append(("tq_proj_inst.hip", obj,
-                              [f"-DTQ_INST_FMT={fmt}", f"-DTQ_INST_LX={lx}", f"-DTQ_INST_SUMS={sums}"]))
+                              [f"-DTQ_INST_FMT={fmt}", f"-DTQ_INST_LX={lx}", f"-DTQ_INST_SUMS={sums}",
+                               "-mllvm", "-amdgpu-kernarg-preload-count=16"]))
     # the persistent decode-token kernel: one object per packed format
     for fmt, fname in ((0, "b3"), (1, "2b"), (2, "bp")):
         units.append(("tq_stack.hip", f"tq_stack_{fname}.o", [f"-DTQ_STACK_FMT={fmt}"]))

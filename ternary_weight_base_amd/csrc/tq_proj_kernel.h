@@ -546,7 +546,11 @@ struct ProjRun {
       if constexpr (PERSIST) {
         // the array was zeroed before this projection; |y| >= 0, so the
         // bits order as the values
-        if (lane == 0 && __ballot(fin) != 0)
+        // (the ballot with every lane active: inside `lane == 0 && ...` it
+        // would see lane 0's row alone and drop the maximum of a piece whose
+        // finished rows do not include row 0)
+        const bool any_fin = __ballot(fin) != 0;
+        if (lane == 0 && any_fin)
           __hip_atomic_fetch_max(reinterpret_cast<uint32_t *>(A.out_bmax) + b, __float_as_uint(m),
                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
@@ -578,25 +582,43 @@ struct ProjRun {
 // 140 VGPRs, so it is launched only for grids of at most one workgroup per
 // CU (two waves per SIMD, 256 VGPRs); bigger grids keep the SGPR form
 // within 128 VGPRs (two workgroups per CU).
+//
+// The fields the first loads need come first, as separate arguments: the
+// unit is built with kernel-argument preloading (the first 14 dwords of
+// arguments arrive in SGPRs with the wave), so the activation loads go out
+// without waiting for a load of the argument block.  ProjArgs carries the
+// rest.
 template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX, bool SUMS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LX ? 2 : 4)))
-void proj_kernel(ProjArgs A) {
+void proj_kernel(const void *in, const float *in_aux, const uint8_t *W0, const uint8_t *W1, int N, int K,
+                 int in_nb, int C, int W, int I, ProjArgs A) {
   constexpr int NPART = SPLIT ? kMaxParts : 1;
   __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
   __shared__ float red[NPART * NMAT * kNW * 64];
   __shared__ float wmax[kNW];
   __shared__ __attribute__((aligned(16))) uint32_t qs[LX ? kNW * GS * 32 : 1];
-  // The digit table depends on nothing: its LDS stores overlap the kernel
-  // argument loads and the address arithmetic of the body.
-  if constexpr (FMT == 0) fill_b3_lut<kThreads>(lut);
+  A.in = in;
+  A.in_aux = in_aux;
+  A.W0 = W0;
+  A.W1 = W1;
+  A.N = N;
+  A.K = K;
+  A.in_nb = in_nb;
+  A.split = SPLIT ? 1 : 0;  // the launcher picks SPLIT from the plan's split mode
+  A.C = C;
+  A.W = W;
+  A.I = I;
   const ProjLds sm{lut, red, wmax, qs};
   ProjRun<FMT, NMAT, IN, GS, D, SPLIT, LX, SUMS, false> r;
   r.setup(A, (int)blockIdx.x, GS);
   r.load_inputs();
+  // The digit table depends on nothing: its LDS stores overlap the
+  // activation loads just issued.
+  if constexpr (FMT == 0) fill_b3_lut<kThreads>(lut);
   // The CU returns vector loads in issue order, so activation loads issued
   // behind other waves' weight loads would wait for those weights: every
   // wave issues its activation loads before any wave of the workgroup
-  // issues weights.
+  // issues weights.  (The barrier also completes the digit table.)
   __syncthreads();
   r.issue_first();
   r.compute(sm);
@@ -609,7 +631,8 @@ int launch_in(const Plan &p, const ProjArgs &A, hipStream_t st) {
   const dim3 grid((unsigned)p.grid), block(kThreads);
 #define TQ_CASE(G_, S_)                                                                            \
   case G_:                                                                                         \
-    hipLaunchKernelGGL((proj_kernel<FMT, NMAT, IN, G_, D, S_, LX, SUMS>), grid, block, 0, st, A);  \
+    hipLaunchKernelGGL((proj_kernel<FMT, NMAT, IN, G_, D, S_, LX, SUMS>), grid, block, 0, st, A.in,    \
+                       A.in_aux, A.W0, A.W1, A.N, A.K, A.in_nb, A.C, A.W, A.I, A);                 \
     break;
   if constexpr (NMAT == 1) {
     switch (p.gs) {

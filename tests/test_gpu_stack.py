@@ -168,6 +168,36 @@ def test_persistent_matches_launches(fmt, L, hidden, inter, qkv_out, o_in):
 
 
 @pytest.mark.parametrize("fmt", [B3, TB])
+def test_persistent_repeated_calls_identical(fmt):
+    """100 calls of the persistent kernel on one input give identical outputs.
+    Regression: the block maxima of gate/up's output (read by down's
+    quantiser) once took a wave ballot with only lane 0 active, so a piece of
+    a cut block whose finished rows did not include row 0 dropped its
+    maximum -- about one call in 70 quantised h with a smaller absmax."""
+    import ternary_weight_base_amd as tq
+    say(f"persistent repeated {FMTS[fmt]}")
+    L, hidden, inter, qkv_out, o_in, seed = 2, 2048, 5120, 1024, 2048, 63
+    shapes = [(qkv_out, hidden), (hidden, o_in), (inter, hidden), (inter, hidden), (hidden, inter)]
+    devw = [[dev(tq.tq_pack(fmt, synth.trits(synth.seed(seed, l, i, 1), N, K),
+                            synth.scales(synth.seed(seed, l, i, 2), N, K)))
+             for i, (N, K) in enumerate(shapes)] for l in range(L)]
+    x = dev(synth.normal_f16(synth.seed(seed, 99, 1), L, hidden))
+    a = dev(synth.normal_f16(synth.seed(seed, 99, 2), L, o_in))
+    outs = [torch.full((L, n), float("nan"), device="cuda") for n in (qkv_out, hidden, inter, hidden)]
+    nbytes = tq.tq_decode_stack_workspace_bytes(fmt, L, hidden, inter, qkv_out, o_in)
+    ws = torch.zeros((nbytes + 15) // 16 * 4, dtype=torch.int32, device="cuda")
+    ref = None
+    for it in range(100):
+        tq.tq_decode_stack(fmt, L, hidden, inter, qkv_out, o_in, devw, x, a, *outs, ws, persistent=True)
+        cur = torch.cat([o.flatten() for o in outs]).view(torch.int32)
+        if ref is None:
+            ref = cur.clone()
+        else:
+            assert torch.equal(cur, ref), f"call {it} differs"
+    assert tq.stack_timeouts(ws) == 0
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
 def test_persistent_ffn_rotation_matches_launches(fmt):
     """With the FFN input rotated in O's epilogue (counter meet), full shapes."""
     say(f"persistent rotation {FMTS[fmt]}")
