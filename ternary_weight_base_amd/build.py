@@ -60,19 +60,23 @@ def build() -> str:
               "-c", os.path.join(CSRC, src), "-o", o])
         host_objs.append(o)
     objs, cmds = [], []
-    units = [(src, src.replace(".hip", ".o"), []) for src in
-             ("tq_kernels.hip", "tq_proj.hip", "tq_gemv_mfma.hip", "tq_hadamard.hip", "tq_gemm.hip",
-              "tq_stream.hip", "tq_noalloc.hip")]
+    # kernel-argument preloading (-mllvm -amdgpu-kernarg-preload-count=16):
+    # the leading scalar arguments of the launch-latency-bound kernels (the
+    # quantisers, the GEMVs) arrive in SGPRs with the wave
+    preload = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
+    units = [(src, src.replace(".hip", ".o"), preload if src in ("tq_kernels.hip", "tq_gemv_mfma.hip",
+                                                                   "tq_hadamard.hip") else [])
+             for src in ("tq_kernels.hip", "tq_proj.hip", "tq_gemv_mfma.hip", "tq_hadamard.hip",
+                         "tq_gemm.hip", "tq_stream.hip", "tq_noalloc.hip")]
     # the projection kernel: one object per (packed format, activation form, output kind)
     for fmt, fname in ((0, "b3"), (1, "2b"), (2, "bp")):
         for lx in (1, 0):
             for sums in (0, 1):
                 obj = f"tq_proj_{fname}{'' if lx else '_sg'}{'_sums' if sums else ''}.o"
-                # kernel-argument preloading: the kernel's leading scalar
-                # arguments arrive in SGPRs (tq_proj_kernel.h)
+                # with kernel-argument preloading (tq_proj_kernel.h)
                 units.append(("tq_proj_inst.hip", obj,
                               [f"-DTQ_INST_FMT={fmt}", f"-DTQ_INST_LX={lx}", f"-DTQ_INST_SUMS={sums}",
-                               "-mllvm", "-amdgpu-kernarg-preload-count=16"]))
+                               *preload]))
     # the persistent decode-token kernel: one object per packed format
     for fmt, fname in ((0, "b3"), (1, "2b"), (2, "bp")):
         units.append(("tq_stack.hip", f"tq_stack_{fname}.o", [f"-DTQ_STACK_FMT={fmt}"]))

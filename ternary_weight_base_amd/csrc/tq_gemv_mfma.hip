@@ -129,8 +129,19 @@ __device__ __forceinline__ void decode_half(const uint2 *lut, uint32_t laneoff, 
   }
 }
 
+// The fields the first loads need come first, as separate arguments that
+// the unit's kernel-argument preloading places in SGPRs with the wave;
+// MArgs carries the rest.
 template <int FMT, int NMAT, int GS, bool SUMS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void mgemv_kernel(MArgs A) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void mgemv_kernel(
+    const uint8_t *aW0, const uint8_t *aW1, const int8_t *aq, int aM, int aN, int aK, int aC, MArgs A) {
+  A.W0 = aW0;
+  A.W1 = aW1;
+  A.q = aq;
+  A.M = aM;
+  A.N = aN;
+  A.K = aK;
+  A.C = aC;
   constexpr int WPG = FMT == 0 ? 7 : 9;
   constexpr int D0 = GS < 2 ? GS : 2;
   // B3: the digit table; afterwards (both formats) the waves' partial sums
@@ -403,7 +414,8 @@ int launch(const MPlan &p, const MArgs &A, hipStream_t st) {
   const dim3 grid((unsigned)(p.NB * p.C)), block(kThreads);
 #define TQ_CASE(G_)                                                                   \
   case G_:                                                                            \
-    hipLaunchKernelGGL((mgemv_kernel<FMT, NMAT, G_, SUMS>), grid, block, 0, st, A);   \
+    hipLaunchKernelGGL((mgemv_kernel<FMT, NMAT, G_, SUMS>), grid, block, 0, st, A.W0, A.W1, A.q, A.M, \
+                       A.N, A.K, A.C, A);                                                          \
     break;
   switch (p.gs) {
     TQ_CASE(1) TQ_CASE(2) TQ_CASE(3) TQ_CASE(4) TQ_CASE(5) TQ_CASE(6)
