@@ -280,9 +280,10 @@ def main():
 
     # ---- layout A/B: the same stack, inputs and seeds in each packed layout
     if extras is not None:
-        names = {tq.TQ_FMT_B3: "b3", tq.TQ_FMT_2B: "2b", tq.TQ_FMT_BP: "bp"}
+        # b3r: B3's bytes in row-major group order, without the re-tiling
+        names = {tq.TQ_FMT_B3: "b3", tq.TQ_FMT_2B: "2b", tq.TQ_FMT_BP: "bp", tq.TQ_FMT_B3R: "b3r"}
         ab = {names[fmt]: {"tok_s": round(tok_s, 2), "weight_bytes_per_token": stack.step_weight_bytes}}
-        for other in (tq.TQ_FMT_B3, tq.TQ_FMT_2B, tq.TQ_FMT_BP):
+        for other in (tq.TQ_FMT_B3, tq.TQ_FMT_2B, tq.TQ_FMT_BP, tq.TQ_FMT_B3R):
             if other == fmt:
                 continue
             st2 = Stack(tq, synth, torch, other, L)

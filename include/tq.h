@@ -45,6 +45,10 @@
  * the load-time re-tiling into consumption order that the Bonsai page
  * suggests ("后面还有没有优化空间": reorder codes and scales into the order
  * the dot instruction consumes them).
+ *   B3R (the same bytes without that re-tiling, for measuring it): row n's
+ *       group g at byte (n*G + g)*28, its 26 B3 bytes then the fp16 scale;
+ *       no padding rows (N*G*28 bytes).  Only the one-token paths take it,
+ *       as BP.
  *
  * Group bytes (a permutation of the 128 trits chosen so that activations are
  * consumed as aligned 4-byte words):
@@ -62,8 +66,10 @@
  *       0 on zero trits; a sign on a zero trit is non-canonical); in both,
  *       byte 4w + b, bit s holds k = 32w + 4s + b.  2.125 bit per weight.
  *       Only the one-token paths take it (tq_gemv and
- *       tq_gemv_gate_up_swiglu with M = 1, tq_gemv_quant, tq_decode_stack);
- *       the others return TQ_ERR_FORMAT.
+ *       tq_gemv_gate_up_swiglu with M = 1, tq_gemv_quant, tq_decode_stack
+ *       (tq_decode_stack_persistent runs the latter's launches), the
+ *       group-sum hooks of these and tq_debug_unpack); the others return
+ *       TQ_ERR_FORMAT.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -87,7 +93,7 @@ typedef enum {
   TQ_ERR_HIP = -8     /* the HIP runtime refused a launch */
 } tq_status;
 
-typedef enum { TQ_FMT_B3 = 0, TQ_FMT_2B = 1, TQ_FMT_BP = 2 } tq_format;
+typedef enum { TQ_FMT_B3 = 0, TQ_FMT_2B = 1, TQ_FMT_BP = 2, TQ_FMT_B3R = 3 } tq_format;
 typedef enum { TQ_F16 = 0, TQ_F32 = 1 } tq_dtype;
 
 #define TQ_GROUP 128

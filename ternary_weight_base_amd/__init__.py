@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 TQ_FMT_B3 = 0
 TQ_FMT_2B = 1
 TQ_FMT_BP = 2
+TQ_FMT_B3R = 3  # B3 bytes in row-major group order (the layout without the re-tiling)
 TQ_F16 = 0
 TQ_F32 = 1
 TQ_STREAM_READ_WGS = 8192

@@ -69,7 +69,7 @@ def build() -> str:
              for src in ("tq_kernels.hip", "tq_proj.hip", "tq_gemv_mfma.hip", "tq_hadamard.hip",
                          "tq_gemm.hip", "tq_stream.hip", "tq_noalloc.hip")]
     # the projection kernel: one object per (packed format, activation form, output kind)
-    for fmt, fname in ((0, "b3"), (1, "2b"), (2, "bp")):
+    for fmt, fname in ((0, "b3"), (1, "2b"), (2, "bp"), (3, "b3r")):
         for lx in (1, 0):
             for sums in (0, 1):
                 obj = f"tq_proj_{fname}{'' if lx else '_sg'}{'_sums' if sums else ''}.o"

@@ -41,6 +41,13 @@ __device__ __forceinline__ uint4 ld_stream16(const uint8_t *p) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// The same 16 bytes from a 4-byte-aligned address (row-major B3R groups).
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ uint4 ld_stream16u(const uint8_t *p) {
+  const u32x4a4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4a4 *>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 __device__ __forceinline__ uint3 ld_stream12(const uint8_t *p) {
   const u32x3 t = __builtin_nontemporal_load(reinterpret_cast<const u32x3 *>(p));
   return make_uint3(t.x, t.y, t.z);

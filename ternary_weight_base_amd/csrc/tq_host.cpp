@@ -8,7 +8,8 @@
 // (pwwt.cn/news/4940051, section 1.2), each group of 128 weights carrying one
 // fp16 scale ("三值权重 27B 压到 5.9GB｜本地部署成本账单重算", section 三).
 // Groups and scales are re-tiled at pack time into the order the kernels
-// consume them (Bonsai page, section "后面还有没有优化空间").
+// consume them (Bonsai page, section "后面还有没有优化空间"); B3R keeps the
+// plain row-major group order, the layout that re-tiling is measured against.
 #include <stdint.h>
 #include <string.h>
 
@@ -37,7 +38,9 @@ static bool shape_ok(int64_t N, int64_t K) {
          K <= (int64_t)1 << 30;
 }
 
-static bool fmt_ok(int fmt) { return fmt == TQ_FMT_B3 || fmt == TQ_FMT_2B || fmt == TQ_FMT_BP; }
+static bool fmt_ok(int fmt) {
+  return fmt == TQ_FMT_B3 || fmt == TQ_FMT_2B || fmt == TQ_FMT_BP || fmt == TQ_FMT_B3R;
+}
 
 extern "C" size_t tq_packed_bytes(int fmt, int64_t N, int64_t K) {
   if (!fmt_ok(fmt) || !shape_ok(N, K)) return 0;
@@ -137,6 +140,10 @@ struct Pieces {
 };
 
 inline Pieces pieces(int fmt, const Layout &L, int64_t b, int64_t g, int64_t r) {
+  if (fmt == TQ_FMT_B3R) {
+    const int64_t a = tq::rowmajor_group(b * tq::kBlockRows + r, g, L.G);
+    return {a, a + 16, a + 26};
+  }
   int64_t gb = L.group_base(b, g), wb = L.block_rows(b);
   if (fmt == TQ_FMT_B3) return {gb + r * 16, gb + wb * 16 + r * 12, gb + wb * 16 + r * 12 + 10};
   return {gb + r * 16, gb + wb * 16 + r * 16, gb + wb * 32 + r * 2};
@@ -173,7 +180,7 @@ extern "C" int tq_pack(int fmt, int64_t N, int64_t K, const int8_t *trits,
         const int8_t *t = real ? trits + n * K + g * tq::kGroup : zero_trits;
         uint16_t s = real ? scales[n * G + g] : 0;
         Pieces p = pieces(fmt, L, b, g, r);
-        if (fmt == TQ_FMT_B3) {
+        if (fmt == TQ_FMT_B3 || fmt == TQ_FMT_B3R) {
           b3_encode(t, buf);
           memcpy(out + p.a, buf, 16);
           memcpy(out + p.b, buf + 16, 10);
@@ -209,7 +216,7 @@ extern "C" int tq_unpack(int fmt, int64_t N, int64_t K, const void *src, size_t 
       for (int64_t r = 0; r < L.block_rows(b); r++) {
         Pieces p = pieces(fmt, L, b, g, r);
         bool ok;
-        if (fmt == TQ_FMT_B3) {
+        if (fmt == TQ_FMT_B3 || fmt == TQ_FMT_B3R) {
           memcpy(buf, in + p.a, 16);
           memcpy(buf + 16, in + p.b, 10);
           ok = b3_decode(buf, t);

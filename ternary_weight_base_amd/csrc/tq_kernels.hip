@@ -187,18 +187,23 @@ __global__ __launch_bounds__(256) void quant_kernel_long(const T *__restrict__ x
 template <int FMT>
 __global__ __launch_bounds__(64) void unpack_kernel(const uint8_t *__restrict__ W,
                                                     int8_t *__restrict__ t, int N, int K) {
-  __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
+  constexpr bool B3F = FMT == 0 || FMT == 3;
+  __shared__ __attribute__((aligned(16))) uint2 lut[B3F ? kLutEntries * kLutCopies : 1];
   const Layout L(FMT, N, K);
   const int b = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
-  if (FMT == 0) fill_b3_lut<64>(lut);
+  if (B3F) fill_b3_lut<64>(lut);
   __syncthreads();
   const int Wb = (int)L.block_rows(b), rows = (int)L.valid_rows(b);
   if (lane >= rows) return;
   const uint8_t *gb = W + L.group_base(b, g);
   int8_t *tr = t + ((size_t)b * tq::kBlockRows + lane) * K + (size_t)g * tq::kGroup;
-  if (FMT == 0) {
-    const uint4 A = *reinterpret_cast<const uint4 *>(gb + lane * 16);
-    const uint32_t *pb = reinterpret_cast<const uint32_t *>(gb + Wb * 16 + lane * 12);
+  if (B3F) {
+    // B3: the group's pieces of row `lane`; B3R: the row's 28 bytes
+    const uint8_t *ra = FMT == 3 ? W + tq::rowmajor_group((int64_t)b * tq::kBlockRows + lane, g, L.G)
+                                 : gb + lane * 16;
+    const uint32_t *ra4 = reinterpret_cast<const uint32_t *>(ra);
+    const uint4 A = make_uint4(ra4[0], ra4[1], ra4[2], ra4[3]);
+    const uint32_t *pb = reinterpret_cast<const uint32_t *>(FMT == 3 ? ra + 16 : gb + Wb * 16 + lane * 12);
     const uint32_t w[7] = {A.x, A.y, A.z, A.w, pb[0], pb[1], pb[2]};
     const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
     uint2 e[26];
@@ -244,6 +249,11 @@ __global__ __launch_bounds__(64) void unpack_kernel(const uint8_t *__restrict__ 
 // Host side: argument checks and launch plans.
 // ---------------------------------------------------------------------
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+// Formats of the one-token paths; BP and B3R run there only (M = 1).
+bool one_token_fmt(int fmt) {
+  return fmt == TQ_FMT_B3 || fmt == TQ_FMT_2B || fmt == TQ_FMT_BP || fmt == TQ_FMT_B3R;
+}
+bool multi_token_fmt(int fmt) { return fmt == TQ_FMT_B3 || fmt == TQ_FMT_2B; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 bool shape_ok(int64_t N, int64_t K) {
@@ -276,10 +286,10 @@ int gemv_common(int fmt, int64_t M, int64_t N, int64_t K, const void *W0, const 
                 const int8_t *q, const float *a, float *out, int32_t *sums, void *ws,
                 size_t ws_bytes, void *stream, int nmat) {
   if (!W0 || !q || (!sums && (!a || !out)) || (nmat == 2 && !W1)) return TQ_ERR_NULL;
-  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B && fmt != TQ_FMT_BP) return TQ_ERR_FORMAT;
+  if (!one_token_fmt(fmt)) return TQ_ERR_FORMAT;
   if (!shape_ok(N, K) || M < 1 || M > TQ_GEMV_MAX_M) return TQ_ERR_SHAPE;
-  // BP runs on the one-token projection kernel only
-  if (fmt == TQ_FMT_BP && M != 1) return TQ_ERR_FORMAT;
+  // BP and B3R run on the one-token projection kernel only
+  if (!multi_token_fmt(fmt) && M != 1) return TQ_ERR_FORMAT;
   if (!aligned16(W0) || (W1 && !aligned16(W1)) || !aligned16(q) || (a && !aligned4(a)) ||
       (out && !aligned4(out)) || (sums && !aligned4(sums)))
     return TQ_ERR_ALIGN;
@@ -319,8 +329,8 @@ extern "C" int tq_quant_act(int dtype, int64_t M, int64_t K, const void *x, int8
 }
 
 extern "C" size_t tq_gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
-  if ((fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B && fmt != TQ_FMT_BP) || !shape_ok(N, K) || M < 1 ||
-      M > TQ_GEMV_MAX_M || (fmt == TQ_FMT_BP && M != 1))
+  if ((!one_token_fmt(fmt)) || !shape_ok(N, K) || M < 1 ||
+      M > TQ_GEMV_MAX_M || (!multi_token_fmt(fmt) && M != 1))
     return 0;
   // covers both tq_gemv and the fused gate/up call (two partial planes)
   if (M == 1) {
@@ -364,7 +374,7 @@ extern "C" int tq_gemm(int fmt, int64_t M, int64_t N, int64_t K, const void *W, 
 extern "C" int tq_debug_unpack(int fmt, int64_t N, int64_t K, const void *W, int8_t *trits,
                                void *stream) {
   if (!W || !trits) return TQ_ERR_NULL;
-  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B && fmt != TQ_FMT_BP) return TQ_ERR_FORMAT;
+  if (!one_token_fmt(fmt)) return TQ_ERR_FORMAT;
   if (!shape_ok(N, K)) return TQ_ERR_SHAPE;
   if (!aligned16(W) || !aligned4(trits)) return TQ_ERR_ALIGN;
   const Layout L(fmt, N, K);
@@ -375,6 +385,8 @@ extern "C" int tq_debug_unpack(int fmt, int64_t N, int64_t K, const void *W, int
     hipLaunchKernelGGL((unpack_kernel<0>), grid, dim3(64), 0, st, Wp, trits, (int)N, (int)K);
   else if (fmt == TQ_FMT_2B)
     hipLaunchKernelGGL((unpack_kernel<1>), grid, dim3(64), 0, st, Wp, trits, (int)N, (int)K);
+  else if (fmt == TQ_FMT_B3R)
+    hipLaunchKernelGGL((unpack_kernel<3>), grid, dim3(64), 0, st, Wp, trits, (int)N, (int)K);
   else
     hipLaunchKernelGGL((unpack_kernel<2>), grid, dim3(64), 0, st, Wp, trits, (int)N, (int)K);
   return check_stream_launch();
@@ -383,11 +395,11 @@ extern "C" int tq_debug_unpack(int fmt, int64_t N, int64_t K, const void *W, int
 extern "C" int tq_debug_group_sums(int fmt, int64_t M, int64_t N, int64_t K, const void *W,
                                    const int8_t *q, int32_t *S, int use_gemm_path, void *stream) {
   if (!W || !q || !S) return TQ_ERR_NULL;
-  if (fmt != TQ_FMT_B3 && fmt != TQ_FMT_2B && fmt != TQ_FMT_BP) return TQ_ERR_FORMAT;
+  if (!one_token_fmt(fmt)) return TQ_ERR_FORMAT;
   if (!shape_ok(N, K) || M < 1) return TQ_ERR_SHAPE;
   if (!aligned16(W) || !aligned16(q) || !aligned4(S)) return TQ_ERR_ALIGN;
   if (use_gemm_path) {
-    if (fmt == TQ_FMT_BP) return TQ_ERR_FORMAT;
+    if (!multi_token_fmt(fmt)) return TQ_ERR_FORMAT;
     if (M > ((int64_t)1 << 24)) return TQ_ERR_SHAPE;
     return gemm_launch(fmt, M, N, K, W, q, nullptr, nullptr, S, (hipStream_t)stream);
   }

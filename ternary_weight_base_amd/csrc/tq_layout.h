@@ -14,11 +14,16 @@ namespace tq {
 constexpr int kGroup = 128;
 constexpr int kBlockRows = 64;
 
+// Formats: 0 B3, 1 2B, 2 BP (block-interleaved, the kernels' consumption
+// order); 3 B3R, the B3 group bytes in row-major group order.
 // Bytes per (row, group): trits plus the fp16 scale.
-TQ_HD int group_bytes(int fmt) { return fmt == 0 ? 28 : 34; }
+TQ_HD int group_bytes(int fmt) { return fmt == 0 || fmt == 3 ? 28 : 34; }
 // The last block's rows are padded to this multiple so that every 16-byte
-// piece stays 16-byte aligned.
-TQ_HD int tail_align(int fmt) { return fmt == 0 ? 4 : 8; }
+// piece stays 16-byte aligned (B3R: no padding, rows are not interleaved).
+TQ_HD int tail_align(int fmt) { return fmt == 3 ? 1 : fmt == 0 ? 4 : 8; }
+// B3R: row n's group g at byte (n G + g) 28 -- the 26 B3 bytes, then the
+// fp16 scale.
+TQ_HD int64_t rowmajor_group(int64_t n, int64_t g, int64_t G) { return (n * G + g) * 28; }
 
 struct Layout {
   int64_t N, K, G, NB;

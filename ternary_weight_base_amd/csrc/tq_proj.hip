@@ -145,6 +145,7 @@ int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, i
             : launch_lx<F_, false, false>(p, A, nmat, in_kind, st);
   if (fmt == TQ_FMT_B3) { TQ_LAUNCH(0) }
   if (fmt == TQ_FMT_2B) { TQ_LAUNCH(1) }
+  if (fmt == TQ_FMT_B3R) { TQ_LAUNCH(3) }
   TQ_LAUNCH(2)
 #undef TQ_LAUNCH
 }
@@ -158,7 +159,9 @@ size_t proj_ws_bytes(int fmt, int64_t N, int64_t K, int nmat) { return proj_ws(f
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // The one-token projection takes all three packed formats.
-bool fmt_ok(int fmt) { return fmt == TQ_FMT_B3 || fmt == TQ_FMT_2B || fmt == TQ_FMT_BP; }
+bool fmt_ok(int fmt) {
+  return fmt == TQ_FMT_B3 || fmt == TQ_FMT_2B || fmt == TQ_FMT_BP || fmt == TQ_FMT_B3R;
+}
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 bool shape_ok(int64_t N, int64_t K) {
   return N >= 1 && K >= tq::kGroup && K % tq::kGroup == 0 && N <= ((int64_t)1 << 24) &&
@@ -354,6 +357,10 @@ extern "C" int tq_decode_stack_persistent(int fmt, int64_t layers, int64_t hidde
                        y_out, ws, ws_bytes);
   if (rc != TQ_OK) return rc;
   if (ffn_signs && hidden % 64 != 0) return TQ_ERR_SHAPE;
+  // the persistent kernel is built for the block-interleaved formats
+  if (fmt == TQ_FMT_B3R)
+    return tq_decode_stack(fmt, layers, hidden, inter, qkv_out, o_in, weights, x_in, a_in, y_qkv, y_o, h,
+                           y_out, ffn_signs, ws, ws_bytes, stream);
   const int nwg = stack_grid(fmt);
   if (nwg < 1) return TQ_ERR_HIP;
   const StackWs w = stack_ws(fmt, hidden, inter, qkv_out, o_in);

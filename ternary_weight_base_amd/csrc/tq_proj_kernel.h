@@ -150,7 +150,8 @@ __device__ __forceinline__ void st_dev_f32(float *p, float v) {
 // maxima go through an atomic maximum on a zeroed array.
 template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX, bool SUMS, bool PERSIST>
 struct ProjRun {
-  static constexpr int WPG = FMT == 0 ? 7 : 9;   // words per (row, group) in registers
+  static constexpr bool B3F = FMT == 0 || FMT == 3;  // base-3 bytes (block-interleaved or row-major)
+  static constexpr int WPG = B3F ? 7 : 9;        // words per (row, group) in registers
   static constexpr int NP = (GS + 1) / 2;        // group pairs: one activation word per lane each
   static constexpr int D0 = D < GS ? D : GS;
   static constexpr int NPART = SPLIT ? kMaxParts : 1;  // blocks a range can touch
@@ -224,6 +225,20 @@ struct ProjRun {
     const uint8_t *Wm[2] = {A.W0, A.W1};
 #pragma unroll
     for (int mat = 0; mat < NMAT; mat++) {
+      if constexpr (FMT == 3) {
+        // row-major groups: each lane reads its own row's 28 bytes
+        const uint8_t *rp = Wm[mat] + tq::rowmajor_group((int64_t)bi * tq::kBlockRows + lr, gi, G);
+        const uint4 P = ld_stream16u(rp);
+        const uint3 B = ld_stream12(rp + 16);
+        wd[mat][i][0] = P.x;
+        wd[mat][i][1] = P.y;
+        wd[mat][i][2] = P.z;
+        wd[mat][i][3] = P.w;
+        wd[mat][i][4] = B.x;
+        wd[mat][i][5] = B.y;
+        wd[mat][i][6] = B.z;
+        continue;
+      }
       const uint8_t *gp = Wm[mat] + L.group_base(bi, gi);
       const uint4 P = ld_stream16(gp + lr * 16);
       wd[mat][i][0] = P.x;
@@ -411,7 +426,7 @@ struct ProjRun {
         for (int k = 0; k < WPG; k++) asm volatile("" : "+v"(wd[mat][i][k]));  // this matrix starts here
         int S[1] = {0};
         float sc;
-        if constexpr (FMT == 0) {
+        if constexpr (B3F) {
           const uint32_t w[7] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2], wd[mat][i][3],
                                  wd[mat][i][4], wd[mat][i][5], wd[mat][i][6]};
           if constexpr (LX) S[0] = b3_group_v(lut, laneoff, w, xa.v[0]);
@@ -593,7 +608,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LX ? 2
 void proj_kernel(const void *in, const float *in_aux, const uint8_t *W0, const uint8_t *W1, int N, int K,
                  int in_nb, int C, int W, int I, ProjArgs A) {
   constexpr int NPART = SPLIT ? kMaxParts : 1;
-  __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 ? kLutEntries * kLutCopies : 1];
+  __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 || FMT == 3 ? kLutEntries * kLutCopies : 1];
   __shared__ float red[NPART * NMAT * kNW * 64];
   __shared__ float wmax[kNW];
   __shared__ __attribute__((aligned(16))) uint32_t qs[LX ? kNW * GS * 32 : 1];
@@ -614,7 +629,7 @@ void proj_kernel(const void *in, const float *in_aux, const uint8_t *W0, const u
   r.load_inputs();
   // The digit table depends on nothing: its LDS stores overlap the
   // activation loads just issued.
-  if constexpr (FMT == 0) fill_b3_lut<kThreads>(lut);
+  if constexpr (FMT == 0 || FMT == 3) fill_b3_lut<kThreads>(lut);
   // The CU returns vector loads in issue order, so activation loads issued
   // behind other waves' weight loads would wait for those weights: every
   // wave issues its activation loads before any wave of the workgroup

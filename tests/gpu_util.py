@@ -6,8 +6,9 @@ import numpy as np
 
 import synth
 
-B3, TB, BP = 0, 1, 2
-FMTS = {B3: "b3", TB: "2b", BP: "bp"}
+B3, TB, BP, B3R = 0, 1, 2, 3
+FMTS = {B3: "b3", TB: "2b", BP: "bp", B3R: "b3r"}
+ONE_TOKEN_ONLY = (BP, B3R)  # formats the one-token paths alone take
 
 
 def say(*a):

@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import B3, BP, TB, FMTS, acts_f16, dev, say, weights
+from gpu_util import B3, B3R, BP, ONE_TOKEN_ONLY, TB, FMTS, acts_f16, dev, say, weights
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -63,8 +63,8 @@ def _sums(M, N, K, nmat=1):
 # blocks, more workgroups than CUs -> the SGPR activation form), plus ragged
 # shapes with a partial last block.
 SHAPES = [(10240, 5120), (5120, 8192), (5120, 17408), (17408, 5120), (100, 640), (65, 384)]
-# (format, tokens): BP runs on the one-token kernel only
-FMT_M = [(f, m) for f in (B3, TB, BP) for m in (1, 2, 4, 8, 16) if f != BP or m == 1]
+# (format, tokens): BP and B3R run on the one-token kernel only
+FMT_M = [(f, m) for f in (B3, TB, BP, B3R) for m in (1, 2, 4, 8, 16) if f not in ONE_TOKEN_ONLY or m == 1]
 
 
 @pytest.mark.parametrize("fmt,M", FMT_M)
@@ -110,7 +110,7 @@ STACK_LAUNCHES = [(10240, 5120, "f16", False), (5120, 8192, "f16", False),
                   (17408, 5120, "f32", True), (5120, 17408, "f32", False), (1152, 640, "f32", True)]
 
 
-@pytest.mark.parametrize("fmt", [B3, TB, BP])
+@pytest.mark.parametrize("fmt", [B3, TB, BP, B3R])
 @pytest.mark.parametrize("N,K,dtype,gate_up", STACK_LAUNCHES)
 def test_gemv_quant_group_sums(fmt, N, K, dtype, gate_up):
     """The quantiser fused into the stack's projection launches: the int8
@@ -210,7 +210,8 @@ def _edge_acts(M, K, seed):
     return q
 
 
-@pytest.mark.parametrize("fmt,M", [(f, m) for f in (B3, TB, BP) for m in (1, 3, 16) if f != BP or m == 1])
+@pytest.mark.parametrize("fmt,M", [(f, m) for f in (B3, TB, BP, B3R) for m in (1, 3, 16)
+                                   if f not in ONE_TOKEN_ONLY or m == 1])
 @pytest.mark.parametrize("N,K", [(200, 1024), (5120, 8192)])
 def test_edge_values_gemv(fmt, M, N, K):
     """Extreme sums and special scales through tq_gemv: the int32 sums are
@@ -253,7 +254,7 @@ def test_edge_values_gemm(fmt, M):
     assert_close(y.cpu().numpy(), oracle.gemv(t, s, q, a), "edge gemm")
 
 
-@pytest.mark.parametrize("fmt", [B3, TB, BP])
+@pytest.mark.parametrize("fmt", [B3, TB, BP, B3R])
 def test_edge_values_gate_up(fmt):
     from gpu_util import assert_close
     N, K = 17408, 5120

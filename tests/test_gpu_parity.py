@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import B3, BP, TB, FMTS, acts_f16, assert_close, dev, say, upload_blob, weights
+from gpu_util import B3, B3R, BP, TB, FMTS, ONE_TOKEN_ONLY, acts_f16, assert_close, dev, say, upload_blob, weights
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +71,7 @@ def test_quant_special_rows():
 
 # --------------------------------------------------------------- decoder ---
 
-@pytest.mark.parametrize("fmt", [B3, TB, BP])
+@pytest.mark.parametrize("fmt", [B3, TB, BP, B3R])
 @pytest.mark.parametrize("N,K", [(1, 128), (64, 1024), (65, 384), (100, 640), (1024, 1024), (300, 5120)])
 def test_debug_unpack_bitexact(fmt, N, K):
     say(f"unpack {FMTS[fmt]} N={N} K={K}")
@@ -155,24 +155,26 @@ def test_gemv_vs_oracle(fmt, M, N, K):
         assert not ws.any().item()
 
 
+@pytest.mark.parametrize("fmt", ONE_TOKEN_ONLY)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 65, 384), (1, 1024, 1024), (1, 10240, 5120),
                                    (1, 5120, 8192), (1, 5120, 17408)])
-def test_gemv_bp_one_token(M, N, K):
-    """The bit-plane layout on the one-token projection kernel."""
-    say(f"gemv bp N={N} K={K}")
-    BP = _tq().TQ_FMT_BP
+def test_gemv_one_token_layouts(fmt, M, N, K):
+    """The bit-plane layout (BP) and the row-major B3 groups (B3R) on the
+    one-token projection kernel."""
+    say(f"gemv {FMTS[fmt]} N={N} K={K}")
     t, s = weights(N, K, 4300 + N + K)
     q, a = _quant_gpu(acts_f16(M, K, 4400 + K))
-    W = upload_blob(BP, t, s)
-    y, _ = _gemv_gpu(BP, M, N, K, W, q, a)
-    assert_close(y, oracle.gemv(t, s, q.cpu().numpy(), a.cpu().numpy()), f"gemv bp {N}x{K}")
+    W = upload_blob(fmt, t, s)
+    y, _ = _gemv_gpu(fmt, M, N, K, W, q, a)
+    assert_close(y, oracle.gemv(t, s, q.cpu().numpy(), a.cpu().numpy()), f"gemv {FMTS[fmt]} {N}x{K}")
 
 
+@pytest.mark.parametrize("fmt", ONE_TOKEN_ONLY)
 @pytest.mark.parametrize("N,K", [(17408, 5120), (130, 640)])
-def test_gate_up_swiglu_bp_one_token(N, K):
-    say(f"swiglu bp N={N} K={K}")
+def test_gate_up_swiglu_one_token_layouts(fmt, N, K):
+    say(f"swiglu {FMTS[fmt]} N={N} K={K}")
     tq = _tq()
-    BP = tq.TQ_FMT_BP
+    BP = fmt
     tg, sg = weights(N, K, 4500 + N)
     tu, su = weights(N, K, 4501 + N)
     q, a = _quant_gpu(acts_f16(1, K, 4600))
@@ -182,7 +184,7 @@ def test_gate_up_swiglu_bp_one_token(N, K):
                               tq.workspace(BP, 1, N, K))
     torch.cuda.synchronize()
     ref = oracle.swiglu(oracle.gemv(tg, sg, qn, an), oracle.gemv(tu, su, qn, an))
-    assert_close(h.cpu().numpy(), ref, "swiglu bp")
+    assert_close(h.cpu().numpy(), ref, f"swiglu {FMTS[fmt]}")
 
 
 def test_gemv_zero_weights_and_zero_activations():
@@ -316,7 +318,7 @@ def test_gemm_prefill_full_size(fmt, N, K):
 
 # ------------------------------------------- ternariser -> pack -> GPU -----
 
-@pytest.mark.parametrize("fmt", [B3, TB, BP])
+@pytest.mark.parametrize("fmt", [B3, TB, BP, B3R])
 def test_ternarize_pack_gpu_end_to_end(fmt):
     """fp32 weights -> tq_ternarize (host) -> tq_pack -> GPU projections,
     against oracle.ternarize -> oracle.gemv: trits and scales bit-identical,
@@ -332,7 +334,7 @@ def test_ternarize_pack_gpu_end_to_end(fmt):
     tr, sr = oracle.ternarize(w)
     assert np.array_equal(t, tr) and np.array_equal(s, sr)
     W = upload_blob(fmt, t, s)
-    Ms = (1,) if fmt == tq.TQ_FMT_BP else (1, 4, 64)
+    Ms = (1,) if fmt in ONE_TOKEN_ONLY else (1, 4, 64)
     for M in Ms:
         q, a = _quant_gpu(acts_f16(M, K, 8200 + M))
         qn, an = q.cpu().numpy(), a.cpu().numpy()

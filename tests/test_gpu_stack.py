@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import B3, BP, TB, FMTS, assert_close, dev, say
+from gpu_util import B3, B3R, BP, TB, FMTS, assert_close, dev, say
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -80,7 +80,7 @@ def _check_layers(host, x, a, outs, what):
         assert_close(y_out[l:l + 1], oracle.gemv(*hw["down"], q, s), f"{what} down[{l}]")
 
 
-@pytest.mark.parametrize("fmt", [B3, TB, BP])
+@pytest.mark.parametrize("fmt", [B3, TB, BP, B3R])
 @pytest.mark.parametrize("L,hidden,inter,qkv_out,o_in", [(3, 640, 1152, 1280, 1024),
                                                           (2, 384, 2176, 1600, 768)])
 def test_decode_stack_small(fmt, L, hidden, inter, qkv_out, o_in):
@@ -89,7 +89,7 @@ def test_decode_stack_small(fmt, L, hidden, inter, qkv_out, o_in):
     _check_layers(host, x, a, outs, FMTS[fmt])
 
 
-@pytest.mark.parametrize("fmt", [B3, TB, BP])
+@pytest.mark.parametrize("fmt", [B3, TB, BP, B3R])
 def test_decode_stack_full_shapes_two_layers(fmt):
     """The 27B-shaped layer (hidden 5120, intermediate 17408, QKV 10240, O 8192),
     two layers."""

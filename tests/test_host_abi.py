@@ -13,7 +13,7 @@ import synth
 import ternary_weight_base_amd as tq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-B3, TB, BP = tq.TQ_FMT_B3, tq.TQ_FMT_2B, tq.TQ_FMT_BP
+B3, TB, BP, B3R = tq.TQ_FMT_B3, tq.TQ_FMT_2B, tq.TQ_FMT_BP, tq.TQ_FMT_B3R
 
 
 def _header_functions():
@@ -41,13 +41,13 @@ def _rand(N, K, seed):
     return synth.trits(synth.seed(seed, 1), N, K), synth.scales(synth.seed(seed, 2), N, K)
 
 
-@pytest.mark.parametrize("fmt", [B3, TB, BP])
+@pytest.mark.parametrize("fmt", [B3, TB, BP, B3R])
 @pytest.mark.parametrize("N,K", [(1, 128), (3, 256), (64, 1024), (65, 384), (130, 640), (200, 128)])
 def test_pack_roundtrip_and_size(fmt, N, K):
     t, s = _rand(N, K, N * 7 + K)
     blob = tq.tq_pack(fmt, t, s)
-    P = 28 if fmt == B3 else 34
-    align = 4 if fmt == B3 else 8
+    P = 28 if fmt in (B3, B3R) else 34
+    align = {B3: 4, B3R: 1}.get(fmt, 8)
     nb = (N + 63) // 64
     w = N - 64 * (nb - 1)
     rows = 64 * (nb - 1) + (w + align - 1) // align * align
@@ -59,6 +59,9 @@ def test_pack_roundtrip_and_size(fmt, N, K):
 def _device_group_bytes(fmt, blob, N, K, n, g):
     """The (row n, group g) bytes and scale, located as include/tq.h describes."""
     G = K // 128
+    if fmt == B3R:  # row-major: row n's group g at (n G + g) 28, 26 bytes then the scale
+        a = (n * G + g) * 28
+        return blob[a: a + 26], int(blob[a + 26]) | (int(blob[a + 27]) << 8)
     P = 28 if fmt == B3 else 34
     align = 4 if fmt == B3 else 8
     nb = (N + 63) // 64
@@ -117,7 +120,7 @@ def _decode_2b_doc(body):
     return t
 
 
-@pytest.mark.parametrize("fmt", [B3, TB, BP])
+@pytest.mark.parametrize("fmt", [B3, TB, BP, B3R])
 def test_pack_matches_documented_layout(fmt):
     N, K = 70, 384
     t, s = _rand(N, K, 5 + fmt)
@@ -125,7 +128,7 @@ def test_pack_matches_documented_layout(fmt):
     for n in (0, 1, 63, 64, 69):
         for g in range(K // 128):
             body, sc = _device_group_bytes(fmt, blob, N, K, n, g)
-            dec = {B3: _decode_b3_doc, TB: _decode_2b_doc, BP: _decode_bp_doc}[fmt](body)
+            dec = {B3: _decode_b3_doc, TB: _decode_2b_doc, BP: _decode_bp_doc, B3R: _decode_b3_doc}[fmt](body)
             assert np.array_equal(dec, t[n, 128 * g: 128 * g + 128]), (n, g)
             assert sc == s[n, g]
 
@@ -137,6 +140,15 @@ def test_pack_same_information_as_oracle_canonical():
         rc, t1, s1 = oracle.unpack(fmt, oracle.pack(fmt, t, s), N, K)
         t2, s2 = tq.tq_unpack(fmt, tq.tq_pack(fmt, t, s), N, K)
         assert rc == 0 and np.array_equal(t1, t2) and np.array_equal(s1, s2)
+    # B3R holds exactly B3's group bytes and scales, in row-major group order
+    b3, b3r = tq.tq_pack(B3, t, s), tq.tq_pack(B3R, t, s)
+    for n in range(N):
+        for g in range(K // 128):
+            u, su = _device_group_bytes(B3, b3, N, K, n, g)
+            v, sv = _device_group_bytes(B3R, b3r, N, K, n, g)
+            assert np.array_equal(u, v) and su == sv
+    t3, s3 = tq.tq_unpack(B3R, b3r, N, K)
+    assert np.array_equal(t3, t) and np.array_equal(s3, s)
 
 
 def test_b3_closed_form_device_bytes():
@@ -191,6 +203,19 @@ def test_unpack_rejects_noncanonical():
     with pytest.raises(tq.TQError) as e:
         tq.tq_unpack(B3, bad, N, K)
     assert e.value.status == -4
+    # B3R: a byte >= 243 (row 1, group 1, byte 3) and a bad padding digit in byte 25
+    blobr = tq.tq_pack(B3R, t, s)
+    bad = blobr.copy()
+    bad[(1 * (K // 128) + 1) * 28 + 3] = 250
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_unpack(B3R, bad, N, K)
+    assert e.value.status == -5
+    bad = blobr.copy()
+    assert bad[25] % 3 == 1
+    bad[25] -= 1
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_unpack(B3R, bad, N, K)
+    assert e.value.status == -5
 
 
 def test_pack_rejects_bad_arguments():
@@ -234,7 +259,7 @@ def test_device_entry_points_validate_on_host():
     assert L.tq_gemv(B3, 0, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
     assert L.tq_gemv(B3, 17, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
     assert L.tq_gemv(B3, 1, 64, 130, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2
-    assert L.tq_gemv(3, 1, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
+    assert L.tq_gemv(4, 1, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
     assert L.tq_gemv(B3, 1, 64, 128, None, FAKE, FAKE, FAKE, None, 0, None) == -1
     assert L.tq_gemv(B3, 1, 64, 128, FAKE, MIS, FAKE, FAKE, None, 0, None) == -3
     # a shape that splits K across workgroups needs a workspace of the stated size
@@ -246,13 +271,18 @@ def test_device_entry_points_validate_on_host():
                                     need - 1, None) == -7
     assert L.tq_gemv(B3, 1, 5120, 17408, FAKE, FAKE, FAKE, FAKE, MIS, need, None) == -3
     assert L.tq_gemv_gate_up_swiglu(B3, 1, 64, 128, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == -1
-    # BP runs on the one-token kernel only
+    # BP and B3R run on the one-token kernel only
+    for f in (BP, B3R):
+        assert L.tq_gemv(f, 2, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
+        assert L.tq_gemm(f, 512, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
+        assert L.tq_debug_group_sums(f, 1, 64, 128, FAKE, FAKE, FAKE, 1, None) == -5
+    assert L.tq_debug_unpack(4, 64, 128, FAKE, FAKE, None) == -5
     assert L.tq_gemv(BP, 2, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
     assert L.tq_gemm(BP, 512, 64, 128, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -5
     assert L.tq_debug_group_sums(BP, 2, 64, 128, FAKE, FAKE, FAKE, 0, None) == -5
     assert L.tq_debug_group_sums(BP, 1, 64, 128, FAKE, FAKE, FAKE, 1, None) == -5
     assert L.tq_debug_gate_up_sums(BP, 2, 64, 128, FAKE, FAKE, FAKE, FAKE, None) == -5
-    assert L.tq_debug_unpack(3, 64, 128, FAKE, FAKE, None) == -5
+    assert L.tq_debug_unpack(5, 64, 128, FAKE, FAKE, None) == -5
     assert tq.tq_gemv_workspace_bytes(BP, 2, 5120, 8192) == 0
     assert tq.tq_gemv_workspace_bytes(BP, 1, 5120, 8192) > 0
     # gemm
