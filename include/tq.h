@@ -99,6 +99,7 @@ typedef enum { TQ_F16 = 0, TQ_F32 = 1 } tq_dtype;
 #define TQ_GROUP 128
 #define TQ_BLOCK_ROWS 64
 #define TQ_GEMV_MAX_M 16
+#define TQ_STACK_MAX_ROWS 4 /* token rows of tq_decode_stack_batch */
 #define TQ_STREAM_READ_WGS 8192 /* workgroups (and sink words) of tq_debug_stream_read */
 
 /* Human-readable name of a status code (static string). */
@@ -323,6 +324,35 @@ int tq_decode_stack_persistent(int fmt, int64_t layers, int64_t hidden, int64_t 
                                const void *x_in, const void *a_in, float *y_qkv, float *y_o,
                                float *h, float *y_out, const int8_t *ffn_signs, void *ws,
                                size_t ws_bytes, void *stream);
+
+/* Workspace bytes of tq_decode_stack_batch for `rows` token rows (same
+ * zero-fill rule); 0 on a bad format, row count or shape. */
+size_t tq_decode_stack_batch_workspace_bytes(int fmt, int64_t rows, int64_t layers, int64_t hidden,
+                                             int64_t inter, int64_t qkv_out, int64_t o_in);
+
+/* tq_decode_stack for `rows` (1..TQ_STACK_MAX_ROWS) independent token rows at once: the
+ * small-batch decode step of a server running a few sequences together
+ * ("Ternary Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section "Decode 为什么
+ * 只能算一般": decode streams every weight once per step, so tokens that
+ * share a step share that stream).  Layer l, row r:
+ *   y_qkv[l][r] = QKV . quant(x_in[l][r]),  y_o[l][r] = O . quant(a_in[l][r]),
+ *   h[l][r] = silu(gate . quant(y_o[l][r])) * (up . quant(y_o[l][r])),
+ *   y_out[l][r] = down . quant(h[l][r]),
+ * each quant per row (tq_quant_act's).  Layouts: x_in fp16
+ * [layers][rows][hidden], a_in fp16 [layers][rows][o_in], y_qkv fp32
+ * [layers][rows][qkv_out], y_o and y_out [layers][rows][hidden], h
+ * [layers][rows][inter]; alignment, ffn_signs (shared by the rows) and the
+ * workspace rule as tq_decode_stack.  Each projection is one launch over
+ * all rows: a weight group is loaded and decoded once and dotted with every
+ * row's int8 activations, so the weight stream is paid once per step.
+ * Every output row is bit-identical to tq_decode_stack on that row alone.
+ * Formats B3 and 2B (else TQ_ERR_FORMAT); rows outside
+ * 1..TQ_STACK_MAX_ROWS give TQ_ERR_SHAPE. */
+int tq_decode_stack_batch(int fmt, int64_t rows, int64_t layers, int64_t hidden, int64_t inter,
+                          int64_t qkv_out, int64_t o_in, const tq_layer *weights /* host [layers] */,
+                          const void *x_in, const void *a_in, float *y_qkv, float *y_o, float *h,
+                          float *y_out, const int8_t *ffn_signs, void *ws, size_t ws_bytes,
+                          void *stream);
 
 /* ---- device: prefill GEMM --------------------------------------------- */
 

@@ -26,6 +26,7 @@ TQ_F32 = 1
 TQ_STREAM_READ_WGS = 8192
 GROUP = 128
 GEMV_MAX_M = 16
+STACK_MAX_ROWS = 4
 
 _STATUS = {0: "TQ_OK", -1: "TQ_ERR_NULL", -2: "TQ_ERR_SHAPE", -3: "TQ_ERR_ALIGN",
            -4: "TQ_ERR_VALUE", -5: "TQ_ERR_FORMAT", -6: "TQ_ERR_DTYPE", -7: "TQ_ERR_SIZE",
@@ -38,7 +39,8 @@ EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant
            "tq_decode_stack_workspace_bytes", "tq_decode_stack", "tq_hadamard_quant_act",
            "tq_ternarize", "tq_debug_stream_read", "tq_debug_gate_up_sums",
            "tq_debug_gemv_quant_sums", "tq_decode_stack_persistent",
-           "tq_gemv_noalloc", "tq_noalloc_scratch_bytes")
+           "tq_gemv_noalloc", "tq_noalloc_scratch_bytes",
+           "tq_decode_stack_batch_workspace_bytes", "tq_decode_stack_batch")
 
 
 class TqLayer(ctypes.Structure):
@@ -76,6 +78,8 @@ def _load():
         "tq_decode_stack_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "tq_decode_stack": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
         "tq_decode_stack_persistent": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
+        "tq_decode_stack_batch_workspace_bytes": ([I, I64, I64, I64, I64, I64, I64], SZ),
+        "tq_decode_stack_batch": ([I, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
         "tq_gemv_noalloc": ([I, I64, I64, I64, P, P, P, P, P], I),
         "tq_noalloc_scratch_bytes": ([], SZ),
         "tq_hadamard_quant_act": ([I, I64, I64, P, P, P, P, P], I),
@@ -284,6 +288,22 @@ def tq_decode_stack(fmt, layers, hidden, inter, qkv_out, o_in, weights, x_in, a_
     _check(fn(fmt, layers, hidden, inter, qkv_out, o_in, ctypes.cast(arr, ctypes.c_void_p),
               _ptr(x_in), _ptr(a_in), _ptr(y_qkv), _ptr(y_o), _ptr(h), _ptr(y_out), _ptr(ffn_signs),
               wp, wb, _stream(stream)), "tq_decode_stack_persistent" if persistent else "tq_decode_stack")
+
+
+def tq_decode_stack_batch_workspace_bytes(fmt, rows, layers, hidden, inter, qkv_out, o_in) -> int:
+    return int(lib.tq_decode_stack_batch_workspace_bytes(fmt, rows, layers, hidden, inter, qkv_out, o_in))
+
+
+def tq_decode_stack_batch(fmt, rows, layers, hidden, inter, qkv_out, o_in, weights, x_in, a_in,
+                          y_qkv, y_o, h, y_out, ws, stream=None, ffn_signs=None) -> None:
+    """tq_decode_stack for `rows` token rows per launch: x_in [layers][rows][hidden],
+    a_in [layers][rows][o_in], outputs [layers][rows][N]."""
+    arr = weights if isinstance(weights, ctypes.Array) else stack_layers(weights)
+    wp, wb = _ws(ws)
+    _check(lib.tq_decode_stack_batch(fmt, rows, layers, hidden, inter, qkv_out, o_in,
+                                     ctypes.cast(arr, ctypes.c_void_p), _ptr(x_in), _ptr(a_in),
+                                     _ptr(y_qkv), _ptr(y_o), _ptr(h), _ptr(y_out), _ptr(ffn_signs),
+                                     wp, wb, _stream(stream)), "tq_decode_stack_batch")
 
 
 def stack_timeouts(ws) -> int:

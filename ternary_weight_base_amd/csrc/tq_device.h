@@ -173,30 +173,63 @@ __device__ __forceinline__ uint32_t pack_y4(uint32_t a, uint32_t b, uint32_t c, 
   return lo | (hi << 16);
 }
 
-// Integer core of one B3 group with the activation words in VGPRs (read
-// from LDS by the caller, the same address in every lane): the dots take
-// VGPR operands, so the fifth trits of bytes 4c..4c+3 are packed into one
-// word (two byte merges and a shift-or) for a single dot with word 25 + c,
-// where the SGPR form shifts the activation word instead.
-__device__ __forceinline__ int b3_group_v(const uint2 *lut, uint32_t laneoff, const uint32_t (&w)[7],
-                                          const uint32_t (&x)[32]) {
+// One B3 group decoded for several activation rows: the 26 digit-table
+// entries of this lane's row and the fifth trits of bytes 4c..4c+3 packed
+// into one word each (two byte merges and a shift-or), made once and
+// dotted with each row's activation words.
+struct B3Dec {
   uint2 e[26];
-#define TQ_LK(J) e[J] = b3_byte<J>(lut, w, laneoff);
+  uint32_t py[6];
+};
+
+__device__ __forceinline__ void b3_decode(const uint2 *lut, uint32_t laneoff, const uint32_t (&w)[7], B3Dec &d) {
+  // all 26 table lookups before the first use, so that the LDS latency overlaps
+#define TQ_LK(J) d.e[J] = b3_byte<J>(lut, w, laneoff);
   TQ_LK(0) TQ_LK(1) TQ_LK(2) TQ_LK(3) TQ_LK(4) TQ_LK(5) TQ_LK(6) TQ_LK(7) TQ_LK(8)
   TQ_LK(9) TQ_LK(10) TQ_LK(11) TQ_LK(12) TQ_LK(13) TQ_LK(14) TQ_LK(15) TQ_LK(16)
   TQ_LK(17) TQ_LK(18) TQ_LK(19) TQ_LK(20) TQ_LK(21) TQ_LK(22) TQ_LK(23) TQ_LK(24)
   TQ_LK(25)
 #undef TQ_LK
+#pragma unroll
+  for (int c = 0; c < 6; c++) d.py[c] = pack_y4(d.e[4 * c].y, d.e[4 * c + 1].y, d.e[4 * c + 2].y, d.e[4 * c + 3].y);
+}
+
+// Integer core of a decoded B3 group with one row's activation words in
+// VGPRs (read from LDS by the caller, the same address in every lane): the
+// dots take VGPR operands, so the fifth trits go in packed (B3Dec::py), one
+// dot with word 25 + c per four bytes, where the SGPR form shifts the
+// activation word instead.
+__device__ __forceinline__ int b3_dot_v(const B3Dec &d, const uint32_t (&x)[32]) {
   int S = 0, S2 = 0;
 #pragma unroll
-  for (int j = 0; j < 25; j++) S = sdot4(e[j].x, x[j], S);
+  for (int j = 0; j < 25; j++) S = sdot4(d.e[j].x, x[j], S);
 #pragma unroll
-  for (int c = 0; c < 6; c++) {
-    S2 = sdot4(pack_y4(e[4 * c].y, e[4 * c + 1].y, e[4 * c + 2].y, e[4 * c + 3].y), x[25 + c], S2);
-  }
+  for (int c = 0; c < 6; c++) S2 = sdot4(d.py[c], x[25 + c], S2);
   // word 31: the fifth trit of byte 24 (byte 0) and digits 1..3 of byte 25
-  S2 = sdot4(e[24].y, x[31], S2);
-  return sdot4(e[25].x, x[31], S) + S2;
+  S2 = sdot4(d.e[24].y, x[31], S2);
+  return sdot4(d.e[25].x, x[31], S) + S2;
+}
+
+// The same with the activation words in SGPRs (XS::get(0, i)), two
+// accumulator chains; the fifth trit of byte j pairs with byte j % 4 of
+// word 25 + j / 4, shifted down.
+template <typename XS>
+__device__ __forceinline__ int b3_dot_s(const B3Dec &d, const XS &x) {
+  int S = 0, S2 = 0;
+#pragma unroll
+  for (int j = 0; j < 25; j++) {
+    S = sdot4(d.e[j].x, x.get(0, j), S);
+    S2 = sdot4(d.e[j].y, x.get(0, 25 + (j >> 2)) >> (8 * (j & 3)), S2);
+  }
+  return sdot4(d.e[25].x, x.get(0, 31), S) + S2;
+}
+
+// One row, decode and dot together (VGPR activation words).
+__device__ __forceinline__ int b3_group_v(const uint2 *lut, uint32_t laneoff, const uint32_t (&w)[7],
+                                          const uint32_t (&x)[32]) {
+  B3Dec d;
+  b3_decode(lut, laneoff, w, d);
+  return b3_dot_v(d, x);
 }
 
 // Exchange meet of one output's sums between the pieces of a block cut
@@ -240,6 +273,54 @@ __device__ __forceinline__ bool meet_tree(float (&tot)[NMAT], bool live, int pc,
   tot[0] = meet_dec((uint32_t)v);
   if constexpr (NMAT == 2) tot[1] = meet_dec((uint32_t)(v >> 32));
   return holder;
+}
+
+// The same meet for MT token rows at once: row r's slots lie r * row_stride
+// words after row 0's; holder[r] (in: the thread has row r's sums; out: it
+// holds row r's total).  Each tree level issues the rows' exchanges
+// together, so the rows share its round trip.
+template <int NMAT, int MT>
+__device__ __forceinline__ void meet_tree(float (&tot)[MT][NMAT], bool (&holder)[MT], int pc, int npc,
+                                          void *slot0_v, size_t node_stride, size_t row_stride) {
+  using S = typename std::conditional<NMAT == 1, uint32_t, uint64_t>::type;
+  S *slot0 = reinterpret_cast<S *>(slot0_v);
+  S v[MT];
+#pragma unroll
+  for (int r = 0; r < MT; r++) {
+    v[r] = (S)meet_enc(tot[r][0]);
+    if constexpr (NMAT == 2) v[r] |= (S)meet_enc(tot[r][1]) << 32;
+  }
+  for (int l = 0; (1 << l) < npc; l++) {
+    const int mid = (((pc >> l) & ~1) + 1) << l;  // first piece of the right subtree
+    if (mid >= npc) continue;
+    S old[MT];
+#pragma unroll
+    for (int r = 0; r < MT; r++) {
+      old[r] = 0;
+      if (holder[r])
+        old[r] = __hip_atomic_exchange(slot0 + r * row_stride + (size_t)(mid - 1) * node_stride, v[r],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int r = 0; r < MT; r++) {
+      if (!holder[r]) continue;
+      if (old[r] == 0) {
+        holder[r] = false;
+      } else {
+        S w = (S)meet_enc(meet_dec((uint32_t)old[r]) + meet_dec((uint32_t)v[r]));
+        if constexpr (NMAT == 2)
+          w |= (S)meet_enc(meet_dec((uint32_t)(old[r] >> 32)) + meet_dec((uint32_t)(v[r] >> 32))) << 32;
+        v[r] = w;
+        __hip_atomic_store(slot0 + r * row_stride + (size_t)(mid - 1) * node_stride, (S)0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < MT; r++) {
+    tot[r][0] = meet_dec((uint32_t)v[r]);
+    if constexpr (NMAT == 2) tot[r][1] = meet_dec((uint32_t)(v[r] >> 32));
+  }
 }
 
 // Integer core of one 2B group.  Device byte 4c' + c, bits 2s hold

@@ -31,6 +31,8 @@ constexpr int kGsMax2 = 5;          // groups per wave, gate + up
 constexpr int kGsSplit = 6;         // groups per wave, gate + up split over 256 workgroups
 constexpr int kBmaxPerLane = 5;     // producer block maxima per lane in one pass
 constexpr int kXmaxLoads = 2;       // fp16 absmax pass: 16-byte loads per thread in one pass
+constexpr int kMaxRows = 4;         // token rows of one launch (each weight group is decoded
+                                    // once and dotted with every row)
 
 enum InKind { kInInt8 = 0, kInF16 = 1, kInF32 = 2 };
 
@@ -97,8 +99,8 @@ struct WsLayout {
   size_t counters, meet, slots, partials, total;
 };
 
-// Launch the kernel of packed format FMT (0 B3, 1 2B, 2 BP) for this plan
-// (nmat 1 or 2, in_kind one of InKind), with the activations in VGPRs
+// Launch the kernel of packed format FMT (0 B3, 1 2B, 2 BP, 3 B3R) for this
+// plan (nmat 1 or 2, in_kind one of InKind), with the activations in VGPRs
 // through LDS (LX, grids of at most kLxMaxGrid workgroups) or in SGPRs.
 // SUMS: the same kernel with the same work split, quantiser and integer
 // core, storing each (row, group)'s int32 sum into A.sums instead of
@@ -107,5 +109,14 @@ struct WsLayout {
 // that they compile in parallel.
 template <int FMT, bool LX, bool SUMS>
 int launch_lx(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st);
+
+// The same kernel for MT (2..kMaxRows) token rows in one launch: the inputs
+// are MT rows of K (block maxima: MT rows of in_nb), the outputs MT rows of
+// N (block maxima: MT rows of NB), and the workspace sections are MT times
+// those of one row (Plan::*_bytes of plan_proj with rows = MT).  fp16 and
+// fp32 inputs only (TQ_ERR_DTYPE for int8); no SUMS form.  One object per
+// (FMT, LX, MT).
+template <int FMT, bool LX, int MT>
+int launch_rows(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st);
 
 }  // namespace tqproj

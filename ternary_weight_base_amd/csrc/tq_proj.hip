@@ -24,7 +24,8 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 // leave NB - 256 CUs with two workgroups and the rest with one; otherwise
 // as one matrix, with up to 512 workgroups and kGsMax2 groups per wave
 // (also when a split range would exceed kGsSplit groups per wave).
-Plan plan_proj(int fmt, int64_t N, int64_t K, int nmat) {
+// rows token rows per launch: every workspace section is rows times one row's.
+Plan plan_proj(int fmt, int64_t N, int64_t K, int nmat, int rows = 1) {
   const Layout L(fmt, N, K);
   const int64_t G = L.G, NB = L.NB, I = NB * G;
   Plan p;
@@ -64,9 +65,9 @@ Plan plan_proj(int fmt, int64_t N, int64_t K, int nmat) {
   p.slot_stride = !p.meet_ok ? 0 : p.split ? 1 : p.C - 1;
   const bool counter = cut && !p.split;  // the rotated output needs the counter meet
   p.counters_bytes = counter ? round256((size_t)NB * 4) : 0;
-  p.partials_bytes = counter ? round256((size_t)p.C * nmat * N * 4) : 0;
-  p.meet_bytes = p.meet_ok ? round256((size_t)NB * 8) : 0;
-  p.slots_bytes = p.meet_ok ? round256((size_t)NB * p.slot_stride * 64 * 4 * nmat) : 0;
+  p.partials_bytes = counter ? round256((size_t)p.C * nmat * rows * N * 4) : 0;
+  p.meet_bytes = p.meet_ok ? round256((size_t)rows * NB * 8) : 0;
+  p.slots_bytes = p.meet_ok ? round256((size_t)rows * NB * p.slot_stride * 64 * 4 * nmat) : 0;
   return p;
 }
 
@@ -124,19 +125,41 @@ int proj_args(const Plan &p, int64_t N, int64_t K, const void *W0, const void *W
   return TQ_OK;
 }
 
+// The kernel for `rows` (2..kMaxRows) token rows; multi-token formats only.
+int launch_rows_fmt(int fmt, int rows, bool lx, const Plan &p, const ProjArgs &A, int nmat, int in_kind,
+                    hipStream_t st) {
+#define TQ_ROWS(F_)                                                                           \
+  switch (rows) {                                                                             \
+    case 2: return lx ? launch_rows<F_, true, 2>(p, A, nmat, in_kind, st)                     \
+                      : launch_rows<F_, false, 2>(p, A, nmat, in_kind, st);                   \
+    case 3: return lx ? launch_rows<F_, true, 3>(p, A, nmat, in_kind, st)                     \
+                      : launch_rows<F_, false, 3>(p, A, nmat, in_kind, st);                   \
+    case 4: return lx ? launch_rows<F_, true, 4>(p, A, nmat, in_kind, st)                     \
+                      : launch_rows<F_, false, 4>(p, A, nmat, in_kind, st);                   \
+    default: return TQ_ERR_SHAPE;                                                             \
+  }
+  if (fmt == TQ_FMT_B3) { TQ_ROWS(0) }
+  if (fmt == TQ_FMT_2B) { TQ_ROWS(1) }
+#undef TQ_ROWS
+  return TQ_ERR_FORMAT;
+}
+
 // One projection as its own launch.  With `sums` the same plan runs the
-// group-sum instantiation instead (no workspace, no output).
+// group-sum instantiation instead (no workspace, no output).  rows > 1:
+// that many token rows in one launch (in, in_aux, out and out_bmax hold
+// rows consecutive rows; the workspace laid out for that many rows).
 int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, int in_kind,
                 const void *in, const float *in_aux, int in_nb, float *out, float *out_bmax,
                 char *ws, const WsLayout &w, hipStream_t st, const int8_t *out_signs = nullptr,
-                int32_t *sums = nullptr, float *sums_scale = nullptr) {
+                int32_t *sums = nullptr, float *sums_scale = nullptr, int rows = 1) {
   const int nmat = W1 ? 2 : 1;
-  const Plan p = plan_proj(fmt, N, K, nmat);
+  const Plan p = plan_proj(fmt, N, K, nmat, rows);
   ProjArgs A;
   int rc = proj_args(p, N, K, W0, W1, in, in_aux, in_nb, out, out_bmax, ws, w, out_signs, sums,
                      sums_scale, A);
   if (rc != TQ_OK) return rc;
   const bool lx = p.grid <= kLxMaxGrid;
+  if (rows > 1) return sums ? TQ_ERR_SHAPE : launch_rows_fmt(fmt, rows, lx, p, A, nmat, in_kind, st);
 #define TQ_LAUNCH(F_)                                                                         \
   if (sums)                                                                                   \
     return lx ? launch_lx<F_, true, true>(p, A, nmat, in_kind, st)                            \
@@ -177,15 +200,16 @@ struct StackWs {
   size_t bmax_o, bmax_h, total;
 };
 
-StackWs stack_ws(int fmt, int64_t hidden, int64_t inter, int64_t qkv_out, int64_t o_in) {
-  const Plan ps[4] = {plan_proj(fmt, qkv_out, hidden, 1), plan_proj(fmt, hidden, o_in, 1),
-                      plan_proj(fmt, inter, hidden, 2), plan_proj(fmt, hidden, inter, 1)};
+// rows token rows: the meet sections and block maxima of that many rows.
+StackWs stack_ws(int fmt, int64_t hidden, int64_t inter, int64_t qkv_out, int64_t o_in, int rows = 1) {
+  const Plan ps[4] = {plan_proj(fmt, qkv_out, hidden, 1, rows), plan_proj(fmt, hidden, o_in, 1, rows),
+                      plan_proj(fmt, inter, hidden, 2, rows), plan_proj(fmt, hidden, inter, 1, rows)};
   StackWs w;
   w.meet_base = round256(tqstack::kSyncBytes);
   w.meet = ws_layout(ps, 4);
   w.bmax_o = w.meet_base + w.meet.total;
-  w.bmax_h = w.bmax_o + round256((size_t)Layout(fmt, hidden, o_in).NB * 4);
-  w.total = w.bmax_h + round256((size_t)Layout(fmt, inter, hidden).NB * 4);
+  w.bmax_h = w.bmax_o + round256((size_t)rows * Layout(fmt, hidden, o_in).NB * 4);
+  w.total = w.bmax_h + round256((size_t)rows * Layout(fmt, inter, hidden).NB * 4);
   return w;
 }
 
@@ -418,6 +442,65 @@ extern "C" int tq_decode_stack_persistent(int fmt, int64_t layers, int64_t hidde
     else if (fmt == TQ_FMT_2B) rc = tqstack::launch_stack<1>(S, nwg, st);
     else rc = tqstack::launch_stack<2>(S, nwg, st);
     if (rc != TQ_OK) return rc;
+  }
+  return TQ_OK;
+}
+
+// ---------------------------------------------------------------------
+// C ABI: decode stack, several token rows per launch
+// ---------------------------------------------------------------------
+namespace {
+bool batch_fmt_ok(int fmt) { return fmt == TQ_FMT_B3 || fmt == TQ_FMT_2B; }
+}  // namespace
+
+extern "C" size_t tq_decode_stack_batch_workspace_bytes(int fmt, int64_t rows, int64_t layers, int64_t hidden,
+                                                        int64_t inter, int64_t qkv_out, int64_t o_in) {
+  if (!batch_fmt_ok(fmt) || rows < 1 || rows > kMaxRows || layers < 1 || !shape_ok(qkv_out, hidden) ||
+      !shape_ok(hidden, o_in) || !shape_ok(inter, hidden) || !shape_ok(hidden, inter))
+    return 0;
+  return stack_ws(fmt, hidden, inter, qkv_out, o_in, (int)rows).total;
+}
+
+extern "C" int tq_decode_stack_batch(int fmt, int64_t rows, int64_t layers, int64_t hidden, int64_t inter,
+                                     int64_t qkv_out, int64_t o_in, const tq_layer *weights,
+                                     const void *x_in, const void *a_in, float *y_qkv, float *y_o, float *h,
+                                     float *y_out, const int8_t *ffn_signs, void *ws, size_t ws_bytes,
+                                     void *stream) {
+  if (!batch_fmt_ok(fmt)) return TQ_ERR_FORMAT;
+  if (rows < 1 || rows > kMaxRows) return TQ_ERR_SHAPE;
+  int rc = stack_check(fmt, layers, hidden, inter, qkv_out, o_in, weights, x_in, a_in, y_qkv, y_o, h, y_out,
+                       ws, ws_bytes);
+  if (rc != TQ_OK) return rc;
+  const size_t need = tq_decode_stack_batch_workspace_bytes(fmt, rows, layers, hidden, inter, qkv_out, o_in);
+  if (ws_bytes < need) return TQ_ERR_SIZE;
+  if (ffn_signs && hidden % 64 != 0) return TQ_ERR_SHAPE;
+  const int R = (int)rows;
+  const StackWs w = stack_ws(fmt, hidden, inter, qkv_out, o_in, R);
+  char *base = (char *)ws;
+  char *meet = base + w.meet_base;
+  float *bmax_o = reinterpret_cast<float *>(base + w.bmax_o);
+  float *bmax_h = reinterpret_cast<float *>(base + w.bmax_h);
+  const int nb_o = (int)Layout(fmt, hidden, o_in).NB, nb_h = (int)Layout(fmt, inter, hidden).NB;
+  const uint16_t *x16 = (const uint16_t *)x_in, *a16 = (const uint16_t *)a_in;
+  hipStream_t st = (hipStream_t)stream;
+  for (int64_t l = 0; l < layers; l++) {
+    const tq_layer &Lw = weights[l];
+    const int64_t lr = l * rows;  // first token row of layer l
+    float *yo = y_o + lr * hidden, *hl = h + lr * inter;
+    if ((rc = launch_proj(fmt, qkv_out, hidden, Lw.qkv, nullptr, kInF16, x16 + lr * hidden, nullptr, 0,
+                          y_qkv + lr * qkv_out, nullptr, meet, w.meet, st, nullptr, nullptr, nullptr, R)) !=
+        TQ_OK)
+      return rc;
+    if ((rc = launch_proj(fmt, hidden, o_in, Lw.o, nullptr, kInF16, a16 + lr * o_in, nullptr, 0, yo, bmax_o,
+                          meet, w.meet, st, ffn_signs ? ffn_signs + l * hidden : nullptr, nullptr, nullptr,
+                          R)) != TQ_OK)
+      return rc;
+    if ((rc = launch_proj(fmt, inter, hidden, Lw.gate, Lw.up, kInF32, yo, bmax_o, nb_o, hl, bmax_h, meet,
+                          w.meet, st, nullptr, nullptr, nullptr, R)) != TQ_OK)
+      return rc;
+    if ((rc = launch_proj(fmt, hidden, inter, Lw.down, nullptr, kInF32, hl, bmax_h, nb_h, y_out + lr * hidden,
+                          nullptr, meet, w.meet, st, nullptr, nullptr, nullptr, R)) != TQ_OK)
+      return rc;
   }
   return TQ_OK;
 }

@@ -148,13 +148,14 @@ __device__ __forceinline__ void st_dev_f32(float *p, float v) {
 // device-scope loads; outputs are stored with device-scope stores (not
 // waited for: the finishing waves, wave < NPART, wait for them), and block
 // maxima go through an atomic maximum on a zeroed array.
-template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX, bool SUMS, bool PERSIST>
+template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX, bool SUMS, bool PERSIST, int MT = 1>
 struct ProjRun {
   static constexpr bool B3F = FMT == 0 || FMT == 3;  // base-3 bytes (block-interleaved or row-major)
   static constexpr int WPG = B3F ? 7 : 9;        // words per (row, group) in registers
   static constexpr int NP = (GS + 1) / 2;        // group pairs: one activation word per lane each
   static constexpr int D0 = D < GS ? D : GS;
   static constexpr int NPART = SPLIT ? kMaxParts : 1;  // blocks a range can touch
+  static_assert(MT >= 1 && MT <= kMaxRows && (MT == 1 || !PERSIST), "token rows");
 
   ProjArgs A;
   int wg, gsv, G, N, K;
@@ -163,14 +164,14 @@ struct ProjRun {
   // trip to HBM), an idle wave's slots the range's last item.
   int bw0, ilast_b, ns, gb, jmax, sb[GS], sg[GS];
   uint32_t wd[NMAT][GS][WPG];
-  float4 xf[IN == kInF32 ? NP : 1];
-  uint2 xh[IN == kInF16 ? NP : 1];
-  uint32_t qv[NP];
-  float bm[IN == kInF32 ? kBmaxPerLane : 1];
-  uint4 xm[IN == kInF16 ? kXmaxLoads : 1];
-  float acc[NPART][NMAT];  // [block of the range][matrix]
-  float a_scale;
-
+  // per token row m: its activation slice, quantised words, absmax inputs
+  float4 xf[MT][IN == kInF32 ? NP : 1];
+  uint2 xh[MT][IN == kInF16 ? NP : 1];
+  uint32_t qv[MT][NP];
+  float bm[MT][IN == kInF32 ? kBmaxPerLane : 1];
+  uint4 xm[MT][IN == kInF16 ? kXmaxLoads : 1];
+  float acc[NPART][NMAT][MT];  // [block of the range][matrix][token row]
+  float a_scale[MT];
   __device__ __forceinline__ void setup(const ProjArgs &args, int wg_, int gs_rt) {
     A = args;
     wg = wg_;
@@ -270,46 +271,50 @@ struct ProjRun {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- 1a/1b. the activation slice (lane l holds word l % 32 of group
-  // 2p + l / 32; int8 input: the words themselves; fp16 / fp32: four values
-  // to quantise) and what the absmax needs
+  // ---- 1a/1b. the activation slices of the MT token rows (lane l holds
+  // word l % 32 of group 2p + l / 32; int8 input: the words themselves; fp16
+  // / fp32: four values to quantise) and what the absmaxes need.  Row m of
+  // the input starts K elements after row m - 1 (block maxima: in_nb).
   __device__ __forceinline__ void load_inputs() {
     const int tid = threadIdx.x, lane = tid & 63;
     const int hsel = lane >> 5, word = lane & 31;
 #pragma unroll
-    for (int p = 0; p < NP; p++) {
-      if (PERSIST && 2 * p >= gsv) break;
-      // this lane's slot, as arithmetic (an indexed sg[] would be moved to LDS)
-      const int jl = min(2 * p + hsel, gsv - 1);
-      const int gl = gb + min(jl, jmax);
-      const int gp = SPLIT && gl >= G ? gl - G : gl;
-      const size_t off = (size_t)gp * tq::kGroup + 4 * (size_t)word;
-      if constexpr (IN == kInF32) {
-        const float *src = (const float *)A.in + off;
-        if constexpr (PERSIST) {
-          const uint64_t lo = ld_dev_u64(src), hi = ld_dev_u64(src + 2);
-          xf[p] = make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
-                              __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+    for (int m = 0; m < MT; m++) {
+#pragma unroll
+      for (int p = 0; p < NP; p++) {
+        if (PERSIST && 2 * p >= gsv) break;
+        // this lane's slot, as arithmetic (an indexed sg[] would be moved to LDS)
+        const int jl = min(2 * p + hsel, gsv - 1);
+        const int gl = gb + min(jl, jmax);
+        const int gp = SPLIT && gl >= G ? gl - G : gl;
+        const size_t off = (size_t)m * K + (size_t)gp * tq::kGroup + 4 * (size_t)word;
+        if constexpr (IN == kInF32) {
+          const float *src = (const float *)A.in + off;
+          if constexpr (PERSIST) {
+            const uint64_t lo = ld_dev_u64(src), hi = ld_dev_u64(src + 2);
+            xf[m][p] = make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                                   __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+          } else {
+            xf[m][p] = *reinterpret_cast<const float4 *>(src);
+          }
+        } else if constexpr (IN == kInF16) {
+          xh[m][p] = *reinterpret_cast<const uint2 *>((const uint16_t *)A.in + off);
         } else {
-          xf[p] = *reinterpret_cast<const float4 *>(src);
+          qv[m][p] = *reinterpret_cast<const uint32_t *>((const int8_t *)A.in + off);
         }
-      } else if constexpr (IN == kInF16) {
-        xh[p] = *reinterpret_cast<const uint2 *>((const uint16_t *)A.in + off);
-      } else {
-        qv[p] = *reinterpret_cast<const uint32_t *>((const int8_t *)A.in + off);
       }
-    }
-    if constexpr (IN == kInF32) {
+      if constexpr (IN == kInF32) {
 #pragma unroll
-      for (int i = 0; i < kBmaxPerLane; i++) {
-        const float *src = A.in_aux + min(lane + 64 * i, A.in_nb - 1);
-        bm[i] = PERSIST ? ld_dev_f32(src) : *src;
+        for (int i = 0; i < kBmaxPerLane; i++) {
+          const float *src = A.in_aux + (size_t)m * A.in_nb + min(lane + 64 * i, A.in_nb - 1);
+          bm[m][i] = PERSIST ? ld_dev_f32(src) : *src;
+        }
       }
-    }
-    if constexpr (IN == kInF16) {
+      if constexpr (IN == kInF16) {
+        const uint4 *row = reinterpret_cast<const uint4 *>((const uint16_t *)A.in + (size_t)m * K);
 #pragma unroll
-      for (int i = 0; i < kXmaxLoads; i++)
-        xm[i] = reinterpret_cast<const uint4 *>(A.in)[min(tid + kThreads * i, K / 8 - 1)];
+        for (int i = 0; i < kXmaxLoads; i++) xm[m][i] = row[min(tid + kThreads * i, K / 8 - 1)];
+      }
     }
   }
 
@@ -320,69 +325,78 @@ struct ProjRun {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hsel = lane >> 5, word = lane & 31;
     const uint2 *lut = sm.lut;
-    uint32_t *qs = sm.qs + (size_t)wave * GS * 32;  // this wave's [GS][32] words
+    uint32_t *qs = sm.qs + (size_t)wave * MT * GS * 32;  // this wave's [MT][GS][32] words
 
-    // ---- 2. fp16 input: per-wave maxima of the whole x ----------------------
+    // ---- 2. fp16 input: per-wave maxima of each whole row ------------------
     if constexpr (IN == kInF16) {
-      float m = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kXmaxLoads; i++) m = habs_max8(xm[i], m);
-      for (int j = tid + kThreads * kXmaxLoads; j < K / 8; j += kThreads)
-        m = habs_max8(reinterpret_cast<const uint4 *>(A.in)[j], m);
-      m = wave_max(m);
-      if (lane == 0) sm.wmax[wave] = m;
+      for (int r = 0; r < MT; r++) {
+        const uint4 *row = reinterpret_cast<const uint4 *>((const uint16_t *)A.in + (size_t)r * K);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kXmaxLoads; i++) m = habs_max8(xm[r][i], m);
+        for (int j = tid + kThreads * kXmaxLoads; j < K / 8; j += kThreads) m = habs_max8(row[j], m);
+        m = wave_max(m);
+        if (lane == 0) sm.wmax[r * kNW + wave] = m;
+      }
       __syncthreads();
     }
 
-    // ---- 3. absmax, quantise the slice --------------------------------------
-    if constexpr (IN == kInInt8) {
-      a_scale = SUMS ? 0.0f : A.in_aux[0];
-    } else {
-      float amax = 0.0f;
-      if constexpr (IN == kInF16) {
+    // ---- 3. absmax, quantise the slice, per row -----------------------------
 #pragma unroll
-        for (int w = 0; w < kNW; w++) amax = fmaxf(amax, sm.wmax[w]);
+    for (int r = 0; r < MT; r++) {
+      if constexpr (IN == kInInt8) {
+        a_scale[r] = SUMS ? 0.0f : A.in_aux[r];
       } else {
-        float m = 0.0f;
+        float amax = 0.0f;
+        if constexpr (IN == kInF16) {
 #pragma unroll
-        for (int i = 0; i < kBmaxPerLane; i++) m = fmaxf(m, bm[i]);
-        for (int j = lane + 64 * kBmaxPerLane; j < A.in_nb; j += 64)
-          m = fmaxf(m, PERSIST ? ld_dev_f32(A.in_aux + j) : A.in_aux[j]);
-        amax = wave_max(m);
-      }
-      const bool zero = amax == 0.0f;
-      const float inv = zero ? 0.0f : 127.0f / amax;  // IEEE division, as the quantiser
-      a_scale = zero ? 0.0f : amax / 127.0f;
-#pragma unroll
-      for (int p = 0; p < NP; p++) {
-        if (PERSIST && 2 * p >= gsv) break;
-        if constexpr (IN == kInF32) {
-          qv[p] = quant4(xf[p].x, xf[p].y, xf[p].z, xf[p].w, inv, zero);
+          for (int w = 0; w < kNW; w++) amax = fmaxf(amax, sm.wmax[r * kNW + w]);
         } else {
-          qv[p] = quant4(half_bits(xh[p].x & 0xffffu), half_bits(xh[p].x >> 16),
-                         half_bits(xh[p].y & 0xffffu), half_bits(xh[p].y >> 16), inv, zero);
+          float m = 0.0f;
+#pragma unroll
+          for (int i = 0; i < kBmaxPerLane; i++) m = fmaxf(m, bm[r][i]);
+          const float *aux = A.in_aux + (size_t)r * A.in_nb;
+          for (int j = lane + 64 * kBmaxPerLane; j < A.in_nb; j += 64)
+            m = fmaxf(m, PERSIST ? ld_dev_f32(aux + j) : aux[j]);
+          amax = wave_max(m);
+        }
+        const bool zero = amax == 0.0f;
+        const float inv = zero ? 0.0f : 127.0f / amax;  // IEEE division, as the quantiser
+        a_scale[r] = zero ? 0.0f : amax / 127.0f;
+#pragma unroll
+        for (int p = 0; p < NP; p++) {
+          if (PERSIST && 2 * p >= gsv) break;
+          if constexpr (IN == kInF32) {
+            qv[r][p] = quant4(xf[r][p].x, xf[r][p].y, xf[r][p].z, xf[r][p].w, inv, zero);
+          } else {
+            qv[r][p] = quant4(half_bits(xh[r][p].x & 0xffffu), half_bits(xh[r][p].x >> 16),
+                              half_bits(xh[r][p].y & 0xffffu), half_bits(xh[r][p].y >> 16), inv, zero);
+          }
+        }
+      }
+      if constexpr (LX) {  // the wave's own slice: no barrier needed
+#pragma unroll
+        for (int p = 0; p < NP; p++) {
+          const int jl = 2 * p + hsel;
+          if (jl < gsv) qs[(r * GS + jl) * 32 + word] = qv[r][p];
         }
       }
     }
-    if constexpr (LX) {  // the wave's own slice: no barrier needed
-#pragma unroll
-      for (int p = 0; p < NP; p++) {
-        const int jl = 2 * p + hsel;
-        if (jl < gsv) qs[jl * 32 + word] = qv[p];
-      }
-    }
-    // 2B: activation sum of every group of the slice (a 32-lane reduction)
-    int xsum[GS];
+    // 2B: activation sum of every group of the slice, per row (a 32-lane reduction)
+    int xsum[MT][GS];
     if constexpr (FMT == 1) {
 #pragma unroll
-      for (int p = 0; p < NP; p++) {
-        if (PERSIST && 2 * p >= gsv) break;
-        int s = sdot4(qv[p], 0x01010101u, 0);
+      for (int r = 0; r < MT; r++)
 #pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off, 32);
-        xsum[2 * p] = __builtin_amdgcn_readlane(s, 0);
-        if (2 * p + 1 < GS) xsum[2 * p + 1] = __builtin_amdgcn_readlane(s, 32);
-      }
+        for (int p = 0; p < NP; p++) {
+          if (PERSIST && 2 * p >= gsv) break;
+          int s = sdot4(qv[r][p], 0x01010101u, 0);
+#pragma unroll
+          for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off, 32);
+          xsum[r][2 * p] = __builtin_amdgcn_readlane(s, 0);
+          if (2 * p + 1 < GS) xsum[r][2 * p + 1] = __builtin_amdgcn_readlane(s, 32);
+        }
     }
 
     // ---- 4. pipelined decode + integer dot + scale -------------------------
@@ -390,22 +404,16 @@ struct ProjRun {
 #pragma unroll
     for (int p = 0; p < NPART; p++)
 #pragma unroll
-      for (int mat = 0; mat < NMAT; mat++) acc[p][mat] = 0.0f;
-    // Empty asm statements (kept in program order) pin the schedule through
-    // data dependences: a group's activation words enter its iteration
-    // through one; each matrix's weight words enter through one (so the wait
-    // for its loads lands there) and its accumulator leaves through another,
-    // so one matrix's lookups and dots are in flight at a time; the loads of
-    // issue() take their group index from one.  Without them the compiler
-    // interleaves iterations and holds several groups' lookups at once.
+      for (int mat = 0; mat < NMAT; mat++)
 #pragma unroll
-    for (int i = 0; i < GS; i++) {
-      if (PERSIST && i >= gsv) break;
-      if (i + D0 < GS && (!PERSIST || i + D0 < gsv)) issue(i + D0);
-      asm volatile("" : "+v"(qv[i >> 1]));
-      XRegs<1> xa;  // SGPRs (v_readlane) or, with LX, VGPRs (LDS)
+        for (int r = 0; r < MT; r++) acc[p][mat][r] = 0.0f;
+    // Activation words of row r for slot i: SGPRs (v_readlane) or, with LX,
+    // VGPRs (LDS).  One or two rows are fetched once per slot; more rows are
+    // fetched per matrix, one row at a time, to bound the registers.
+    constexpr bool kXPre = MT == 1 || (LX && MT <= 2);
+    auto load_x = [&](int r, int i, XRegs<1> &xa) {
       if constexpr (LX) {
-        const uint4 *xq = reinterpret_cast<const uint4 *>(qs + i * 32);
+        const uint4 *xq = reinterpret_cast<const uint4 *>(qs + (r * GS + i) * 32);
 #pragma unroll
         for (int k = 0; k < 8; k++) {
           const uint4 t = xq[k];
@@ -416,7 +424,27 @@ struct ProjRun {
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < 32; k++) xa.v[0][k] = __builtin_amdgcn_readlane(qv[i >> 1], 32 * (i & 1) + k);
+        for (int k = 0; k < 32; k++) xa.v[0][k] = __builtin_amdgcn_readlane(qv[r][i >> 1], 32 * (i & 1) + k);
+      }
+    };
+    // Empty asm statements (kept in program order) pin the schedule through
+    // data dependences: a group's activation words enter its iteration
+    // through one; each matrix's weight words enter through one (so the wait
+    // for its loads lands there) and its accumulators leave through others,
+    // so one matrix's lookups and dots are in flight at a time; the loads of
+    // issue() take their group index from one.  Without them the compiler
+    // interleaves iterations and holds several groups' lookups at once.
+    // A group is decoded once per matrix and dotted with every row.
+#pragma unroll
+    for (int i = 0; i < GS; i++) {
+      if (PERSIST && i >= gsv) break;
+      if (i + D0 < GS && (!PERSIST || i + D0 < gsv)) issue(i + D0);
+#pragma unroll
+      for (int r = 0; r < MT; r++) asm volatile("" : "+v"(qv[r][i >> 1]));
+      XRegs<1> xpre[kXPre ? MT : 1];
+      if constexpr (kXPre) {
+#pragma unroll
+        for (int r = 0; r < MT; r++) load_x(r, i, xpre[r]);
       }
       const bool live = i < ns;
       const int part = SPLIT ? sb[i] - bw0 : 0;
@@ -424,49 +452,78 @@ struct ProjRun {
       for (int mat = 0; mat < NMAT; mat++) {
 #pragma unroll
         for (int k = 0; k < WPG; k++) asm volatile("" : "+v"(wd[mat][i][k]));  // this matrix starts here
-        int S[1] = {0};
+        int S[MT];
         float sc;
         if constexpr (B3F) {
           const uint32_t w[7] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2], wd[mat][i][3],
                                  wd[mat][i][4], wd[mat][i][5], wd[mat][i][6]};
-          if constexpr (LX) S[0] = b3_group_v(lut, laneoff, w, xa.v[0]);
-          else b3_group<1>(lut, laneoff, w, xa, S);
+          B3Dec dec;
+          b3_decode(lut, laneoff, w, dec);
+#pragma unroll
+          for (int r = 0; r < MT; r++) {
+            XRegs<1> xr;
+            if constexpr (!kXPre) load_x(r, i, xr);
+            const XRegs<1> &xa = kXPre ? xpre[r] : xr;
+            if constexpr (LX) S[r] = b3_dot_v(dec, xa.v[0]);
+            else S[r] = b3_dot_s(dec, xa);
+          }
           sc = half_bits(wd[mat][i][6] >> 16);
         } else {
           const uint32_t w[9] = {wd[mat][i][0], wd[mat][i][1], wd[mat][i][2],
                                  wd[mat][i][3], wd[mat][i][4], wd[mat][i][5],
                                  wd[mat][i][6], wd[mat][i][7], wd[mat][i][8]};
-          if constexpr (FMT == 1) {
-            const int xs[1] = {xsum[i]};
-            tb_group<1>(w, xa, xs, S);
-          } else {
-            S[0] = bp_group(w, xa);
+#pragma unroll
+          for (int r = 0; r < MT; r++) {
+            XRegs<1> xr;
+            if constexpr (!kXPre) load_x(r, i, xr);
+            const XRegs<1> &xa = kXPre ? xpre[r] : xr;
+            if constexpr (FMT == 1) {
+              const int xs[1] = {xsum[r][i]};
+              int S1[1] = {0};
+              tb_group<1>(w, xa, xs, S1);
+              S[r] = S1[0];
+            } else {
+              S[r] = bp_group(w, xa);
+            }
           }
           sc = half_bits(wd[mat][i][8]);
         }
         if constexpr (SUMS) {
-          if (live && lane < (int)L.valid_rows(sb[i]))
-            A.sums[((size_t)mat * N + (size_t)sb[i] * tq::kBlockRows + lane) * G + sg[i]] = S[0];
+          if (live && lane < (int)L.valid_rows(sb[i])) {
+#pragma unroll
+            for (int r = 0; r < MT; r++)
+              A.sums[(((size_t)mat * MT + r) * N + (size_t)sb[i] * tq::kBlockRows + lane) * G + sg[i]] = S[r];
+          }
           continue;
         }
         const float s = live ? sc : 0.0f;
 #pragma unroll
-        for (int p = 0; p < NPART; p++) {
-          acc[p][mat] = fmaf(p == part ? s : 0.0f, (float)S[0], acc[p][mat]);
-          asm volatile("" : "+v"(acc[p][mat]));  // ... and ends here: one matrix at a time
-        }
+        for (int p = 0; p < NPART; p++)
+#pragma unroll
+          for (int r = 0; r < MT; r++) {
+            acc[p][mat][r] = fmaf(p == part ? s : 0.0f, (float)S[r], acc[p][mat][r]);
+            asm volatile("" : "+v"(acc[p][mat][r]));  // ... and ends here: one matrix at a time
+          }
       }
     }
     if constexpr (SUMS) {
-      if (wg == 0 && tid == 0 && A.sums_scale) *A.sums_scale = a_scale;
+      if (wg == 0 && tid == 0 && A.sums_scale) {
+#pragma unroll
+        for (int r = 0; r < MT; r++) A.sums_scale[r] = a_scale[r];
+      }
     }
   }
 
   // ---- 5. reduce: waves in LDS, cut blocks through the workspace, store --
-  // (PERSIST: the stores are issued but not waited for)
+  // (PERSIST: the stores are issued but not waited for).  Token row r goes
+  // to out + r N and out_bmax + r NB; its exchange slots and block-maximum
+  // words sit r times the row-0 sections further on; the counter meet's
+  // partial sums are [C][nmat][MT][N], the block's counter is shared by the
+  // rows.
   __device__ __forceinline__ void finish(const ProjLds &sm) {
     if constexpr (SUMS) return;
     const Layout L(FMT, A.N, A.K);
+    const int NB = (int)L.NB;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     float *red = sm.red;
@@ -474,36 +531,44 @@ struct ProjRun {
     for (int p = 0; p < NPART; p++)
 #pragma unroll
       for (int mat = 0; mat < NMAT; mat++)
-        red[((p * NMAT + mat) * kNW + wave) * 64 + lane] = acc[p][mat];
+#pragma unroll
+        for (int r = 0; r < MT; r++) red[(((p * NMAT + mat) * MT + r) * kNW + wave) * 64 + lane] = acc[p][mat][r];
     __syncthreads();
     // wave p finishes block bw0 + p of the range (if the range reaches it)
     const int part = wave, b = bw0 + part;
     if (part >= NPART || b > ilast_b) return;
-    float tot[NMAT];
+    float tot[MT][NMAT];
 #pragma unroll
-    for (int mat = 0; mat < NMAT; mat++) {
-      float s = 0.0f;
+    for (int r = 0; r < MT; r++)
 #pragma unroll
-      for (int w = 0; w < kNW; w++) s += red[((part * NMAT + mat) * kNW + w) * 64 + lane];
-      tot[mat] = s;
-    }
+      for (int mat = 0; mat < NMAT; mat++) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kNW; w++) s += red[(((part * NMAT + mat) * MT + r) * kNW + w) * 64 + lane];
+        tot[r][mat] = s;
+      }
     const size_t n = (size_t)b * tq::kBlockRows + lane;
     const bool row_ok = lane < (int)L.valid_rows(b);
     // The pieces of a block cut over several workgroups meet (tq_proj.h).
-    bool fin = row_ok;  // this lane stores row n
+    bool fin[MT];  // this lane stores row n of token row r
+#pragma unroll
+    for (int r = 0; r < MT; r++) fin[r] = row_ok;
+    const size_t row_slots = (size_t)NB * A.slot_stride * 64;
     if constexpr (SPLIT) {
       // each range holds at least G items, so a cut block has two pieces
       const int wf = item_wg(b * G, A, G), wl = item_wg(b * G + G - 1, A, G);
-      if (wf != wl) fin = meet_tree<NMAT>(tot, row_ok, wg - wf, 2, meet_slot0<NMAT>(A, b, lane), 64);
+      if (wf != wl) meet_tree<NMAT, MT>(tot, fin, wg - wf, 2, meet_slot0<NMAT>(A, b, lane), 64, row_slots);
     } else if (A.C > 1 && A.meet) {
-      fin = meet_tree<NMAT>(tot, row_ok, wg - b * A.C, A.C, meet_slot0<NMAT>(A, b, lane), 64);
+      meet_tree<NMAT, MT>(tot, fin, wg - b * A.C, A.C, meet_slot0<NMAT>(A, b, lane), 64, row_slots);
     } else if (A.C > 1) {
       const int c = wg - b * A.C;
       if (row_ok) {
 #pragma unroll
         for (int mat = 0; mat < NMAT; mat++)
-          __hip_atomic_store(&A.partials[((size_t)c * NMAT + mat) * N + n], tot[mat], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int r = 0; r < MT; r++)
+            __hip_atomic_store(&A.partials[(((size_t)c * NMAT + mat) * MT + r) * N + n], tot[r][mat],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __builtin_amdgcn_s_waitcnt(0);  // the partial sums have reached device scope
       uint32_t prev = 0;
@@ -512,80 +577,86 @@ struct ProjRun {
       prev = __shfl(prev, 0, 64);
       if (prev != (uint32_t)(A.C - 1)) return;  // another chunk finishes this block
 #pragma unroll
-      for (int mat = 0; mat < NMAT; mat++) {
-        float s = 0.0f;
-        if (row_ok) {
-          for (int cc = 0; cc < A.C; cc++)
-            s += __hip_atomic_load(&A.partials[((size_t)cc * NMAT + mat) * N + n], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-          // consumed: leave the workspace zero for the next call, whatever its shape
-          for (int cc = 0; cc < A.C; cc++)
-            __hip_atomic_store(&A.partials[((size_t)cc * NMAT + mat) * N + n], 0.0f, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+      for (int mat = 0; mat < NMAT; mat++)
+#pragma unroll
+        for (int r = 0; r < MT; r++) {
+          float s = 0.0f;
+          if (row_ok) {
+            float *pp = A.partials + ((size_t)mat * MT + r) * N + n;
+            const size_t cstride = (size_t)NMAT * MT * N;
+            for (int cc = 0; cc < A.C; cc++)
+              s += __hip_atomic_load(pp + cc * cstride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // consumed: leave the workspace zero for the next call, whatever its shape
+            for (int cc = 0; cc < A.C; cc++)
+              __hip_atomic_store(pp + cc * cstride, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          tot[r][mat] = s;
         }
-        tot[mat] = s;
-      }
       if (lane == 0) __hip_atomic_store(&A.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    float y;
-    if (NMAT == 1) {
-      y = a_scale * tot[0];
-    } else {
-      const float yg = a_scale * tot[0], yu = a_scale * tot[NMAT - 1];
-      y = yg / (1.0f + expf(-yg)) * yu;
-    }
-    if constexpr (NMAT == 1) {
-      if (A.out_signs) {
-        // Online Hadamard rotation of the block before the next projection
-        // consumes it ("Ternary Bonsai 2 27B…", section "Decode 为什么只能算一般":
-        // a Hadamard transform shared by gate and up, the sign multiply merged
-        // into the path): Sylvester's H_64 over the 64 rows (lanes),
-        // butterflies in double, scaled by 1/8, then the row's sign.  Every
-        // row is valid (N % 64 == 0).
-        double v = (double)y;
 #pragma unroll
-        for (int h = 1; h < 64; h <<= 1) {
-          const double o = __shfl_xor(v, h, 64);
-          v = (lane & h) ? o - v : v + o;
+    for (int r = 0; r < MT; r++) {
+      float y;
+      if (NMAT == 1) {
+        y = a_scale[r] * tot[r][0];
+      } else {
+        const float yg = a_scale[r] * tot[r][0], yu = a_scale[r] * tot[r][NMAT - 1];
+        y = yg / (1.0f + expf(-yg)) * yu;
+      }
+      if constexpr (NMAT == 1) {
+        if (A.out_signs) {
+          // Online Hadamard rotation of the block before the next projection
+          // consumes it ("Ternary Bonsai 2 27B…", section "Decode 为什么只能算一般":
+          // a Hadamard transform shared by gate and up, the sign multiply merged
+          // into the path): Sylvester's H_64 over the 64 rows (lanes),
+          // butterflies in double, scaled by 1/8, then the row's sign.  Every
+          // row is valid (N % 64 == 0).
+          double v = (double)y;
+#pragma unroll
+          for (int h = 1; h < 64; h <<= 1) {
+            const double o = __shfl_xor(v, h, 64);
+            v = (lane & h) ? o - v : v + o;
+          }
+          const float rv = (float)(v * 0.125);
+          y = A.out_signs[n] < 0 ? -rv : rv;
         }
-        const float r = (float)(v * 0.125);
-        y = A.out_signs[n] < 0 ? -r : r;
       }
-    }
-    if (fin) {
-      if constexpr (PERSIST) st_dev_f32(A.out + n, y);
-      else A.out[n] = y;
-    }
-    if (A.out_bmax) {
-      const float m = wave_max(fin ? fabsf(y) : 0.0f);
-      if constexpr (PERSIST) {
-        // the array was zeroed before this projection; |y| >= 0, so the
-        // bits order as the values
-        // (the ballot with every lane active: inside `lane == 0 && ...` it
-        // would see lane 0's row alone and drop the maximum of a piece whose
-        // finished rows do not include row 0)
-        const bool any_fin = __ballot(fin) != 0;
-        if (lane == 0 && any_fin)
-          __hip_atomic_fetch_max(reinterpret_cast<uint32_t *>(A.out_bmax) + b, __float_as_uint(m),
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
+      if (fin[r]) {
+        if constexpr (PERSIST) st_dev_f32(A.out + n, y);
+        else A.out[(size_t)r * N + n] = y;
       }
-      const uint64_t fm = __ballot(fin), vm = __ballot(row_ok);
-      if (fm == vm) {
-        if (lane == 0) A.out_bmax[b] = m;  // this wave stored every row of the block
-      } else if (fm != 0 && lane == 0) {
-        // exchange meet, rows finished by several workgroups: each adds its
-        // maximum (|y| >= 0, so the bits order as the values) and then, once
-        // that is done, its row count; the one completing the count stores
-        uint32_t *mm = A.meet_max + 2 * (size_t)b;
-        __hip_atomic_fetch_max(&mm[0], __float_as_uint(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-        const uint32_t k = (uint32_t)__popcll(fm), rows = (uint32_t)__popcll(vm);
-        const uint32_t prev = __hip_atomic_fetch_add(&mm[1], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev + k == rows) {
-          A.out_bmax[b] = __uint_as_float(__hip_atomic_load(&mm[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-          __hip_atomic_store(&mm[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(&mm[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (A.out_bmax) {
+        const float m = wave_max(fin[r] ? fabsf(y) : 0.0f);
+        if constexpr (PERSIST) {
+          // (one token row) the array was zeroed before this projection;
+          // |y| >= 0, so the bits order as the values (the ballot with every
+          // lane active: inside `lane == 0 && ...` it would see lane 0's row
+          // alone and drop the maximum of a piece whose finished rows do not
+          // include row 0)
+          const bool any_fin = __ballot(fin[r]) != 0;
+          if (lane == 0 && any_fin)
+            __hip_atomic_fetch_max(reinterpret_cast<uint32_t *>(A.out_bmax) + b, __float_as_uint(m),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          continue;
+        }
+        const uint64_t fm = __ballot(fin[r]), vm = __ballot(row_ok);
+        const size_t rb = (size_t)r * NB + b;
+        if (fm == vm) {
+          if (lane == 0) A.out_bmax[rb] = m;  // this wave stored every row of the block
+        } else if (fm != 0 && lane == 0) {
+          // exchange meet, rows finished by several workgroups: each adds its
+          // maximum (|y| >= 0, so the bits order as the values) and then, once
+          // that is done, its row count; the one completing the count stores
+          uint32_t *mm = A.meet_max + 2 * rb;
+          __hip_atomic_fetch_max(&mm[0], __float_as_uint(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_s_waitcnt(0);
+          const uint32_t k = (uint32_t)__popcll(fm), rows = (uint32_t)__popcll(vm);
+          const uint32_t prev = __hip_atomic_fetch_add(&mm[1], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (prev + k == rows) {
+            A.out_bmax[rb] = __uint_as_float(__hip_atomic_load(&mm[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            __hip_atomic_store(&mm[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&mm[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
       }
     }
@@ -603,15 +674,15 @@ struct ProjRun {
 // arguments arrive in SGPRs with the wave), so the activation loads go out
 // without waiting for a load of the argument block.  ProjArgs carries the
 // rest.
-template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX, bool SUMS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LX ? 2 : 4)))
+template <int FMT, int NMAT, int IN, int GS, int D, bool SPLIT, bool LX, bool SUMS, int MT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LX || MT > 2 ? 2 : 4)))
 void proj_kernel(const void *in, const float *in_aux, const uint8_t *W0, const uint8_t *W1, int N, int K,
                  int in_nb, int C, int W, int I, ProjArgs A) {
   constexpr int NPART = SPLIT ? kMaxParts : 1;
   __shared__ __attribute__((aligned(16))) uint2 lut[FMT == 0 || FMT == 3 ? kLutEntries * kLutCopies : 1];
-  __shared__ float red[NPART * NMAT * kNW * 64];
-  __shared__ float wmax[kNW];
-  __shared__ __attribute__((aligned(16))) uint32_t qs[LX ? kNW * GS * 32 : 1];
+  __shared__ float red[NPART * NMAT * MT * kNW * 64];
+  __shared__ float wmax[MT * kNW];
+  __shared__ __attribute__((aligned(16))) uint32_t qs[LX ? kNW * MT * GS * 32 : 1];
   A.in = in;
   A.in_aux = in_aux;
   A.W0 = W0;
@@ -624,7 +695,7 @@ void proj_kernel(const void *in, const float *in_aux, const uint8_t *W0, const u
   A.W = W;
   A.I = I;
   const ProjLds sm{lut, red, wmax, qs};
-  ProjRun<FMT, NMAT, IN, GS, D, SPLIT, LX, SUMS, false> r;
+  ProjRun<FMT, NMAT, IN, GS, D, SPLIT, LX, SUMS, false, MT> r;
   r.setup(A, (int)blockIdx.x, GS);
   r.load_inputs();
   // The digit table depends on nothing: its LDS stores overlap the
@@ -640,14 +711,14 @@ void proj_kernel(const void *in, const float *in_aux, const uint8_t *W0, const u
   r.finish(sm);
 }
 
-template <int FMT, int NMAT, int IN, bool LX, bool SUMS>
+template <int FMT, int NMAT, int IN, bool LX, bool SUMS, int MT>
 int launch_in(const Plan &p, const ProjArgs &A, hipStream_t st) {
   constexpr int D = NMAT == 2 ? TQ_PROJ_D2 : TQ_PROJ_D1;
   const dim3 grid((unsigned)p.grid), block(kThreads);
 #define TQ_CASE(G_, S_)                                                                            \
   case G_:                                                                                         \
-    hipLaunchKernelGGL((proj_kernel<FMT, NMAT, IN, G_, D, S_, LX, SUMS>), grid, block, 0, st, A.in,    \
-                       A.in_aux, A.W0, A.W1, A.N, A.K, A.in_nb, A.C, A.W, A.I, A);                 \
+    hipLaunchKernelGGL((proj_kernel<FMT, NMAT, IN, G_, D, S_, LX, SUMS, MT>), grid, block, 0, st,     \
+                       A.in, A.in_aux, A.W0, A.W1, A.N, A.K, A.in_nb, A.C, A.W, A.I, A);           \
     break;
   if constexpr (NMAT == 1) {
     switch (p.gs) {
@@ -656,9 +727,15 @@ int launch_in(const Plan &p, const ProjArgs &A, hipStream_t st) {
       default: return TQ_ERR_SHAPE;
     }
   } else if (p.split) {
-    switch (p.gs) {
-      TQ_CASE(1, true) TQ_CASE(2, true) TQ_CASE(3, true) TQ_CASE(4, true) TQ_CASE(5, true) TQ_CASE(6, true)
-      default: return TQ_ERR_SHAPE;
+    // the equal split runs on kLxMaxGrid workgroups: always LX (the SGPR
+    // form is kept for one token row only)
+    if constexpr (!LX && MT > 1) {
+      return TQ_ERR_SHAPE;
+    } else {
+      switch (p.gs) {
+        TQ_CASE(1, true) TQ_CASE(2, true) TQ_CASE(3, true) TQ_CASE(4, true) TQ_CASE(5, true) TQ_CASE(6, true)
+        default: return TQ_ERR_SHAPE;
+      }
     }
   } else {
     switch (p.gs) {
@@ -673,14 +750,24 @@ int launch_in(const Plan &p, const ProjArgs &A, hipStream_t st) {
 template <int FMT, bool LX, bool SUMS>
 int launch_lx(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st) {
   if (nmat == 2) {
-    if (in_kind == kInInt8) return launch_in<FMT, 2, kInInt8, LX, SUMS>(p, A, st);
-    if (in_kind == kInF16) return launch_in<FMT, 2, kInF16, LX, SUMS>(p, A, st);
-    return launch_in<FMT, 2, kInF32, LX, SUMS>(p, A, st);
+    if (in_kind == kInInt8) return launch_in<FMT, 2, kInInt8, LX, SUMS, 1>(p, A, st);
+    if (in_kind == kInF16) return launch_in<FMT, 2, kInF16, LX, SUMS, 1>(p, A, st);
+    return launch_in<FMT, 2, kInF32, LX, SUMS, 1>(p, A, st);
   }
-  if (in_kind == kInInt8) return launch_in<FMT, 1, kInInt8, LX, SUMS>(p, A, st);
-  if (in_kind == kInF16) return launch_in<FMT, 1, kInF16, LX, SUMS>(p, A, st);
-  return launch_in<FMT, 1, kInF32, LX, SUMS>(p, A, st);
+  if (in_kind == kInInt8) return launch_in<FMT, 1, kInInt8, LX, SUMS, 1>(p, A, st);
+  if (in_kind == kInF16) return launch_in<FMT, 1, kInF16, LX, SUMS, 1>(p, A, st);
+  return launch_in<FMT, 1, kInF32, LX, SUMS, 1>(p, A, st);
 }
 
+template <int FMT, bool LX, int MT>
+int launch_rows(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st) {
+  if (in_kind == kInInt8) return TQ_ERR_DTYPE;
+  if (nmat == 2) {
+    if (in_kind == kInF16) return launch_in<FMT, 2, kInF16, LX, false, MT>(p, A, st);
+    return launch_in<FMT, 2, kInF32, LX, false, MT>(p, A, st);
+  }
+  if (in_kind == kInF16) return launch_in<FMT, 1, kInF16, LX, false, MT>(p, A, st);
+  return launch_in<FMT, 1, kInF32, LX, false, MT>(p, A, st);
+}
 
 }  // namespace tqproj

@@ -351,6 +351,39 @@ def test_decode_stack_validates_on_host(name):
     assert L.tq_decode_stack(*args, c(good), FAKE, FAKE, *outs, FAKE, FAKE, need - 1, None) == -7
 
 
+def test_decode_stack_batch_validates_on_host():
+    """Every rejection of tq_decode_stack_batch happens on the host."""
+    L = tq.lib
+    args = (2, 640, 1152, 1280, 1024)  # layers, hidden, inter, qkv_out, o_in
+    W = tq.tq_decode_stack_batch_workspace_bytes
+    need = {r: W(B3, r, *args) for r in (1, 2, 3, 4)}
+    assert need[1] == tq.tq_decode_stack_workspace_bytes(B3, *args)
+    assert need[1] <= need[2] <= need[3] <= need[4] and need[1] < need[4]
+    assert W(B3, 0, *args) == 0 and W(B3, 5, *args) == 0
+    assert W(BP, 2, *args) == 0 and W(B3R, 2, *args) == 0 and W(9, 2, *args) == 0
+    assert W(TB, 2, *args) > 0
+    assert W(B3, 2, 2, 600, 1152, 1280, 1024) == 0
+    good = (tq.TqLayer * 2)(*[tq.TqLayer(FAKE, FAKE, FAKE, FAKE, FAKE)] * 2)
+    bad = (tq.TqLayer * 2)(tq.TqLayer(FAKE, FAKE, FAKE, FAKE, FAKE), tq.TqLayer(FAKE, None, FAKE, FAKE, FAKE))
+    c = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    outs = (FAKE,) * 4
+    S = L.tq_decode_stack_batch
+    # (fmt, rows, layers, hidden, inter, qkv_out, o_in, weights, x_in, a_in, y_qkv, y_o, h, y_out,
+    #  ffn_signs, ws, ws_bytes, stream)
+    assert S(B3, 3, *args, c(good), FAKE, FAKE, *outs, None, FAKE, need[3] - 1, None) == -7
+    assert S(B3, 4, *args, c(good), FAKE, FAKE, *outs, None, FAKE, need[1], None) == -7
+    assert S(B3, 0, *args, c(good), FAKE, FAKE, *outs, None, FAKE, need[4], None) == -2
+    assert S(B3, 5, *args, c(good), FAKE, FAKE, *outs, None, FAKE, need[4], None) == -2
+    assert S(BP, 2, *args, c(good), FAKE, FAKE, *outs, None, FAKE, need[4], None) == -5
+    assert S(B3R, 2, *args, c(good), FAKE, FAKE, *outs, None, FAKE, need[4], None) == -5
+    assert S(B3, 2, *args, c(bad), FAKE, FAKE, *outs, None, FAKE, need[2], None) == -1
+    assert S(B3, 2, *args, None, FAKE, FAKE, *outs, None, FAKE, need[2], None) == -1
+    assert S(B3, 2, *args, c(good), MIS, FAKE, *outs, None, FAKE, need[2], None) == -3
+    assert S(B3, 2, *args, c(good), FAKE, FAKE, FAKE, ODD, FAKE, FAKE, None, FAKE, need[2], None) == -3
+    assert S(B3, 2, 2, 640, 1152, 1280, 1000, c(good), FAKE, FAKE, *outs, None, FAKE, need[4],
+             None) == -2
+
+
 def test_gemv_quant_validates_on_host():
     """Every rejection of tq_gemv_quant happens on the host (no GPU here:
     the device pointers are never dereferenced)."""
