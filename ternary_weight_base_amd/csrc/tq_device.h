@@ -25,6 +25,49 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t s0, uint32_t s1, uint32_t 
   return __builtin_amdgcn_perm(s0, s1, sel);
 }
 
+// Cross-lane reductions without an LDS round trip.  DPP moves within rows
+// of 16 lanes (a VALU operand modifier, a few cycles) replace the 64-lane
+// __shfl_xor ladder (a chain of ds_bpermute, each one an LDS round trip):
+// swap neighbours (quad_perm [1,0,3,2]), swap pairs ([2,3,0,1]), rotate the
+// row by 4 and by 8 lanes; the four row results are then read out with
+// v_readlane.  Every lane of the wave must be active.
+constexpr int kDppSwap1 = 0xB1, kDppSwap2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// In every lane: the maximum over its row of 16 lanes.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(dpp_move<kDppSwap1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<kDppSwap2>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<kDppRor4>(__float_as_int(v))));
+  return fmaxf(v, __int_as_float(dpp_move<kDppRor8>(__float_as_int(v))));
+}
+
+// The maximum over the 64 lanes, wave-uniform.  fmaxf is exact and
+// order-free, so this equals any other reduction order.
+__device__ __forceinline__ float wave_max64(float v) {
+  v = row16_max(v);
+  const int b = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// The integer sums over lanes 0..31 (lo) and 32..63 (hi), wave-uniform.
+__device__ __forceinline__ void half_sums(int v, int &lo, int &hi) {
+  v += dpp_move<kDppSwap1>(v);
+  v += dpp_move<kDppSwap2>(v);
+  v += dpp_move<kDppRor4>(v);
+  v += dpp_move<kDppRor8>(v);
+  lo = __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16);
+  hi = __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
 __device__ __forceinline__ float half_bits(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }

@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include "tq.h"
+#include "tq_device.h"
 
 namespace {
 
@@ -78,10 +79,7 @@ __device__ __forceinline__ void rotate_half(const T *xr, const int8_t *signs, in
   }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return tqdev::wave_max64(v); }
 
 // One workgroup per row, two threads per 64-element block, kHThreads / 2
 // blocks per pass.  Rows of up to kHRes passes (the 27B intermediate, 272

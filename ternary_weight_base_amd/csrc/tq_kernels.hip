@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const T *__restric
   for (int i = 0; i < NV; i++)
 #pragma unroll
     for (int j = 0; j < V; j++) a = fmaxf(a, fabsf(v[i][j]));
-  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+  a = wave_max64(a);
   __shared__ float wmax[kQuantThreads / 64];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
   __syncthreads();
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void quant_kernel_long(const T *__restrict__ x
 #pragma unroll
     for (int i = 0; i < V; i++) a = fmaxf(a, fabsf(v[i]));
   }
-  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+  a = wave_max64(a);
   __shared__ float wmax[4];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
   __syncthreads();

@@ -52,10 +52,7 @@ namespace tqproj {
 using namespace tqdev;
 using tq::Layout;
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave_max64(v); }
 
 // The quantiser's fp32 steps for four values: rint(v * inv), clamp to
 // [-127, 127]; packed as four int8 in one word.
@@ -391,11 +388,10 @@ struct ProjRun {
 #pragma unroll
         for (int p = 0; p < NP; p++) {
           if (PERSIST && 2 * p >= gsv) break;
-          int s = sdot4(qv[r][p], 0x01010101u, 0);
-#pragma unroll
-          for (int off = 16; off >= 1; off >>= 1) s += __shfl_xor(s, off, 32);
-          xsum[r][2 * p] = __builtin_amdgcn_readlane(s, 0);
-          if (2 * p + 1 < GS) xsum[r][2 * p + 1] = __builtin_amdgcn_readlane(s, 32);
+          int lo, hi;
+          half_sums(sdot4(qv[r][p], 0x01010101u, 0), lo, hi);
+          xsum[r][2 * p] = lo;
+          if (2 * p + 1 < GS) xsum[r][2 * p + 1] = hi;
         }
     }
 
