@@ -436,7 +436,9 @@ def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time
     - prefill GEMM (M = 512 on the layer-0 gate and down matrices) against
       the int8 MFMA peak;
     - small-batch decode (M tokens per step through the whole stack:
-      tq_quant_act + tq_gemv per projection, 8 launches a layer);
+      tq_quant_act + tq_gemv per projection, 8 launches a layer), and for
+      M = 2..4 the batch stack (tq_decode_stack_batch: 4 launches a layer,
+      quantisers fused, each weight group decoded once for all rows);
     - ternarize_host: the host ternariser on one fp32 gate matrix
       (17408 x 5120, 356 MB), the load-time step before tq_pack.
     (main() adds layout_ab: the decode stack in each packed layout.)"""
@@ -521,7 +523,7 @@ def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time
         out[f"prefill_gemm_{name}"] = {"M": M, "N": N, "K": K, "us": round(ms * 1e3, 2),
                                        "TOP/s": round(tops, 1), "peak_int8_mfma_TOP/s": 5000.0,
                                        "frac": round(tops / 5000.0, 4)}
-    for Mb in (2, 4, 8, 16):
+    for Mb in (2, 3, 4, 8, 16):
         xs = torch.from_numpy(synth.normal_f16(synth.seed(5, Mb, 1), L, Mb, HIDDEN)).to(dev)
         as_ = torch.from_numpy(synth.normal_f16(synth.seed(5, Mb, 2), L, Mb, O_IN)).to(dev)
         qh, qo, qi = (torch.empty((Mb, k), dtype=torch.int8, device=dev) for k in (HIDDEN, O_IN, INTER))
@@ -548,6 +550,18 @@ def measure_extras(args, tq, synth, torch, fmt, stack, x_in, a_in, capture, time
         ms = time_graph(capture(step), 5, 1)
         out[f"small_batch_M{Mb}"] = {"tok/s": round(Mb * 1000.0 / ms, 1), "ms_per_step": round(ms, 3),
                                      "weight_stream_GBps": round(stack.step_weight_bytes / (ms * 1e-3) / 1e9, 1)}
+    lay = tq.stack_layers([tuple(stack.W[k][l] for k in ("qkv", "o", "gate", "up", "down")) for l in range(L)])
+    for Mb in range(2, tq.STACK_MAX_ROWS + 1):
+        xs = torch.from_numpy(synth.normal_f16(synth.seed(5, Mb, 1), L, Mb, HIDDEN)).to(dev)
+        as_ = torch.from_numpy(synth.normal_f16(synth.seed(5, Mb, 2), L, Mb, O_IN)).to(dev)
+        outs = [torch.empty((L, Mb, n), device=dev) for n in (QKV_OUT, HIDDEN, INTER, HIDDEN)]
+        nb = tq.tq_decode_stack_batch_workspace_bytes(fmt, Mb, L, HIDDEN, INTER, QKV_OUT, O_IN)
+        ws = torch.zeros((nb + 15) // 16 * 4, dtype=torch.int32, device=dev)
+        ms = time_graph(capture(lambda: tq.tq_decode_stack_batch(fmt, Mb, L, HIDDEN, INTER, QKV_OUT, O_IN, lay,
+                                                                 xs, as_, *outs, ws)), 5, 1)
+        out[f"small_batch_fused_M{Mb}"] = {
+            "tok/s": round(Mb * 1000.0 / ms, 1), "ms_per_step": round(ms, 3),
+            "weight_stream_GBps": round(stack.step_weight_bytes / (ms * 1e-3) / 1e9, 1)}
     return out
 
 
@@ -574,9 +588,13 @@ def _rocpd(d):
     return durs, ctrs
 
 
-# Kernels whose counters counter_summary reports (name prefixes, B3 instantiations).
-COUNTER_KERNELS = (("QKV", "proj_kernel<0, 1, 1, 5,"), ("O", "proj_kernel<0, 1, 1, 3,"),
-                   ("gate/up", "proj_kernel<0, 2, 2, 6,"), ("down", "proj_kernel<0, 1, 2, 6,"),
+# Kernels whose counters counter_summary reports (name parts, B3 instantiations;
+# the last template argument of proj_kernel is the number of token rows).
+COUNTER_KERNELS = (("QKV", "proj_kernel<0, 1, 1, 5, 2, false, true, false, 1>"),
+                   ("O", "proj_kernel<0, 1, 1, 3, 2, false, true, false, 1>"),
+                   ("gate/up", "proj_kernel<0, 2, 2, 6, 2, true, true, false, 1>"),
+                   ("down", "proj_kernel<0, 1, 2, 6, 2, false, true, false, 1>"),
+                   ("batch-stack gate/up, 4 token rows", "proj_kernel<0, 2, 2, 6, 2, true, true, false, 4>"),
                    ("prefill GEMM, 128-row tiles (gate shape)", "gemm_kernel<0, false, 2>"),
                    ("prefill GEMM, 256-row tiles (down shape)", "gemm_kernel<0, false, 4>"),
                    ("small-batch gate/up", "mgemv_kernel<0, 2, 5>"))
@@ -611,7 +629,7 @@ def profile_summary(trace_dir, fetch_dir, write_dir):
     _, fetch = _rocpd(fetch_dir)
     _, write = _rocpd(write_dir)
     read_bytes, copy_bytes = 1 << 31, 64 << 20
-    dom = [n for n in durs if "proj_kernel<0, 2, 2," in n and "true, true, false>" in n]
+    dom = [n for n in durs if "proj_kernel<0, 2, 2, 6, 2, true, true, false, 1>" in n]
     print("kernel                                                        calls   avg_us   total_ms")
     for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:28]:
         print(f"{name[:60]:60s} {len(v):7d} {sum(v) / len(v) / 1e3:8.3f} {sum(v) / 1e6:10.3f}")

@@ -11,8 +11,9 @@ import pytest
 
 import bench
 
-DOM = "void tqproj::proj_kernel<0, 2, 2, 6, 2, true, true, false>(tqproj::ProjArgs)"
-SUMS = "void tqproj::proj_kernel<0, 2, 2, 6, 2, true, true, true>(tqproj::ProjArgs)"
+DOM = "void tqproj::proj_kernel<0, 2, 2, 6, 2, true, true, false, 1>(tqproj::ProjArgs)"
+SUMS = "void tqproj::proj_kernel<0, 2, 2, 6, 2, true, true, true, 1>(tqproj::ProjArgs)"
+ROWS4 = "void tqproj::proj_kernel<0, 2, 2, 6, 2, true, true, false, 4>(tqproj::ProjArgs)"
 COPY = "__amd_rocclr_copyBuffer"
 READ = "void (anonymous namespace)::stream_read_kernel(uint4 const*, unsigned long, unsigned int*)"
 
@@ -34,7 +35,7 @@ def _db(path, kernels=(), counters=()):
 def test_profile_summary_scales_traffic_by_the_calibrations(tmp_path, monkeypatch, capsys):
     kt, fe, wr = (str(tmp_path / d) for d in ("kt", "fetch", "write"))
     _db(os.path.join(kt, "a", "kt.db"),
-        kernels=[(DOM, 12000), (DOM, 13000), ("other_kernel", 5000), (SUMS, 99000)])
+        kernels=[(DOM, 12000), (DOM, 13000), ("other_kernel", 5000), (SUMS, 99000), (ROWS4, 24000)])
     # per dispatch the counter arrives split over instances (summed per dispatch);
     # the streaming read of 2 GiB reports half its true bytes (scale 2), the
     # copy's writes are counted in full (scale 1)
@@ -42,7 +43,7 @@ def test_profile_summary_scales_traffic_by_the_calibrations(tmp_path, monkeypatc
         counters=[(READ, "FETCH_SIZE", 1, 524288), (READ, "FETCH_SIZE", 1, 524288),
                   (COPY, "FETCH_SIZE", 2, 1000),              # not a calibration
                   (DOM, "FETCH_SIZE", 3, 9000), (DOM, "FETCH_SIZE", 3, 10000),
-                  (DOM, "FETCH_SIZE", 4, 21000)])
+                  (DOM, "FETCH_SIZE", 4, 21000), (ROWS4, "FETCH_SIZE", 5, 99000)])
     _db(os.path.join(wr, "w.db"),
         counters=[(COPY, "WRITE_SIZE", 1, 65536), (COPY, "WRITE_SIZE", 2, 20000),
                   (DOM, "WRITE_SIZE", 3, 300), (DOM, "WRITE_SIZE", 4, 500)])
