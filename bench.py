@@ -597,7 +597,7 @@ COUNTER_KERNELS = (("QKV", "proj_kernel<0, 1, 1, 5, 2, false, true, false, 1>"),
                    ("batch-stack gate/up, 4 token rows", "proj_kernel<0, 2, 2, 6, 2, true, true, false, 4>"),
                    ("prefill GEMM, 128-row tiles (gate shape)", "gemm_kernel<0, false, 2>"),
                    ("prefill GEMM, 256-row tiles (down shape)", "gemm_kernel<0, false, 4>"),
-                   ("small-batch gate/up", "mgemv_kernel<0, 2, 5>"))
+                   ("small-batch gate/up", "mgemv_kernel<0, 2, 5, false>"))
 
 
 def counter_summary(dirs):
@@ -618,6 +618,21 @@ def counter_summary(dirs):
             print(f"  {cname:28s} {v:16.1f}")
 
 
+def _short(name):
+    """A kernel's name without return type, namespaces and parameter list, so
+    that its template arguments fit a table column."""
+    import re
+    s = re.sub(r"^void ", "", name)
+    s = re.sub(r"\(anonymous namespace\)::|tqproj::|tqstack::", "", s)
+    depth = 0
+    for i, ch in enumerate(s):
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0 and i > 0:
+            return s[:i]
+    return s
+
+
 def profile_summary(trace_dir, fetch_dir, write_dir):
     """Text summary of a profiled bench run (printed) and the dominant kernel's
     trace duration and HBM traffic per launch (written to TRAFFIC_FILE).
@@ -631,8 +646,8 @@ def profile_summary(trace_dir, fetch_dir, write_dir):
     read_bytes, copy_bytes = 1 << 31, 64 << 20
     dom = [n for n in durs if "proj_kernel<0, 2, 2, 6, 2, true, true, false, 1>" in n]
     print("kernel                                                        calls   avg_us   total_ms")
-    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:28]:
-        print(f"{name[:60]:60s} {len(v):7d} {sum(v) / len(v) / 1e3:8.3f} {sum(v) / 1e6:10.3f}")
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1]))[:32]:
+        print(f"{_short(name)[:60]:60s} {len(v):7d} {sum(v) / len(v) / 1e3:8.3f} {sum(v) / 1e6:10.3f}")
 
     def per_dispatch(ctrs, cname, pick):
         return [x for (k, cn), v in ctrs.items() if cn == cname and pick(k) for x in v]

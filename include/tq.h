@@ -411,6 +411,16 @@ int tq_debug_gemv_quant_sums(int fmt, int64_t N, int64_t K, const void *W, const
                              int x_dtype, const void *x, const float *x_bmax, int64_t x_nb,
                              int32_t *S, float *a_scale, void *stream);
 
+/* The same for the launches of tq_decode_stack_batch: one projection over
+ * `rows` (1..TQ_STACK_MAX_ROWS) token rows, x holding rows consecutive rows
+ * of K (fp16, or fp32 with x_bmax holding rows consecutive rows of x_nb =
+ * K / 64 block maxima), with that call's plan and kernel; S is int32
+ * [nmat][rows][N][K/128] and a_scale (optional) fp32 [rows].  Formats B3
+ * and 2B. */
+int tq_debug_gemv_quant_rows_sums(int fmt, int64_t rows, int64_t N, int64_t K, const void *W,
+                                  const void *Wu, int x_dtype, const void *x, const float *x_bmax,
+                                  int64_t x_nb, int32_t *S, float *a_scale, void *stream);
+
 /* ---- device: measurement hook ----------------------------------------- */
 
 /* A plain streaming read of `bytes` bytes at src (device, 16-byte aligned,

@@ -40,7 +40,8 @@ EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant
            "tq_ternarize", "tq_debug_stream_read", "tq_debug_gate_up_sums",
            "tq_debug_gemv_quant_sums", "tq_decode_stack_persistent",
            "tq_gemv_noalloc", "tq_noalloc_scratch_bytes",
-           "tq_decode_stack_batch_workspace_bytes", "tq_decode_stack_batch")
+           "tq_decode_stack_batch_workspace_bytes", "tq_decode_stack_batch",
+           "tq_debug_gemv_quant_rows_sums")
 
 
 class TqLayer(ctypes.Structure):
@@ -79,6 +80,7 @@ def _load():
         "tq_decode_stack": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
         "tq_decode_stack_persistent": ([I, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
         "tq_decode_stack_batch_workspace_bytes": ([I, I64, I64, I64, I64, I64, I64], SZ),
+        "tq_debug_gemv_quant_rows_sums": ([I, I64, I64, I64, P, P, I, P, P, I64, P, P, P], I),
         "tq_decode_stack_batch": ([I, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I),
         "tq_gemv_noalloc": ([I, I64, I64, I64, P, P, P, P, P], I),
         "tq_noalloc_scratch_bytes": ([], SZ),
@@ -243,6 +245,19 @@ def tq_debug_gemv_quant_sums(fmt, N, K, W, Wu, x, S, x_bmax=None, a_scale=None, 
     _check(lib.tq_debug_gemv_quant_sums(fmt, N, K, _ptr(W), _ptr(Wu), dtype, _ptr(x), _ptr(x_bmax), nb,
                                         _ptr(S), _ptr(a_scale), _stream(stream)),
            "tq_debug_gemv_quant_sums")
+
+
+def tq_debug_gemv_quant_rows_sums(fmt, rows, N, K, W, Wu, x, S, x_bmax=None, a_scale=None,
+                                  stream=None) -> None:
+    """S int32 [nmat][rows][N][K/128] (and a_scale fp32 [rows]) from the batch
+    stack's kernel over `rows` token rows of x (fp16 [rows][K], or fp32 with
+    x_bmax [rows][K/64])."""
+    import torch
+    dtype = {torch.float16: TQ_F16, torch.float32: TQ_F32}.get(x.dtype, -1)
+    nb = 0 if x_bmax is None else K // 64
+    _check(lib.tq_debug_gemv_quant_rows_sums(fmt, rows, N, K, _ptr(W), _ptr(Wu), dtype, _ptr(x),
+                                             _ptr(x_bmax), nb, _ptr(S), _ptr(a_scale), _stream(stream)),
+           "tq_debug_gemv_quant_rows_sums")
 
 
 def tq_debug_stream_read(src, sink, stream=None) -> None:

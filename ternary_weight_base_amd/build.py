@@ -77,15 +77,17 @@ def build() -> str:
                 units.append(("tq_proj_inst.hip", obj,
                               [f"-DTQ_INST_FMT={fmt}", f"-DTQ_INST_LX={lx}", f"-DTQ_INST_SUMS={sums}",
                                *preload]))
-    # the projection kernel over 2..4 token rows (the batch decode stack):
-    # one object per (multi-token format, activation form, rows)
+    # the projection kernel over 2..4 token rows (the batch decode stack and
+    # its group-sum hook): one object per (multi-token format, activation
+    # form, rows, output kind)
     for fmt, fname in ((0, "b3"), (1, "2b")):
         for lx in (1, 0):
             for mt in (2, 3, 4):
-                obj = f"tq_proj_{fname}{'' if lx else '_sg'}_r{mt}.o"
-                units.append(("tq_proj_inst.hip", obj,
-                              [f"-DTQ_INST_FMT={fmt}", f"-DTQ_INST_LX={lx}", f"-DTQ_INST_MT={mt}",
-                               *preload]))
+                for sums in (0, 1):
+                    obj = f"tq_proj_{fname}{'' if lx else '_sg'}_r{mt}{'_sums' if sums else ''}.o"
+                    units.append(("tq_proj_inst.hip", obj,
+                                  [f"-DTQ_INST_FMT={fmt}", f"-DTQ_INST_LX={lx}", f"-DTQ_INST_MT={mt}",
+                                   f"-DTQ_INST_SUMS={sums}", *preload]))
     # the persistent decode-token kernel: one object per packed format
     for fmt, fname in ((0, "b3"), (1, "2b"), (2, "bp")):
         units.append(("tq_stack.hip", f"tq_stack_{fname}.o", [f"-DTQ_STACK_FMT={fmt}"]))

@@ -114,9 +114,10 @@ int launch_lx(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream
 // are MT rows of K (block maxima: MT rows of in_nb), the outputs MT rows of
 // N (block maxima: MT rows of NB), and the workspace sections are MT times
 // those of one row (Plan::*_bytes of plan_proj with rows = MT).  fp16 and
-// fp32 inputs only (TQ_ERR_DTYPE for int8); no SUMS form.  One object per
-// (FMT, LX, MT).
-template <int FMT, bool LX, int MT>
+// fp32 inputs only (TQ_ERR_DTYPE for int8).  SUMS: the group-sum form, as
+// above, with A.sums [nmat][MT][N][K/128] and A.sums_scale [MT].  One object
+// per (FMT, LX, MT, SUMS).
+template <int FMT, bool LX, int MT, bool SUMS>
 int launch_rows(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st);
 
 }  // namespace tqproj

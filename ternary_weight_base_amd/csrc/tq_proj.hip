@@ -126,16 +126,17 @@ int proj_args(const Plan &p, int64_t N, int64_t K, const void *W0, const void *W
 }
 
 // The kernel for `rows` (2..kMaxRows) token rows; multi-token formats only.
+template <bool SUMS>
 int launch_rows_fmt(int fmt, int rows, bool lx, const Plan &p, const ProjArgs &A, int nmat, int in_kind,
                     hipStream_t st) {
 #define TQ_ROWS(F_)                                                                           \
   switch (rows) {                                                                             \
-    case 2: return lx ? launch_rows<F_, true, 2>(p, A, nmat, in_kind, st)                     \
-                      : launch_rows<F_, false, 2>(p, A, nmat, in_kind, st);                   \
-    case 3: return lx ? launch_rows<F_, true, 3>(p, A, nmat, in_kind, st)                     \
-                      : launch_rows<F_, false, 3>(p, A, nmat, in_kind, st);                   \
-    case 4: return lx ? launch_rows<F_, true, 4>(p, A, nmat, in_kind, st)                     \
-                      : launch_rows<F_, false, 4>(p, A, nmat, in_kind, st);                   \
+    case 2: return lx ? launch_rows<F_, true, 2, SUMS>(p, A, nmat, in_kind, st)               \
+                      : launch_rows<F_, false, 2, SUMS>(p, A, nmat, in_kind, st);             \
+    case 3: return lx ? launch_rows<F_, true, 3, SUMS>(p, A, nmat, in_kind, st)               \
+                      : launch_rows<F_, false, 3, SUMS>(p, A, nmat, in_kind, st);             \
+    case 4: return lx ? launch_rows<F_, true, 4, SUMS>(p, A, nmat, in_kind, st)               \
+                      : launch_rows<F_, false, 4, SUMS>(p, A, nmat, in_kind, st);             \
     default: return TQ_ERR_SHAPE;                                                             \
   }
   if (fmt == TQ_FMT_B3) { TQ_ROWS(0) }
@@ -159,7 +160,9 @@ int launch_proj(int fmt, int64_t N, int64_t K, const void *W0, const void *W1, i
                      sums_scale, A);
   if (rc != TQ_OK) return rc;
   const bool lx = p.grid <= kLxMaxGrid;
-  if (rows > 1) return sums ? TQ_ERR_SHAPE : launch_rows_fmt(fmt, rows, lx, p, A, nmat, in_kind, st);
+  if (rows > 1)
+    return sums ? launch_rows_fmt<true>(fmt, rows, lx, p, A, nmat, in_kind, st)
+                : launch_rows_fmt<false>(fmt, rows, lx, p, A, nmat, in_kind, st);
 #define TQ_LAUNCH(F_)                                                                         \
   if (sums)                                                                                   \
     return lx ? launch_lx<F_, true, true>(p, A, nmat, in_kind, st)                            \
@@ -503,4 +506,24 @@ extern "C" int tq_decode_stack_batch(int fmt, int64_t rows, int64_t layers, int6
       return rc;
   }
   return TQ_OK;
+}
+
+// The group-sum hook of the batch stack's launches: one projection over
+// `rows` token rows with the batch stack's plan and kernel, int32 sums out
+// (S: [nmat][rows][N][K/128]) and the rows' activation scales (a_scale:
+// [rows], optional).
+extern "C" int tq_debug_gemv_quant_rows_sums(int fmt, int64_t rows, int64_t N, int64_t K, const void *W,
+                                             const void *Wu, int x_dtype, const void *x, const float *x_bmax,
+                                             int64_t x_nb, int32_t *S, float *a_scale, void *stream) {
+  if (!W || !x || !S || (x_dtype == TQ_F32 && !x_bmax)) return TQ_ERR_NULL;
+  if (!batch_fmt_ok(fmt)) return TQ_ERR_FORMAT;
+  if (x_dtype != TQ_F16 && x_dtype != TQ_F32) return TQ_ERR_DTYPE;
+  if (rows < 1 || rows > kMaxRows || !shape_ok(N, K) || (x_dtype == TQ_F32 && x_nb != K / 64))
+    return TQ_ERR_SHAPE;
+  if (!aligned16(W) || (Wu && !aligned16(Wu)) || !aligned16(x) || !aligned4(S) ||
+      (x_bmax && !aligned4(x_bmax)) || (a_scale && !aligned4(a_scale)))
+    return TQ_ERR_ALIGN;
+  const WsLayout w = proj_ws(fmt, N, K, Wu ? 2 : 1);
+  return launch_proj(fmt, N, K, W, Wu, x_dtype == TQ_F16 ? kInF16 : kInF32, x, x_bmax, (int)x_nb, nullptr,
+                     nullptr, nullptr, w, (hipStream_t)stream, nullptr, S, a_scale, (int)rows);
 }

@@ -755,15 +755,15 @@ int launch_lx(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream
   return launch_in<FMT, 1, kInF32, LX, SUMS, 1>(p, A, st);
 }
 
-template <int FMT, bool LX, int MT>
+template <int FMT, bool LX, int MT, bool SUMS>
 int launch_rows(const Plan &p, const ProjArgs &A, int nmat, int in_kind, hipStream_t st) {
   if (in_kind == kInInt8) return TQ_ERR_DTYPE;
   if (nmat == 2) {
-    if (in_kind == kInF16) return launch_in<FMT, 2, kInF16, LX, false, MT>(p, A, st);
-    return launch_in<FMT, 2, kInF32, LX, false, MT>(p, A, st);
+    if (in_kind == kInF16) return launch_in<FMT, 2, kInF16, LX, SUMS, MT>(p, A, st);
+    return launch_in<FMT, 2, kInF32, LX, SUMS, MT>(p, A, st);
   }
-  if (in_kind == kInF16) return launch_in<FMT, 1, kInF16, LX, false, MT>(p, A, st);
-  return launch_in<FMT, 1, kInF32, LX, false, MT>(p, A, st);
+  if (in_kind == kInF16) return launch_in<FMT, 1, kInF16, LX, SUMS, MT>(p, A, st);
+  return launch_in<FMT, 1, kInF32, LX, SUMS, MT>(p, A, st);
 }
 
 }  // namespace tqproj

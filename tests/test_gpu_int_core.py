@@ -1,10 +1,11 @@
 """Bit-exact parity of the integer core in the kernels the product runs.
 
 The group-sum hooks (tq_debug_group_sums, tq_debug_gate_up_sums,
-tq_debug_gemv_quant_sums) launch the very kernel, plan and decode path of the
-matching product call -- the one-token projection kernel in both activation
-forms, the MFMA GEMV for 2..16 tokens, the GEMM with its 64/128/256-row tiles
-and K chunks, the fused quantiser of the stack's launches -- with the scaling
+tq_debug_gemv_quant_sums, tq_debug_gemv_quant_rows_sums) launch the very
+kernel, plan and decode path of the matching product call -- the one-token
+projection kernel in both activation forms, the MFMA GEMV for 2..16 tokens,
+the GEMM with its 64/128/256-row tiles and K chunks, the fused quantiser of
+the stack's launches and of the batch stack's 2..4-row launches -- with the scaling
 replaced by a store of S[m][n][g] = sum_i t[n][128g+i] * q[m][128g+i].  Every
 S is compared element by element with the oracle's plain int32 sum
 (oracle.group_sums), at the 27B shapes and on ragged shapes.
@@ -140,6 +141,50 @@ def test_gemv_quant_group_sums(fmt, N, K, dtype, gate_up):
     assert np.array_equal(Sh[0], oracle.group_sums(t, q)[0])
     if gate_up:
         assert np.array_equal(Sh[1], oracle.group_sums(tu, q)[0])
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
+@pytest.mark.parametrize("rows", [2, 3, 4])
+@pytest.mark.parametrize("N,K,dtype,gate_up", STACK_LAUNCHES)
+def test_gemv_quant_rows_group_sums(fmt, rows, N, K, dtype, gate_up):
+    """The batch stack's launches (tq_decode_stack_batch: each weight group
+    decoded once and dotted with every token row): per row, the int8 codes
+    the fused quantiser derives and the integer sums equal the oracle's bit
+    for bit, and so does each row's activation scale.  One row is all zero
+    (scale 0, every sum 0) when there are more than two."""
+    say(f"gemv_quant rows sums {FMTS[fmt]} rows={rows} {N}x{K} {dtype} gate_up={gate_up}")
+    tq = _tq()
+    seed = 7700 + N + K + rows
+    x = synth.normal_f16(synth.seed(seed, 3), rows, K)
+    if dtype == "f32":
+        x = (x.astype(np.float32) * np.float32(3.3)
+             + synth.normal_f32(synth.seed(seed, 4), rows, K) * np.float32(1e-3)).astype(np.float32)
+    if rows > 2:
+        x[1] = 0
+    xb = dev(np.stack([_block_max(x[r]) for r in range(rows)])) if dtype == "f32" else None
+    t, _ = _weights(N, K, seed)
+    Wu, tu = None, None
+    if gate_up:
+        tu, _ = _weights(N, K, seed + 1)
+        Wu = _blob(fmt, N, K, seed + 1)
+    nmat = 2 if gate_up else 1
+    S = torch.full((nmat, rows, N, K // 128), SENTINEL, dtype=torch.int32, device="cuda")
+    a = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    tq.tq_debug_gemv_quant_rows_sums(fmt, rows, N, K, _blob(fmt, N, K, seed), Wu, dev(x), S, x_bmax=xb,
+                                     a_scale=a)
+    torch.cuda.synchronize()
+    q, sc = oracle.quant(x)
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), sc.view(np.uint32)), "activation scales"
+    Sh = S.cpu().numpy()
+    ref = oracle.group_sums(t, q)  # [rows][N][G]
+    for r in range(rows):
+        assert np.array_equal(Sh[0, r], ref[r]), f"row {r}"
+    if gate_up:
+        refu = oracle.group_sums(tu, q)
+        for r in range(rows):
+            assert np.array_equal(Sh[1, r], refu[r]), f"up row {r}"
+    if rows > 2:
+        assert sc[1] == 0 and not Sh[:, 1].any()
 
 
 def _tile_rows(M):

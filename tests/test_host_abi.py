@@ -384,6 +384,25 @@ def test_decode_stack_batch_validates_on_host():
              None) == -2
 
 
+def test_gemv_quant_rows_sums_validates_on_host():
+    """Every rejection of tq_debug_gemv_quant_rows_sums happens on the host."""
+    Q = tq.lib.tq_debug_gemv_quant_rows_sums
+    # (fmt, rows, N, K, W, Wu, x_dtype, x, x_bmax, x_nb, S, a_scale, stream)
+    assert Q(B3, 2, 64, 256, FAKE, None, 0, FAKE, None, 0, None, None, None) == -1
+    assert Q(B3, 2, 64, 256, None, None, 0, FAKE, None, 0, FAKE, None, None) == -1
+    assert Q(B3, 2, 64, 256, FAKE, None, 1, FAKE, None, 4, FAKE, None, None) == -1
+    assert Q(BP, 2, 64, 256, FAKE, None, 0, FAKE, None, 0, FAKE, None, None) == -5
+    assert Q(B3R, 2, 64, 256, FAKE, None, 0, FAKE, None, 0, FAKE, None, None) == -5
+    assert Q(B3, 2, 64, 256, FAKE, None, 2, FAKE, None, 0, FAKE, None, None) == -6
+    assert Q(B3, 0, 64, 256, FAKE, None, 0, FAKE, None, 0, FAKE, None, None) == -2
+    assert Q(B3, 5, 64, 256, FAKE, None, 0, FAKE, None, 0, FAKE, None, None) == -2
+    assert Q(B3, 2, 64, 200, FAKE, None, 0, FAKE, None, 0, FAKE, None, None) == -2
+    assert Q(B3, 2, 64, 256, FAKE, None, 1, FAKE, FAKE, 3, FAKE, None, None) == -2
+    assert Q(B3, 2, 64, 256, FAKE, None, 0, MIS, None, 0, FAKE, None, None) == -3
+    assert Q(B3, 2, 64, 256, FAKE, None, 0, FAKE, None, 0, ODD, None, None) == -3
+    assert Q(B3, 2, 64, 256, FAKE, None, 0, FAKE, None, 0, FAKE, ODD, None) == -3
+
+
 def test_gemv_quant_validates_on_host():
     """Every rejection of tq_gemv_quant happens on the host (no GPU here:
     the device pointers are never dereferenced)."""
