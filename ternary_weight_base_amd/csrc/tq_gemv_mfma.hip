@@ -332,14 +332,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     __syncthreads();
     if (!last_flag) return;  // another chunk finishes this block
+    // in chunk order; the loads of up to 8 chunks are issued before the
+    // first add (loads written one per add are waited for one by one)
 #pragma unroll
     for (int p = 0; p < kPer; p++)
 #pragma unroll
       for (int mat = 0; mat < NMAT; mat++) {
         float s = 0.0f;
-        for (int cc = 0; cc < A.C; cc++)
-          s += __hip_atomic_load(&part[(((size_t)cc * NMAT + mat) * L.NB + b) * 64 * kOut + tid + p * kThreads],
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int c0 = 0; c0 < A.C; c0 += 8) {
+          float v[8];
+#pragma unroll
+          for (int k = 0; k < 8; k++)
+            v[k] = __hip_atomic_load(
+                &part[(((size_t)min(c0 + k, A.C - 1) * NMAT + mat) * L.NB + b) * 64 * kOut + tid + p * kThreads],
+                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int k = 0; k < 8; k++) s = c0 + k < A.C ? s + v[k] : s;
+        }
         tot[p][mat] = s;
       }
     // consumed: leave the workspace zero for the next call, whatever its shape

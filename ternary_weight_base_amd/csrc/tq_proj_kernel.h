@@ -576,17 +576,27 @@ struct ProjRun {
       for (int mat = 0; mat < NMAT; mat++)
 #pragma unroll
         for (int r = 0; r < MT; r++) {
+          // in chunk order; the loads of up to 8 chunks are issued before the
+          // first add (loads written one per add are waited for one by one).
+          // Lanes past the block's valid rows read its first row's sums and drop them.
+          float *pp = A.partials + ((size_t)mat * MT + r) * N + (row_ok ? n : (size_t)b * tq::kBlockRows);
+          const size_t cstride = (size_t)NMAT * MT * N;
           float s = 0.0f;
+          for (int c0 = 0; c0 < A.C; c0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+              v[k] = __hip_atomic_load(pp + min(c0 + k, A.C - 1) * cstride, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int k = 0; k < 8; k++) s = c0 + k < A.C ? s + v[k] : s;
+          }
           if (row_ok) {
-            float *pp = A.partials + ((size_t)mat * MT + r) * N + n;
-            const size_t cstride = (size_t)NMAT * MT * N;
-            for (int cc = 0; cc < A.C; cc++)
-              s += __hip_atomic_load(pp + cc * cstride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // consumed: leave the workspace zero for the next call, whatever its shape
             for (int cc = 0; cc < A.C; cc++)
               __hip_atomic_store(pp + cc * cstride, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-          tot[r][mat] = s;
+          tot[r][mat] = row_ok ? s : 0.0f;
         }
       if (lane == 0) __hip_atomic_store(&A.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
