@@ -210,6 +210,24 @@ size_t tq_noalloc_scratch_bytes(void); /* TQ_NOALLOC_SCRATCH_BYTES, as built */
  * different streams is not allowed. */
 size_t tq_gemv_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
+/* Workspace upkeep.  The calls that take a workspace meet through counters,
+ * slots and partial sums in it: they rely on finding it zero and leave it
+ * zero.  A call that did not complete (an aborted or faulted launch, a
+ * caller's stray write) can leave words behind that every later call
+ * reads.
+ *   tq_workspace_clear zero-fills `bytes` bytes at ws (device, 16-byte
+ *     aligned, bytes % 16 == 0; NULL with bytes 0 is a no-op) with a fill
+ *     kernel on `stream`: the state required before the first use, and
+ *     after any failure.
+ *   tq_workspace_check writes to *nonzero_words (device uint32, 4-byte
+ *     aligned) the number of 32-bit words of the range that are not zero (0
+ *     for a workspace fit for the next call), with two small kernels on
+ *     `stream`; the count is valid once the stream reaches that point.
+ * No memset nodes: both may be captured in a graph.  TQ_ERR_NULL,
+ * TQ_ERR_SHAPE (bytes % 16) or TQ_ERR_ALIGN before any launch. */
+int tq_workspace_clear(void *ws, size_t bytes, void *stream);
+int tq_workspace_check(const void *ws, size_t bytes, uint32_t *nonzero_words, void *stream);
+
 /* The decode matrix-vector product: every token streams the whole packed
  * matrix once, decodes it in registers and runs the integer dot per group
  * ("Ternary Bonsai 2 27B：8GB 显卡硬塞 27B 三元模型…", section

@@ -41,7 +41,7 @@ EXPORTS = ("tq_status_str", "tq_packed_bytes", "tq_pack", "tq_unpack", "tq_quant
            "tq_debug_gemv_quant_sums", "tq_decode_stack_persistent",
            "tq_gemv_noalloc", "tq_noalloc_scratch_bytes",
            "tq_decode_stack_batch_workspace_bytes", "tq_decode_stack_batch",
-           "tq_debug_gemv_quant_rows_sums")
+           "tq_debug_gemv_quant_rows_sums", "tq_workspace_clear", "tq_workspace_check")
 
 
 class TqLayer(ctypes.Structure):
@@ -89,6 +89,8 @@ def _load():
         "tq_debug_stream_read": ([P, SZ, P, I64, P], I),
         "tq_debug_gate_up_sums": ([I, I64, I64, I64, P, P, P, P, P], I),
         "tq_debug_gemv_quant_sums": ([I, I64, I64, P, P, I, P, P, I64, P, P, P], I),
+        "tq_workspace_clear": ([P, SZ, P], I),
+        "tq_workspace_check": ([P, SZ, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -258,6 +260,20 @@ def tq_debug_gemv_quant_rows_sums(fmt, rows, N, K, W, Wu, x, S, x_bmax=None, a_s
     _check(lib.tq_debug_gemv_quant_rows_sums(fmt, rows, N, K, _ptr(W), _ptr(Wu), dtype, _ptr(x),
                                              _ptr(x_bmax), nb, _ptr(S), _ptr(a_scale), _stream(stream)),
            "tq_debug_gemv_quant_rows_sums")
+
+
+def tq_workspace_clear(ws, stream=None) -> None:
+    """Zero-fill a workspace tensor (device, 16-byte aligned, size a multiple
+    of 16 bytes) on the stream: the state every workspace-taking call expects."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.tq_workspace_clear(_ptr(ws), nbytes, _stream(stream)), "tq_workspace_clear")
+
+
+def tq_workspace_check(ws, count, stream=None) -> None:
+    """count (device int32/uint32 [>= 1]) receives the number of non-zero
+    32-bit words of the workspace tensor ws (0: fit for the next call)."""
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.tq_workspace_check(_ptr(ws), nbytes, _ptr(count), _stream(stream)), "tq_workspace_check")
 
 
 def tq_debug_stream_read(src, sink, stream=None) -> None:

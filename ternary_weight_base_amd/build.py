@@ -67,7 +67,7 @@ def build() -> str:
     units = [(src, src.replace(".hip", ".o"), preload if src in ("tq_kernels.hip", "tq_gemv_mfma.hip",
                                                                    "tq_hadamard.hip") else [])
              for src in ("tq_kernels.hip", "tq_proj.hip", "tq_gemv_mfma.hip", "tq_hadamard.hip",
-                         "tq_gemm.hip", "tq_stream.hip", "tq_noalloc.hip")]
+                         "tq_gemm.hip", "tq_stream.hip", "tq_noalloc.hip", "tq_workspace.hip")]
     # the projection kernel: one object per (packed format, activation form, output kind)
     for fmt, fname in ((0, "b3"), (1, "2b"), (2, "bp"), (3, "b3r")):
         for lx in (1, 0):

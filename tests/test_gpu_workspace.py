@@ -104,3 +104,56 @@ def test_one_workspace_for_every_call(fmt):
         for (name, _, _), o, r in zip(calls, outs, ref):
             assert np.array_equal(o.cpu().numpy().view(np.uint32), r.view(np.uint32)), f"{name}, pass {rep}"
         assert not shared.any().item(), f"workspace left non-zero after pass {rep}"
+
+
+def test_workspace_clear_and_check():
+    """tq_workspace_check counts the non-zero 32-bit words exactly;
+    tq_workspace_clear zeroes every byte of the range and nothing past it."""
+    import ternary_weight_base_amd as tq
+    say("workspace clear/check")
+    rng = np.random.default_rng(7)
+    for words in (4, 64, 1000, 262144 + 4):  # up to 1 MiB, one ragged tail of the grid
+        host = rng.integers(-3, 3, size=words + 4, dtype=np.int32)
+        host[-4:] = 5  # guard words past the range
+        buf = dev(host)
+        cnt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        tq.tq_workspace_check(buf[:words], cnt)
+        torch.cuda.synchronize()
+        assert int(cnt.item()) == int(np.count_nonzero(host[:words]))
+        tq.tq_workspace_clear(buf[:words])
+        tq.tq_workspace_check(buf[:words], cnt)
+        torch.cuda.synchronize()
+        assert int(cnt.item()) == 0
+        out = buf.cpu().numpy()
+        assert not out[:words].any() and (out[words:] == 5).all()
+
+
+@pytest.mark.parametrize("fmt", [B3, TB])
+def test_poisoned_workspace_is_detected_and_cleared(fmt):
+    """A workspace holding stale words (as a call that did not complete
+    would leave it) is reported by tq_workspace_check; after
+    tq_workspace_clear a split-K call gives the same output, bit for bit, as
+    on a fresh workspace, and leaves the workspace zero again."""
+    import ternary_weight_base_amd as tq
+    say(f"poisoned workspace {FMTS[fmt]}")
+    N, K = 5120, 17408  # K chunks that meet through the workspace
+    W = upload_blob(fmt, *weights(N, K, 31))
+    q, a = _quant(tq, dev(synth.normal_f16(synth.seed(31, 9), 1, K)))
+    nb = tq.tq_gemv_workspace_bytes(fmt, 1, N, K)
+    assert nb > 0
+    fresh = torch.zeros((nb + 15) // 16 * 4, dtype=torch.int32, device="cuda")
+    y0 = torch.full((1, N), float("nan"), device="cuda")
+    tq.tq_gemv(fmt, 1, N, K, W, q, a, y0, fresh)
+    ws = torch.zeros_like(fresh)
+    ws[::97] = 12345  # stale counters / sums
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tq.tq_workspace_check(ws, cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == int((ws != 0).sum().item()) > 0
+    tq.tq_workspace_clear(ws)
+    y1 = torch.full((1, N), float("nan"), device="cuda")
+    tq.tq_gemv(fmt, 1, N, K, W, q, a, y1, ws)
+    tq.tq_workspace_check(ws, cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 0
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))

@@ -468,6 +468,21 @@ def test_stream_read_validates_on_host():
     assert call(sink=ODD) == -3
 
 
+def test_workspace_upkeep_validates_on_host():
+    L = tq.lib
+    clear = lambda ws=FAKE, n=1 << 20: L.tq_workspace_clear(ws, n, None)
+    check = lambda ws=FAKE, n=1 << 20, cnt=FAKE: L.tq_workspace_check(ws, n, cnt, None)
+    assert clear(ws=None) == -1
+    assert clear(n=24) == -2
+    assert clear(ws=MIS) == -3
+    assert clear(ws=None, n=0) == 0  # nothing to clear: no launch
+    assert check(ws=None) == -1
+    assert check(cnt=None) == -1
+    assert check(n=40) == -2
+    assert check(ws=MIS) == -3
+    assert check(cnt=ODD) == -3
+
+
 def test_workspace_sizes():
     assert tq.tq_gemv_workspace_bytes(B3, 1, 1024, 1024) == 0
     for N, K in ((5120, 8192), (5120, 17408), (10240, 5120)):
