@@ -213,6 +213,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
     for (int j = 0; j < kOut; j++) y[mat][j] = 0.0f;
 
+  // waves 4-7 (the younger wave of each SIMD) take the higher issue priority
+  // for the loop, as in the one-token kernel
+  if (wave >= 4) __builtin_amdgcn_s_setprio(1);
   // Empty asm statements pin the schedule through data dependences, as in
   // the one-token kernel: a group's operands enter its iteration through
   // one, each matrix's accumulators leave through another.
@@ -278,6 +281,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     if (i + D0 < GS) issue(i + D0);  // after this group's registers are free
   }
+  __builtin_amdgcn_s_setprio(0);
   if constexpr (SUMS) return;
 
   // ---- waves meet in LDS (the table is no longer read) ---------------------

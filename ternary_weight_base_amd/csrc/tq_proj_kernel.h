@@ -396,6 +396,12 @@ struct ProjRun {
     }
 
     // ---- 4. pipelined decode + integer dot + scale -------------------------
+    // Waves w and w + 4 share a SIMD, and the issue arbiter favours the older
+    // one: waves 0-3 end their loops well before waves 4-7 with the same
+    // work.  Waves 4-7 take the higher priority for the loop (+1% on the
+    // 64-layer stack; the reverse, or the whole kernel, measured level or
+    // slower).
+    if (wave >= 4) __builtin_amdgcn_s_setprio(1);
     const uint32_t laneoff = (uint32_t)(lane & 31) * 8u;
 #pragma unroll
     for (int p = 0; p < NPART; p++)
@@ -502,6 +508,7 @@ struct ProjRun {
           }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (SUMS) {
       if (wg == 0 && tid == 0 && A.sums_scale) {
 #pragma unroll
