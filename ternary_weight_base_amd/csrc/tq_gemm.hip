@@ -226,6 +226,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
           acc32[ms][ns] = __builtin_amdgcn_mfma_i32_16x16x64_i8(acur[ms][ks], bf[ns], acc32[ms][ns], 0, 0, 0);
     }
     // ---- output element (row 4*slot + v, column li) of each 16x16 tile ---
+    // The 128-row tile's waves rescale at raised issue priority: the rescale
+    // ends the group's chain before the next barrier, and the three
+    // workgroups of a CU contend for the SIMDs (-6% on the gate shape at
+    // M = 512, -5% at M = 256, level at M = 64; the 256-row tile, two
+    // workgroups per CU, measured slower with it).
+    if (TM == 2) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int ns = 0; ns < 4; ns++) {
       const int col = 16 * ns + li;
@@ -244,6 +250,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
         }
       }
     }
+    if (TM == 2) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < WPG; i++) wcur[i] = wnext[i];
   }
