@@ -228,9 +228,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t *__restrict__ W
     // ---- output element (row 4*slot + v, column li) of each 16x16 tile ---
     // The 128-row tile's waves rescale at raised issue priority: the rescale
     // ends the group's chain before the next barrier, and the three
-    // workgroups of a CU contend for the SIMDs (-6% on the gate shape at
-    // M = 512, -5% at M = 256, level at M = 64; the 256-row tile, two
-    // workgroups per CU, measured slower with it).
+    // workgroups of a CU contend for the SIMDs (about -4% on the gate shape
+    // at M = 512, level at M = 64; the 256-row tile, two workgroups per CU,
+    // measured slower with it).
     if (TM == 2) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int ns = 0; ns < 4; ns++) {
