@@ -109,3 +109,23 @@ def test_graph_gemm_and_hadamard():
         tq.tq_hadamard_quant_act(x, s, q, a)
         tq.tq_gemm(TB, M, N, K, W, q, a, y, ws)
     _replays_match(fn, [q, a, y])
+
+
+def test_graph_workspace_clear_and_check():
+    """The workspace helpers captured in a graph: a stale workspace (filled
+    by a kernel inside the graph) is counted, cleared, and counted again as
+    zero on every replay."""
+    import ternary_weight_base_amd as tq
+    say("graph workspace clear/check")
+    words = 70000
+    ws = torch.zeros(words, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cnt2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def fn():
+        ws.fill_(7)
+        tq.tq_workspace_check(ws, cnt)
+        tq.tq_workspace_clear(ws)
+        tq.tq_workspace_check(ws, cnt2)
+    _replays_match(fn, [cnt, cnt2, ws])
+    assert int(cnt.item()) == words and int(cnt2.item()) == 0 and not ws.any().item()
