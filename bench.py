@@ -11,7 +11,7 @@ scales), resident in HBM before timing starts.  Inputs are seeded synthetic
 data with the shapes and distributions of the workload (trits P(0) = 1/2,
 P(+-1) = 1/4; scales uniform in [0.005, 0.05]; activations N(0,1) in fp16).
 
-Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+Prints one JSON line.  --gpus N > 1 is refused: the library has no multi-GPU path.
 
   python bench.py --profile-summary TRACE_DIR FETCH_DIR WRITE_DIR
 turns three rocprofv3 runs of this script (--kernel-trace --stats, then
@@ -108,8 +108,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only; --gpus N with N > 1 is not "
-              "supported (no collectives are built).", file=sys.stderr)
+        print("bench.py: measures one GPU only; --gpus N with N > 1 is not "
+              "supported (the library has no collectives).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -90,7 +90,7 @@ def test_counter_summary_averages_per_dispatch(tmp_path, capsys):
 
 
 def test_bench_refuses_more_than_one_gpu():
-    """--gpus N > 1 exits with a message: this build measures one GPU."""
+    """--gpus N > 1 exits with a message: the bench measures one GPU."""
     import subprocess
     import sys
     r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"),
